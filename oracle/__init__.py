@@ -1,0 +1,36 @@
+"""CPU oracle for context-parallel attention: plain, slow, float64.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package. The product library (``context_attention_dit_amd``) never imports it,
+and it imports nothing from the product: the two share no code, only the
+seeded inputs of the ``synthetic`` package.
+
+Functions and the passages they follow:
+  attention.attention       full softmax attention + LSE by brute force
+                            (diffusers Context parallelism guide, Ring Attention;
+                            Ulysses SP article, notes 2 and 7 for causal masking
+                            from positions)
+  attention.chunk_partial   one ring hop's (O_c, LSE_c)
+                            (diffusers parallel API, ContextParallelConfig:
+                            convert_to_fp32 output + LSE)
+  attention.lse_merge       closed-form merge of partials
+                            (SGLang Diffusion Sequence Parallelism, Numerics
+                            across node boundaries)
+  attention.ring_attention  ring order of hops, then merge (diffusers guide,
+                            Ring Attention and Ring Anything Attention)
+  relayout.seq2head / head2seq (and *_loop forms)
+                            Ulysses sequence<->head regrouping (diffusers guide,
+                            Ulysses Attention; Ulysses SP article, notes 3-4)
+
+Every function is pinned in ``tests/test_oracle.py`` against closed forms,
+hand-derived golden values (``tests/golden/``), identities, a library
+routine (torch's fp64 scaled_dot_product_attention) and explicit loops.
+"""
+from .attention import (attention, bf16_bits_to_f64, chunk_partial, chunk_positions,
+                        lse_merge, ring_attention, softmax_matrix)
+from .relayout import head2seq, head2seq_loop, seq2head, seq2head_loop
+
+__all__ = ["attention", "chunk_partial", "lse_merge", "ring_attention", "softmax_matrix",
+           "bf16_bits_to_f64", "chunk_positions", "seq2head", "head2seq", "seq2head_loop",
+           "head2seq_loop"]
