@@ -1,0 +1,297 @@
+"""Benchmark of the context-parallel attention hot path on one MI355X.
+
+Default workload (the headline line): one ring rank of FLUX.1-dev at
+1024x1024 — B=1, H=24, D=128, S=4608 (4096 image + 512 text tokens), bf16,
+ring degree 4, rank 0's 1152 query rows against 4 K/V chunks of 1152 in ring
+order [0, 3, 2, 1], fp32 output+LSE merge fused. One step = one
+cp_ring_attention call. ``value`` is attention TFLOP/s (4*D FLOP per
+(query, key) pair) with inputs resident in HBM.
+
+The same JSON line also carries, under ``detail``, every other workload:
+Ulysses seq2head/head2seq GB/s and rank-0 attention TFLOP/s for the
+Qwen-Image, Wan and 128K-causal shapes, the ring-anything S=4099 ranks, and
+the standalone LSE merge GB/s; plus the roofline of the dominant kernel and
+the fp64 CPU oracle timed on the host (``cpu_baseline``).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FLUSH_BYTES = 1 << 30         # written between timed launches of HBM-bound kernels
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_flux_ring_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "context_attention_dit_amd", "csrc", "attn_bf16.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_flops(Sq: int, Skv: int, H: int, D: int, causal: bool, q0: int = 0, k0: int = 0) -> float:
+    """4*D FLOP per visible (query, key) pair: 2*D for Q.K, 2*D for P.V."""
+    if not causal:
+        pairs = Sq * Skv
+    else:
+        pairs = 0
+        # key j visible to query i iff k0 + j <= q0 + i
+        for i in range(Sq):
+            pairs += max(0, min(Skv, q0 + i - k0 + 1))
+    return 4.0 * D * H * pairs
+
+
+def causal_pairs_square(S: int) -> int:
+    return S * (S + 1) // 2
+
+
+def time_launches(torch, fn, warmup: int, iters: int, flush=None):
+    """Per-launch durations (ms) from HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    durs = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        durs.append(a.elapsed_time(b))
+    durs.sort()
+    return durs
+
+
+def median(xs):
+    return xs[len(xs) // 2]
+
+
+def traffic_record():
+    """HBM bytes per launch of the attention kernel, if taken on the current source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if rec.get("attn_bf16_sha256") == src_hash:
+            return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """fp64 oracle on a bounded sample of the FLUX ring rank: whole heads until ~budget_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synthetic
+    w = synthetic.FLUX_RING
+    q, k, v = synthetic.make_qkv(w)
+    n = w.chunk_lens[0]
+    f64 = lambda t: oracle.bf16_bits_to_f64(t.contiguous().view(torch.int16).numpy())
+    ncores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(ncores)
+    chunks = []
+    for s0, ln in zip(w.chunk_starts(), w.chunk_lens):
+        chunks.append((f64(k[:, s0:s0 + ln]), f64(v[:, s0:s0 + ln]), np.arange(s0, s0 + ln)))
+    qf = f64(q[:, :n])
+    order = synthetic.ring_order(0, w.P)
+    done_heads, t0 = 0, time.perf_counter()
+    while done_heads < w.H and time.perf_counter() - t0 < budget_s:
+        h = slice(done_heads, done_heads + 1)
+        oracle.ring_attention(qf[:, :, h], [(kc[:, :, h], vc[:, :, h], p) for kc, vc, p in chunks],
+                              order, 1 / math.sqrt(w.D))
+        done_heads += 1
+    dt = time.perf_counter() - t0
+    flops = attn_flops(n, w.S, done_heads, w.D, False)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
+            "sample": f"FLUX ring rank 0 (1152 rows x 4 chunks of 1152), {done_heads} of 24 heads, "
+                      f"fp64 numpy ring_attention (chunk partials + LSE merge), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import context_attention_dit_amd as cp
+    import synthetic
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        flush_buf.fill_(1.0)
+
+    # ---------------------------------------------------------------- headline
+    w = synthetic.FLUX_RING
+    log(f"{w.name}: inputs")
+    q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
+    n = w.chunk_lens[0]
+    q0 = q[:, :n].contiguous()
+    starts = w.chunk_starts()
+    chunks = [(k[:, s:s + ln].contiguous(), v[:, s:s + ln].contiguous(), s)
+              for s, ln in zip(starts, w.chunk_lens)]
+    order = synthetic.ring_order(0, w.P)
+    vis = [chunks[c] for c in order]
+    o = torch.empty_like(q0)
+    lse = torch.empty((1, w.H, n), dtype=torch.float32, device=dev)
+    step = lambda: cp.ring_attention(q0, vis, o, lse)
+    flops = attn_flops(n, w.S, w.H, w.D, False)
+    log(f"{w.name}: warmup {args.warmup}, timed {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms_step * 1e3:.1f} us/step, kernel {launch_ms * 1e3:.1f} us, "
+        f"{achieved:.1f} TFLOP/s")
+
+    detail = {"flux_ring_rank0": {"us_per_step": ms_step * 1e3, "kernel_us": launch_ms * 1e3,
+                                  "tflops": achieved, "gflop": flops / 1e9}}
+    if not args.quick:
+        detail.update(other_workloads(torch, cp, synthetic, dev, flush, q0, vis, w))
+    del flush_buf
+
+    traffic = traffic_record()
+    line = {
+        "metric": "attention TFLOP/s (bf16, 1 MI355X) + % MFMA peak; relayout GB/s",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1) inputs, seed 1002, rounded to bf16",
+        "config": {"workload": "flux-1024x1024 ring rank 0 of ring_degree=4: B=1 H=24 D=128 "
+                               "S=4608, Q 1152 rows x 4 K/V chunks of 1152 in order [0,3,2,1], "
+                               "fused fp32 LSE merge, non-causal",
+                   "global_batch": 1, "seq_len": w.S, "parallelism": "one ring rank (P=4)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "attn_bf16_kernel<128, causal=false, out_bf16=true>",
+                     "flop_per_launch": flops},
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf):
+    out = {}
+    # standalone merge of the FLUX ring's 4 fp32 partials (HBM-bound)
+    parts = [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis]
+    po = torch.stack([p[0] for p in parts])
+    pl = torch.stack([p[1] for p in parts])
+    del parts
+    mo = torch.empty_like(q0)
+    ml = torch.empty((1, wf.H, q0.shape[1]), dtype=torch.float32, device=dev)
+    P, B, Sq, H, D = po.shape
+    mbytes = P * (Sq * H * D * 4 + Sq * H * 4) + Sq * H * D * 2 + Sq * H * 4
+    d = time_launches(torch, lambda: cp.lse_merge(po, pl, mo, ml), 3, 20, flush)
+    out["flux_lse_merge"] = {"us": median(d) * 1e3, "gbs": mbytes / (median(d) * 1e-3) / 1e9,
+                             "bytes": mbytes,
+                             "hbm_frac": mbytes / (median(d) * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    d = time_launches(torch, lambda: [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis], 2,
+                      10)
+    out["flux_partials_x4"] = {"us": median(d) * 1e3}
+    del po, pl, mo, ml
+
+    for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
+        log(f"{w.name}: inputs")
+        P, S_l, H, D = w.P, w.S_local, w.H, w.D
+        qkv = [x.view(P, 1, S_l, H, D).to(dev) for x in synthetic.make_qkv(w)]
+        heads = [torch.empty((P, 1, w.S, w.H_local, D), dtype=w.dtype, device=dev) for _ in qkv]
+        nbytes = qkv[0].numel() * qkv[0].element_size() * 2    # read + write, one tensor
+        d_s2h = time_launches(torch, lambda: cp.ulysses_seq2head(qkv[0], P, heads[0]), 2, 10,
+                              flush)
+        for x, y in zip(qkv, heads):
+            cp.ulysses_seq2head(x, P, y)
+        rq, rk, rv = (y[0] for y in heads)
+        o = torch.empty_like(rq)
+        lse = torch.empty((1, w.H_local, w.S), dtype=torch.float32, device=dev)
+        flops = 4.0 * D * w.H_local * (causal_pairs_square(w.S) if w.causal else w.S * w.S)
+        reps = 3 if w.causal else 10
+        d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
+            rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)
+        back = torch.empty_like(qkv[0])
+        d_h2s = time_launches(torch, lambda: cp.ulysses_head2seq(heads[1], P, back), 2, 10, flush)
+        out[w.name] = {
+            "attn_us": median(d_att) * 1e3,
+            "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
+            "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "seq2head_us": median(d_s2h) * 1e3,
+            "seq2head_gbs": nbytes / (median(d_s2h) * 1e-3) / 1e9,
+            "head2seq_us": median(d_h2s) * 1e3,
+            "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
+            "relayout_bytes_per_tensor": nbytes,
+            "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "causal": w.causal, "gflop": flops / 1e9,
+        }
+        log(f"{w.name}: attn {out[w.name]['attn_tflops']:.0f} TFLOP/s, seq2head "
+            f"{out[w.name]['seq2head_gbs']:.0f} GB/s, head2seq {out[w.name]['head2seq_gbs']:.0f}")
+        del qkv, heads, rq, rk, rv, o, lse, back
+        torch.cuda.empty_cache()
+
+    w = synthetic.LLM_RING_ANYTHING
+    log(f"{w.name}: ranks")
+    q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
+    starts = w.chunk_starts()
+    chunks = [(k[:, s:s + n].contiguous(), v[:, s:s + n].contiguous(), s)
+              for s, n in zip(starts, w.chunk_lens)]
+    res = {}
+    for causal in (False, True):
+        tot_us, tot_flops = 0.0, 0.0
+        for r in range(w.P):
+            s0, n = starts[r], w.chunk_lens[r]
+            qr = q[:, s0:s0 + n].contiguous()
+            vis = [chunks[c] for c in synthetic.ring_order(r, w.P)]
+            d = time_launches(torch, lambda: cp.ring_attention(qr, vis, causal=causal, q_pos0=s0),
+                              2, 10)
+            tot_us += median(d) * 1e3
+            tot_flops += attn_flops(n, w.S, w.H, w.D, causal, s0, 0)
+        res["causal" if causal else "noncausal"] = {
+            "us_all_ranks": tot_us, "tflops": tot_flops / (tot_us * 1e-6) / 1e12,
+            "gflop": tot_flops / 1e9}
+    out[w.name] = res
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,222 @@
+"""Python binding of libcpattn (include/cp_attn.h): argument marshalling only.
+
+Every computation runs in the HIP library; this module only turns torch
+tensors into pointers and sizes, passes torch's current HIP stream, and turns
+a non-zero status into an exception. There is no CPU fallback: if the built
+library is missing, importing this package raises.
+
+Entry points (same names as the C ABI, without the ``cp_`` prefix):
+  attn_chunk_partial   one ring hop: (O_c, LSE_c) of Q over one K/V chunk
+  lse_merge            merge of P fp32 partials into full attention
+  ring_attention       one ring rank: Q over P chunks in visit order, fused fp32 merge
+  ulysses_seq2head     Ulysses regrouping before attention (all P ranks)
+  ulysses_head2seq     Ulysses regrouping after attention (inverse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(or `python context_attention_dit_amd/_build.py`). There is no fallback path.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+CP_BF16, CP_F32 = 0, 1
+STATUS = {0: "CP_OK", 1: "CP_E_INVALID", 2: "CP_E_UNSUPPORTED", 3: "CP_E_DIVISIBILITY",
+          4: "CP_E_WORKSPACE", 5: "CP_E_HIP"}
+MAX_RING_CHUNKS = 64
+
+_i64, _vp, _f32, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+
+
+class KVChunk(ctypes.Structure):
+    _fields_ = [("k", _vp), ("v", _vp), ("len", _i64), ("pos0", _i64)]
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_chunk_partial = _sig("cp_attn_chunk_partial", [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                _i64, _int, _int, _f32, _int, _i64, _i64, _vp])
+_lse_merge = _sig("cp_lse_merge", [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp])
+_ring_ws = _sig("cp_ring_attention_workspace_bytes", [_i64] * 5, ctypes.c_size_t)
+_ring = _sig("cp_ring_attention", [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp, _i64, _i64, _i64,
+                                   _i64, _int, _f32, _int, _i64, _vp, ctypes.c_size_t, _vp])
+_seq2head = _sig("cp_ulysses_seq2head", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
+_head2seq = _sig("cp_ulysses_head2seq", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
+_last_error = _sig("cp_last_error", [], ctypes.c_char_p)
+_abi_version = _sig("cp_abi_version", [])
+
+
+class CpAttnError(RuntimeError):
+    """A cp_* call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise CpAttnError(fn, status, (_last_error() or b"").decode())
+
+
+def last_error() -> str:
+    return (_last_error() or b"").decode()
+
+
+def abi_version() -> int:
+    return _abi_version()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return CP_BF16
+    if t == torch.float32:
+        return CP_F32
+    raise TypeError(f"unsupported dtype {t} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def _bshd(x: torch.Tensor, name: str) -> Tuple[int, int, int, int]:
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B][S][H][D], got shape {tuple(x.shape)}")
+    return tuple(x.shape)  # type: ignore[return-value]
+
+
+def attn_chunk_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
+                       scale: Optional[float] = None, causal: bool = False, q_pos0: int = 0,
+                       kv_pos0: int = 0, out_dtype: torch.dtype = torch.float32,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(O_c, LSE_c) of ``q`` over one K/V chunk; see cp_attn_chunk_partial in include/cp_attn.h."""
+    B, Sq, H, D = _bshd(q, "q")
+    Bk, Skv, Hk, Dk = _bshd(k, "k")
+    if (Bk, Hk, Dk) != (B, H, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v shapes disagree")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check("cp_attn_chunk_partial", _chunk_partial(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Skv, D, _dtype_code(q.dtype),
+        _dtype_code(o.dtype), scale, int(causal), q_pos0, kv_pos0, _stream(stream)))
+    return o, lse
+
+
+def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.float32,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge ``o_parts [P][B][Sq][H][D]`` / ``lse_parts [P][B][H][Sq]`` (fp32); see cp_lse_merge."""
+    if o_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise ValueError("o_parts must be [P][B][Sq][H][D] and lse_parts [P][B][H][Sq]")
+    P, B, Sq, H, D = o_parts.shape
+    if tuple(lse_parts.shape) != (P, B, H, Sq):
+        raise ValueError("lse_parts shape disagrees with o_parts")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=o_parts.device)
+    _check("cp_lse_merge", _lse_merge(_ptr(o_parts), _ptr(lse_parts), P, _ptr(o), _ptr(lse), B, H,
+                                      Sq, D, _dtype_code(o.dtype), _stream(stream)))
+    return o, lse
+
+
+def ring_attention_workspace_bytes(P: int, B: int, H: int, Sq: int, D: int) -> int:
+    return int(_ring_ws(P, B, H, Sq, D))
+
+
+def ring_attention(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
+                   o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
+                   scale: Optional[float] = None, causal: bool = False, q_pos0: int = 0,
+                   workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One ring rank: ``q`` over ``chunks = [(k_c, v_c, pos0_c), ...]`` in visit order.
+
+    Output O has q's dtype; LSE is fp32 ``[B][H][Sq]``. See cp_ring_attention.
+    """
+    B, Sq, H, D = _bshd(q, "q")
+    arr = (KVChunk * max(1, len(chunks)))()
+    for c, (k, v, pos0) in enumerate(chunks):
+        Bk, L, Hk, Dk = _bshd(k, "k")
+        if (Bk, Hk, Dk) != (B, H, D) or tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"chunk {c} shape disagrees with q")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise TypeError(f"chunk {c} dtype disagrees with q")
+        arr[c] = KVChunk(_ptr(k), _ptr(v), L, int(pos0))
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    need = ring_attention_workspace_bytes(len(chunks), B, H, Sq, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check("cp_ring_attention", _ring(
+        _ptr(q), arr, len(chunks), _ptr(o), _ptr(lse), B, H, Sq, D, _dtype_code(q.dtype), scale,
+        int(causal), q_pos0, _ptr(workspace), ws_bytes, _stream(stream)))
+    return o, lse
+
+
+def ulysses_seq2head(x: torch.Tensor, P: int, out: Optional[torch.Tensor] = None, *,
+                     stream=None) -> torch.Tensor:
+    """``[P][B][S_l][H][D]`` -> ``[P][B][P*S_l][H/P][D]``; see cp_ulysses_seq2head."""
+    if x.dim() != 5 or x.shape[0] != P:
+        raise ValueError("x must be [P][B][S_local][H][D]")
+    _, B, S_l, H, D = x.shape
+    if out is None:
+        out = torch.empty((P, B, P * S_l, H // P, D), dtype=x.dtype, device=x.device)
+    _check("cp_ulysses_seq2head", _seq2head(_ptr(x), _ptr(out), P, B, S_l, H, D,
+                                            _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
+def ulysses_head2seq(y: torch.Tensor, P: int, out: Optional[torch.Tensor] = None, *,
+                     stream=None) -> torch.Tensor:
+    """``[P][B][P*S_l][H_l][D]`` -> ``[P][B][S_l][P*H_l][D]``; see cp_ulysses_head2seq."""
+    if y.dim() != 5 or y.shape[0] != P or y.shape[2] % P != 0:
+        raise ValueError("y must be [P][B][P*S_local][H/P][D]")
+    _, B, S, H_l, D = y.shape
+    if out is None:
+        out = torch.empty((P, B, S // P, H_l * P, D), dtype=y.dtype, device=y.device)
+    _check("cp_ulysses_head2seq", _head2seq(_ptr(y), _ptr(out), P, B, S // P, H_l * P, D,
+                                            _dtype_code(y.dtype), _stream(stream)))
+    return out
+
+
+__all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
+           "ulysses_seq2head", "ulysses_head2seq", "last_error", "abi_version", "CpAttnError",
+           "KVChunk", "LIB_PATH"]

@@ -1,0 +1,294 @@
+// extern "C" entry points of libcpattn: argument validation and dispatch.
+//
+// Every argument is checked on the host before anything is enqueued, so a
+// rejected call leaves all outputs untouched (the standard context-parallel
+// modes fail on sizes they cannot split instead of padding silently:
+// Context parallelism guide (diffusers), variant table and the 1008x1008
+// benchmark rows). No entry point allocates device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <initializer_list>
+#include <string>
+
+#include "cp_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+cp_status fail(cp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+cp_status ok() {
+  g_err.clear();
+  return CP_OK;
+}
+
+cp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CP_E_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+int elem_size(cp_dtype t) { return t == CP_BF16 ? 2 : 4; }
+bool valid_dtype(int t) { return t == CP_BF16 || t == CP_F32; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+// Product of non-negative sizes, saturated at INT64_MAX (no overflow).
+int64_t sat_mul(std::initializer_list<int64_t> xs) {
+  __int128 p = 1;
+  for (int64_t x : xs) {
+    p *= x;
+    if (p > INT64_MAX) return INT64_MAX;
+  }
+  return static_cast<int64_t>(p);
+}
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+// Checks shared by the attention entry points. Returns CP_OK or an error.
+cp_status check_attn_common(const char* fn, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                            int in_dtype, int causal, float scale) {
+  if (B < 0 || H < 0 || Sq < 0 || D < 0)
+    return fail(CP_E_INVALID, "%s: negative size (B=%lld H=%lld Sq=%lld D=%lld)", fn,
+                (long long)B, (long long)H, (long long)Sq, (long long)D);
+  if (!valid_dtype(in_dtype)) return fail(CP_E_INVALID, "%s: unknown dtype %d", fn, in_dtype);
+  if (causal != 0 && causal != 1) return fail(CP_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!std::isfinite(scale)) return fail(CP_E_INVALID, "%s: scale must be finite", fn);
+  if (D != 64 && D != 128)
+    return fail(CP_E_UNSUPPORTED, "%s: head dim D=%lld not built (64 or 128)", fn, (long long)D);
+  if (Sq >= kMaxSeq) return fail(CP_E_UNSUPPORTED, "%s: Sq=%lld exceeds 2^30", fn, (long long)Sq);
+  // query tiles x batch x heads must fit one launch grid (64-row tiles worst case)
+  if (sat_mul({(Sq + 63) / 64, B, H}) > kMaxGrid / 8)
+    return fail(CP_E_UNSUPPORTED, "%s: B*H*Sq too large for one launch", fn);
+  return CP_OK;
+}
+
+int32_t clamp_delta(int64_t q_pos0, int64_t kv_pos0, int64_t Sq, int64_t len) {
+  // key j visible to query i iff j <= i + delta; clamping to [-(Sq+1), len+1]
+  // changes no visibility decision for 0 <= i < Sq, 0 <= j < len.
+  const int64_t lo = -(Sq + 1), hi = len + 1;
+  // q_pos0 - kv_pos0 without overflow
+  if (q_pos0 >= 0 && kv_pos0 < 0 && q_pos0 > INT64_MAX + kv_pos0) return static_cast<int32_t>(hi);
+  if (q_pos0 < 0 && kv_pos0 > 0 && q_pos0 < INT64_MIN + kv_pos0) return static_cast<int32_t>(lo);
+  int64_t d = q_pos0 - kv_pos0;
+  if (d < lo) d = lo;
+  if (d > hi) d = hi;
+  return static_cast<int32_t>(d);
+}
+
+cp_status launch_attention(const char* fn, const cpattn::AttnArgs& a, cp_dtype in_dtype,
+                           bool out_bf16, int causal, hipStream_t stream) {
+  hipError_t e = in_dtype == CP_BF16 ? cpattn::launch_attn_bf16(a, causal != 0, out_bf16, stream)
+                                     : cpattn::launch_attn_f32(a, causal != 0, stream);
+  return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int cp_abi_version(void) { return CP_ATTN_ABI_VERSION; }
+
+const char* cp_last_error(void) { return g_err.c_str(); }
+
+cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                cp_dtype in_dtype, cp_dtype o_dtype, float scale, int causal,
+                                int64_t q_pos0, int64_t kv_pos0, void* stream) {
+  const char* fn = "cp_attn_chunk_partial";
+  cp_status s = check_attn_common(fn, B, H, Sq, D, in_dtype, causal, scale);
+  if (s != CP_OK) return s;
+  if (Skv < 0) return fail(CP_E_INVALID, "%s: negative Skv", fn);
+  if (Skv >= kMaxSeq) return fail(CP_E_UNSUPPORTED, "%s: Skv exceeds 2^30", fn);
+  if (!valid_dtype(o_dtype)) return fail(CP_E_INVALID, "%s: unknown o_dtype %d", fn, o_dtype);
+  if (in_dtype == CP_F32 && o_dtype != CP_F32)
+    return fail(CP_E_UNSUPPORTED, "%s: fp32 inputs give fp32 outputs only", fn);
+  if (B == 0 || H == 0 || Sq == 0) return ok();
+  const int64_t es = elem_size(in_dtype);
+  const int64_t q_bytes = sat_mul({B, Sq, H, D, es}), kv_bytes = sat_mul({B, Skv, H, D, es});
+  const int64_t o_bytes = sat_mul({B, Sq, H, D, elem_size(o_dtype)});
+  const int64_t l_bytes = sat_mul({B, H, Sq, 4});
+  if (!q || !o || !lse || (Skv > 0 && (!k || !v)))
+    return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(o, 16) || (Skv > 0 && (!aligned(k, 16) || !aligned(v, 16))) ||
+      !aligned(lse, 4))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse 4 B)", fn);
+  if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
+      overlap(o, o_bytes, v, kv_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
+      overlap(lse, l_bytes, q, q_bytes) || overlap(lse, l_bytes, k, kv_bytes) ||
+      overlap(lse, l_bytes, v, kv_bytes))
+    return fail(CP_E_INVALID, "%s: outputs overlap inputs or each other", fn);
+
+  cpattn::AttnArgs a{};
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.B = static_cast<int32_t>(B);
+  a.H = static_cast<int32_t>(H);
+  a.Sq = static_cast<int32_t>(Sq);
+  a.D = static_cast<int32_t>(D);
+  a.scale = scale;
+  a.nchunks = 1;
+  a.chunks[0].k = k;
+  a.chunks[0].v = v;
+  a.chunks[0].len = static_cast<int32_t>(Skv);
+  a.chunks[0].delta = clamp_delta(q_pos0, kv_pos0, Sq, Skv);
+  return launch_attention(fn, a, in_dtype, o_dtype == CP_BF16, causal,
+                          static_cast<hipStream_t>(stream));
+}
+
+cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, void* o,
+                       float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, cp_dtype o_dtype,
+                       void* stream) {
+  const char* fn = "cp_lse_merge";
+  if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
+  if (P >= kMaxGrid) return fail(CP_E_UNSUPPORTED, "%s: P too large", fn);
+  if (B < 0 || H < 0 || Sq < 0 || D < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
+  if (!valid_dtype(o_dtype)) return fail(CP_E_INVALID, "%s: unknown o_dtype %d", fn, o_dtype);
+  if (D % 4 != 0) return fail(CP_E_UNSUPPORTED, "%s: D=%lld is not a multiple of 4", fn,
+                              (long long)D);
+  if (B == 0 || H == 0 || Sq == 0 || D == 0) return ok();
+  if (sat_mul({B, Sq, H, D / 4}) >= kMaxGrid || sat_mul({P, B, Sq, H, D, 4}) >= INT64_MAX / 2)
+    return fail(CP_E_UNSUPPORTED, "%s: tensor too large for one launch", fn);
+  if (!o_parts || !lse_parts || !o || !lse) return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || !aligned(lse, 4))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse 4 B)", fn);
+  const int64_t op_bytes = sat_mul({P, B, Sq, H, D, 4}), lp_bytes = sat_mul({P, B, H, Sq, 4});
+  const int64_t o_bytes = sat_mul({B, Sq, H, D, elem_size(o_dtype)});
+  const int64_t l_bytes = sat_mul({B, H, Sq, 4});
+  if (overlap(o, o_bytes, o_parts, op_bytes) || overlap(o, o_bytes, lse_parts, lp_bytes) ||
+      overlap(o, o_bytes, lse, l_bytes) || overlap(lse, l_bytes, o_parts, op_bytes) ||
+      overlap(lse, l_bytes, lse_parts, lp_bytes))
+    return fail(CP_E_INVALID, "%s: outputs overlap inputs or each other", fn);
+  return hip_status(cpattn::launch_lse_merge(o_parts, lse_parts, static_cast<int>(P), o, lse, B,
+                                             H, Sq, D, o_dtype == CP_BF16,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D) {
+  (void)P;
+  (void)B;
+  (void)H;
+  (void)Sq;
+  (void)D;
+  return 0;
+}
+
+cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
+                            float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                            cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "cp_ring_attention";
+  cp_status s = check_attn_common(fn, B, H, Sq, D, in_dtype, causal, scale);
+  if (s != CP_OK) return s;
+  if (P < 0) return fail(CP_E_INVALID, "%s: negative P", fn);
+  if (P > CP_MAX_RING_CHUNKS)
+    return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d chunks", fn, (long long)P,
+                CP_MAX_RING_CHUNKS);
+  if (P > 0 && !chunks) return fail(CP_E_INVALID, "%s: null chunk array", fn);
+  const size_t need = cp_ring_attention_workspace_bytes(P, B, H, Sq, D);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(CP_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace_bytes);
+  const int64_t es = elem_size(in_dtype);
+  const int64_t q_bytes = sat_mul({B, Sq, H, D, es}), o_bytes = q_bytes;
+  const int64_t l_bytes = sat_mul({B, H, Sq, 4});
+  for (int64_t c = 0; c < P; ++c) {
+    if (chunks[c].len < 0) return fail(CP_E_INVALID, "%s: chunk %lld has negative length", fn,
+                                       (long long)c);
+    if (chunks[c].len >= kMaxSeq)
+      return fail(CP_E_UNSUPPORTED, "%s: chunk %lld longer than 2^30", fn, (long long)c);
+  }
+  if (B == 0 || H == 0 || Sq == 0) return ok();
+  if (!q || !o || !lse) return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse 4 B)", fn);
+  if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
+      overlap(lse, l_bytes, q, q_bytes))
+    return fail(CP_E_INVALID, "%s: outputs overlap inputs or each other", fn);
+  cpattn::AttnArgs a{};
+  for (int64_t c = 0; c < P; ++c) {
+    const cp_kv_chunk& ch = chunks[c];
+    if (ch.len == 0) continue;
+    if (!ch.k || !ch.v) return fail(CP_E_INVALID, "%s: chunk %lld has a null pointer", fn,
+                                    (long long)c);
+    if (!aligned(ch.k, 16) || !aligned(ch.v, 16))
+      return fail(CP_E_INVALID, "%s: chunk %lld is misaligned", fn, (long long)c);
+    const int64_t kv_bytes = sat_mul({B, ch.len, H, D, es});
+    if (overlap(o, o_bytes, ch.k, kv_bytes) || overlap(o, o_bytes, ch.v, kv_bytes) ||
+        overlap(lse, l_bytes, ch.k, kv_bytes) || overlap(lse, l_bytes, ch.v, kv_bytes))
+      return fail(CP_E_INVALID, "%s: outputs overlap chunk %lld", fn, (long long)c);
+  }
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.B = static_cast<int32_t>(B);
+  a.H = static_cast<int32_t>(H);
+  a.Sq = static_cast<int32_t>(Sq);
+  a.D = static_cast<int32_t>(D);
+  a.scale = scale;
+  a.nchunks = static_cast<int32_t>(P);
+  for (int64_t c = 0; c < P; ++c) {
+    a.chunks[c].k = chunks[c].k;
+    a.chunks[c].v = chunks[c].v;
+    a.chunks[c].len = static_cast<int32_t>(chunks[c].len);
+    a.chunks[c].delta = clamp_delta(q_pos0, chunks[c].pos0, Sq, chunks[c].len);
+  }
+  (void)workspace;
+  return launch_attention(fn, a, in_dtype, in_dtype == CP_BF16, causal,
+                          static_cast<hipStream_t>(stream));
+}
+
+static cp_status relayout(const char* fn, const void* in, void* out, int64_t P, int64_t B,
+                          int64_t S_local, int64_t H, int64_t D, cp_dtype dtype, void* stream,
+                          bool seq2head) {
+  if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
+  if (B < 0 || S_local < 0 || H < 0 || D < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
+  if (!valid_dtype(dtype)) return fail(CP_E_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (H % P != 0)
+    return fail(CP_E_DIVISIBILITY, "%s: H=%lld heads do not divide by P=%lld", fn, (long long)H,
+                (long long)P);
+  if (B == 0 || S_local == 0 || H == 0 || D == 0) return ok();
+  if (!in || !out) return fail(CP_E_INVALID, "%s: null pointer", fn);
+  const int es = elem_size(dtype);
+  if (!aligned(in, es) || !aligned(out, es))
+    return fail(CP_E_INVALID, "%s: pointer not aligned to the element size", fn);
+  const int64_t bytes = sat_mul({P, B, S_local, H, D, es});
+  if (overlap(in, bytes, out, bytes)) return fail(CP_E_INVALID, "%s: out overlaps in", fn);
+  cpattn::RelayoutDesc d{P, B, S_local, H, D, es, seq2head};
+  const int w = cpattn::relayout_word_bytes(in, out, d);
+  if (bytes / w >= (int64_t(1) << 31) || sat_mul({P, B, S_local, P}) >= (int64_t(1) << 31))
+    return fail(CP_E_UNSUPPORTED, "%s: tensor of %lld bytes too large for one launch", fn,
+                (long long)bytes);
+  return hip_status(cpattn::launch_relayout(in, out, d, static_cast<hipStream_t>(stream)), fn);
+}
+
+cp_status cp_ulysses_seq2head(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                              int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  return relayout("cp_ulysses_seq2head", in, out, P, B, S_local, H, D, dtype, stream, true);
+}
+
+cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                              int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  return relayout("cp_ulysses_head2seq", in, out, P, B, S_local, H, D, dtype, stream, false);
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations shared by the HIP translation units of libcpattn.
+// Not part of the public ABI (include/cp_attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cp_attn.h"
+
+namespace cpattn {
+
+// Unsigned 32-bit division by a divisor fixed at launch time, as a multiply
+// and shifts (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (t + ((n - t) >> 1)) >> (l - 1)
+// where t = mulhi(n, m), exact for every 32-bit n. d == 1 is special-cased.
+struct FastDiv {
+  uint32_t d;
+  uint32_t mul;
+  uint32_t shift;  // l - 1 (unused when d == 1)
+  __host__ void init(uint32_t div) {
+    d = div;
+    uint32_t l = 0;
+    while ((1ull << l) < div) ++l;
+    shift = l == 0 ? 0 : l - 1;
+    mul = static_cast<uint32_t>(((1ull << 32) * ((1ull << l) - div)) / div + 1);
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    if (d == 1) return n;
+    uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(n) * mul) >> 32);
+    return (t + ((n - t) >> 1)) >> shift;
+  }
+};
+
+// ----- relayout (relayout.hip)
+struct RelayoutDesc {
+  int64_t P, B, S_local, H, D;
+  int elem_bytes;
+  bool seq2head;
+};
+int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d);
+hipError_t launch_relayout(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream);
+
+// ----- merge (lse_merge.hip)
+hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, void* o,
+                            float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, bool out_bf16,
+                            hipStream_t stream);
+
+// ----- attention (attn_bf16.hip, attn_f32.hip)
+struct ChunkDesc {
+  const void* k;
+  const void* v;
+  int32_t len;
+  int32_t delta;  // q_pos0 - chunk pos0, clamped to [-(Sq+1), len+1]
+};
+
+struct AttnArgs {
+  const void* q;
+  void* o;
+  float* lse;
+  int32_t B, H, Sq, D;
+  float scale;
+  int32_t nchunks;
+  ChunkDesc chunks[CP_MAX_RING_CHUNKS];
+};
+
+// out_bf16: write O as bf16 (else fp32). causal: position-based masking.
+hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, bool causal, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,136 @@
+// Ulysses sequence-shard <-> head-shard relayout for all P ranks of one group.
+//
+// The first Ulysses all-to-all leaves every rank holding all tokens for a
+// subset of heads, and the second one regroups the attention output by token
+// (Context parallelism guide (diffusers), section Ulysses Attention). With the
+// transport removed, both are one permutation of contiguous runs:
+//   seq2head: out[p][b][q*S_l + s][h][d] = in[q][b][s][p*H_l + h][d]
+//   head2seq: out[q][b][s][p*H_l + h][d] = in[p][b][q*S_l + s][h][d]
+// Each run is H_l*D contiguous elements on both sides, so the kernel is a
+// streaming copy: every work-item moves whole UNIT-byte words (16 bytes when
+// the run length and both pointers allow it), consecutive lanes touch
+// consecutive words of a run, and loads/stores are non-temporal because each
+// byte is read once and written once.
+#include "cp_internal.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnitsPerThread = 4;
+
+template <int UNIT>
+struct Word;
+template <>
+struct Word<16> { typedef uint32_t T __attribute__((ext_vector_type(4))); };
+template <>
+struct Word<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <>
+struct Word<4> { using T = uint32_t; };
+template <>
+struct Word<2> { using T = uint16_t; };
+
+struct Geometry {
+  uint32_t total;       // words in the tensor
+  FastDiv run;          // words per run (H_l*D*elem/UNIT)
+  FastDiv seq;          // S_local
+  FastDiv batch;        // B
+  FastDiv seqP;         // P*S_local: tokens of one head shard
+  FastDiv P;            // ranks
+};
+
+// Source word index for output word u.
+template <bool SEQ2HEAD>
+__device__ __forceinline__ uint32_t source_index(uint32_t u, const Geometry& g) {
+  const uint32_t r = g.run.div(u);           // output run index
+  const uint32_t w = u - r * g.run.d;        // word within the run
+  if (SEQ2HEAD) {
+    // output run r = (p*B + b)*(P*S_l) + t, t = q*S_l + s
+    const uint32_t pb = g.seqP.div(r);
+    const uint32_t t = r - pb * g.seqP.d;
+    const uint32_t p = g.batch.div(pb);
+    const uint32_t b = pb - p * g.batch.d;
+    const uint32_t q = g.seq.div(t);
+    const uint32_t s = t - q * g.seq.d;
+    // input run (q, b, s) holds P runs back to back; take the p-th
+    const uint32_t in_row = (q * g.batch.d + b) * g.seq.d + s;
+    return (in_row * g.P.d + p) * g.run.d + w;
+  } else {
+    // output row (q*B + b)*S_l + s holds P runs; r = row*P + p
+    const uint32_t row = g.P.div(r);
+    const uint32_t p = r - row * g.P.d;
+    const uint32_t qb = g.seq.div(row);
+    const uint32_t s = row - qb * g.seq.d;
+    const uint32_t q = g.batch.div(qb);
+    const uint32_t b = qb - q * g.batch.d;
+    // input run (p, b, q*S_l + s)
+    const uint32_t in_run = (p * g.batch.d + b) * g.seqP.d + q * g.seq.d + s;
+    return in_run * g.run.d + w;
+  }
+}
+
+template <int UNIT, bool SEQ2HEAD>
+__global__ __launch_bounds__(kThreads) void relayout_kernel(const void* __restrict__ in_,
+                                                            void* __restrict__ out_, Geometry g) {
+  using T = typename Word<UNIT>::T;
+  const T* in = static_cast<const T*>(in_);
+  T* out = static_cast<T*>(out_);
+  const uint32_t base = blockIdx.x * (kThreads * kUnitsPerThread) + threadIdx.x;
+  T v[kUnitsPerThread];
+  uint32_t dst[kUnitsPerThread];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const uint32_t u = base + i * kThreads;
+    dst[i] = u;
+    if (u < g.total) v[i] = __builtin_nontemporal_load(in + source_index<SEQ2HEAD>(u, g));
+  }
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    if (dst[i] < g.total) __builtin_nontemporal_store(v[i], out + dst[i]);
+  }
+}
+
+template <int UNIT>
+hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream) {
+  const int64_t run_bytes = (d.H / d.P) * d.D * d.elem_bytes;
+  const int64_t total_bytes = d.P * d.B * d.S_local * d.H * d.D * d.elem_bytes;
+  Geometry g;
+  g.total = static_cast<uint32_t>(total_bytes / UNIT);
+  g.run.init(static_cast<uint32_t>(run_bytes / UNIT));
+  g.seq.init(static_cast<uint32_t>(d.S_local));
+  g.batch.init(static_cast<uint32_t>(d.B));
+  g.seqP.init(static_cast<uint32_t>(d.P * d.S_local));
+  g.P.init(static_cast<uint32_t>(d.P));
+  const uint32_t per_block = kThreads * kUnitsPerThread;
+  const uint32_t blocks = (g.total + per_block - 1) / per_block;
+  if (d.seq2head)
+    hipLaunchKernelGGL((relayout_kernel<UNIT, true>), dim3(blocks), dim3(kThreads), 0, stream, in,
+                       out, g);
+  else
+    hipLaunchKernelGGL((relayout_kernel<UNIT, false>), dim3(blocks), dim3(kThreads), 0, stream,
+                       in, out, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Widest word that divides the run length and both base addresses.
+int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d) {
+  const int64_t run_bytes = (d.H / d.P) * d.D * d.elem_bytes;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out);
+  for (int w = 16; w > 2; w /= 2)
+    if (run_bytes % w == 0 && align % w == 0) return w;
+  return 2;
+}
+
+// The caller has checked that the tensor holds fewer than 2^31 words.
+hipError_t launch_relayout(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream) {
+  switch (relayout_word_bytes(in, out, d)) {
+    case 16: return launch_unit<16>(in, out, d, stream);
+    case 8: return launch_unit<8>(in, out, d, stream);
+    case 4: return launch_unit<4>(in, out, d, stream);
+    default: return launch_unit<2>(in, out, d, stream);
+  }
+}
+
+}  // namespace cpattn

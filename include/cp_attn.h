@@ -1,0 +1,196 @@
+/*
+ * cp_attn.h — C ABI of the MI355X (gfx950) context-parallel attention library.
+ *
+ * One rank's share of block-wise softmax attention, as context parallelism
+ * runs it inside the attention backend, plus the Ulysses layout transforms
+ * around it. Everything runs on one GPU; the exchanges between ranks (ring
+ * rotation, all-to-all) are not part of this library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense and contiguous, BSHD: element [b][s][h][d] sits at
+ *    ((b*S + s)*H + h)*D + d. LSE tensors are fp32 [B][H][S]:
+ *    element [b][h][s] at (b*H + h)*S + s.
+ *  - "LSE" is the natural log of the row's softmax normaliser, scale
+ *    included: LSE_i = ln sum_j exp(scale * <q_i, k_j>). A row that sees no
+ *    key has LSE = -inf and output 0 (never NaN).
+ *  - Device pointers are plain device addresses (from hipMalloc or PyTorch).
+ *    The caller allocates and owns every device buffer; the library never
+ *    allocates or frees device memory. Outputs must not overlap inputs.
+ *    Tensor pointers must be 16-byte aligned; LSE pointers 4-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it and no call synchronises: results are valid once
+ *    the stream has reached that point.
+ *  - Arguments are validated on the host before anything is enqueued. On any
+ *    error the call returns a non-zero cp_status, enqueues nothing, leaves
+ *    every output untouched, and cp_last_error() describes the problem. A
+ *    launch failure reported by the HIP runtime returns CP_E_HIP.
+ *  - Zero-sized work (B, H or Sq equal to 0) is a successful no-op. Negative
+ *    sizes are CP_E_INVALID.
+ *  - Repeating a call on identical inputs gives byte-identical outputs
+ *    (fixed reduction order, no floating-point atomics).
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CP_BF16 = 0, CP_F32 = 1 } cp_dtype;
+
+typedef enum {
+  CP_OK = 0,
+  CP_E_INVALID = 1,      /* null/misaligned/overlapping pointer, negative size, bad flag */
+  CP_E_UNSUPPORTED = 2,  /* head dim, dtype combination or size outside what is built  */
+  CP_E_DIVISIBILITY = 3, /* Ulysses: H or the sequence does not divide by P            */
+  CP_E_WORKSPACE = 4,    /* workspace missing or smaller than required                 */
+  CP_E_HIP = 5           /* the HIP runtime reported an error at launch                */
+} cp_status;
+
+/* One K/V chunk of a ring: K and V are [B][len][H][D] in the call's dtype.
+ * pos0 is the global position of the chunk's first key (causal masking only). */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t len;
+  int64_t pos0;
+} cp_kv_chunk;
+
+/* Largest ring degree cp_ring_attention accepts in one call. */
+#define CP_MAX_RING_CHUNKS 64
+
+/*
+ * cp_attn_chunk_partial — one ring hop: attention of a Q shard over ONE K/V chunk.
+ *
+ * Defined by: the Context parallelism guide (diffusers), section Ring
+ * Attention (each GPU attends its Q to the K/V block it holds), and the
+ * diffusers parallel API, ContextParallelConfig (convert_to_fp32: each hop's
+ * output and LSE are kept in float32 for the merge). With one chunk covering
+ * the whole sequence it is the local attention a Ulysses rank runs between
+ * its two all-to-alls (Ulysses Sequence Parallelism article, detailed notes 4).
+ *
+ *   q [B][Sq][H][D], k and v [B][Skv][H][D], dtype in_dtype.
+ *   o [B][Sq][H][D] in o_dtype: O_i = sum_j exp(S_ij - LSE_i) v_j over this chunk.
+ *   lse [B][H][Sq] fp32: LSE_i = ln sum_j exp(S_ij), S_ij = scale * <q_i, k_j>.
+ *   causal != 0: key j is visible to query i iff kv_pos0 + j <= q_pos0 + i
+ *   (causal masking from position ids, Ulysses Sequence Parallelism article,
+ *   detailed notes 7); causal == 0 ignores the positions.
+ *
+ * Supported: D in {64, 128}; in_dtype CP_BF16 with o_dtype CP_F32 or CP_BF16
+ * (bf16 MFMA products, fp32 accumulation, softmax in fp32, probabilities
+ * rounded to bf16 for the P*V product); in_dtype CP_F32 with o_dtype CP_F32
+ * (fp32 throughout). Skv == 0 is allowed: every row gets O = 0, LSE = -inf.
+ * Limits: Sq, Skv < 2^30. scale must be finite.
+ */
+cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                cp_dtype in_dtype, cp_dtype o_dtype, float scale, int causal,
+                                int64_t q_pos0, int64_t kv_pos0, void* stream);
+
+/*
+ * cp_lse_merge — merge P partial (O_c, LSE_c) pairs into attention over all their keys.
+ *
+ * Defined by: the diffusers parallel API, ContextParallelConfig
+ * (convert_to_fp32: outputs and LSE converted to float32 for a stable merge)
+ * and the Sequence Parallelism page (SGLang Diffusion), section Numerics
+ * across node boundaries (hops are merged by online softmax). Per row:
+ *   M = max_c LSE_c;  LSE = M + ln sum_c exp(LSE_c - M);
+ *   O = sum_c exp(LSE_c - LSE) * O_c;   all LSE_c = -inf gives O = 0, LSE = -inf.
+ *
+ *   o_parts [P][B][Sq][H][D] fp32, lse_parts [P][B][H][Sq] fp32 (P >= 1).
+ *   o [B][Sq][H][D] in o_dtype (CP_F32, or CP_BF16 rounded to nearest even);
+ *   lse [B][H][Sq] fp32. D must be a multiple of 4. The partials are combined
+ *   in the fixed order c = 0..P-1.
+ */
+cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, void* o,
+                       float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, cp_dtype o_dtype,
+                       void* stream);
+
+/*
+ * cp_ring_attention_workspace_bytes — device workspace cp_ring_attention needs
+ * for these sizes (may be 0). Pure host function; never fails (returns 0 for
+ * invalid sizes, which cp_ring_attention then rejects).
+ */
+size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D);
+
+/*
+ * cp_ring_attention — one ring rank's whole share: Q attends P K/V chunks in
+ * the given order and the per-chunk results are merged in fp32.
+ *
+ * Defined by: the Context parallelism guide (diffusers), sections Ring
+ * Attention (K/V blocks visit every rank; after a full turn each rank has
+ * attended every token) and Ring Anything Attention (chunks of unequal length:
+ * padding is sliced away before attention, so uneven lengths are accepted
+ * here as they are), and the diffusers parallel API, ContextParallelConfig
+ * (rotate_method "allgather": every chunk is resident when attention runs;
+ * convert_to_fp32). The merge is fused: the running output and LSE stay in
+ * fp32 across chunks and O is rounded to in_dtype once at the end.
+ *
+ *   q [B][Sq][H][D] in in_dtype; chunks: a HOST array of P descriptors in
+ *   visit order (read during the call only), each K/V [B][len][H][D].
+ *   o [B][Sq][H][D] in in_dtype; lse [B][H][Sq] fp32.
+ *   causal != 0: key j of chunk c is visible to query i iff
+ *   chunks[c].pos0 + j <= q_pos0 + i.
+ *   workspace: device buffer of at least
+ *   cp_ring_attention_workspace_bytes(P, B, H, Sq, D) bytes (NULL if 0), owned
+ *   by the caller, contents need no initialisation and are scratch afterwards;
+ *   concurrent calls must not share one workspace.
+ *
+ * 0 <= P <= CP_MAX_RING_CHUNKS; chunk lengths may differ and may be 0. Same D
+ * and dtype support as cp_attn_chunk_partial (O in in_dtype).
+ */
+cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
+                            float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                            cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cp_ulysses_seq2head — the Ulysses regrouping before attention, for all P
+ * ranks at once (pack + unpack of the first all-to-all, transport removed).
+ *
+ * Defined by: the Context parallelism guide (diffusers), section Ulysses
+ * Attention (the first all-to-all leaves each GPU holding every token for a
+ * subset of heads) and the Ulysses Sequence Parallelism article, detailed
+ * notes 3-4. Destination rank p receives the contiguous head group
+ * [p*H/P, (p+1)*H/P); tokens are concatenated in source-rank order:
+ *   out[p][b][q*S_local + s][h][d] = in[q][b][s][p*(H/P) + h][d]
+ *
+ *   in  [P][B][S_local][H][D]    (source rank q's sequence shard is in[q])
+ *   out [P][B][P*S_local][H/P][D] (destination rank p's head shard is out[p])
+ * A pure bit copy in the element size of dtype (2 bytes for CP_BF16, 4 for
+ * CP_F32): NaN payloads, infinities and -0 are moved unchanged.
+ * H % P != 0 is CP_E_DIVISIBILITY (the standard Ulysses mode needs the heads
+ * to divide by the degree; it fails rather than padding). P >= 1, any D >= 1.
+ */
+cp_status cp_ulysses_seq2head(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                              int64_t H, int64_t D, cp_dtype dtype, void* stream);
+
+/*
+ * cp_ulysses_head2seq — the Ulysses regrouping after attention: the exact
+ * inverse of cp_ulysses_seq2head (the second all-to-all regroups the output
+ * by token, same passages as above):
+ *   out[q][b][s][p*(H/P) + h][d] = in[p][b][q*S_local + s][h][d]
+ *
+ *   in  [P][B][P*S_local][H/P][D], out [P][B][S_local][H][D]; H is the FULL
+ *   head count. Same dtype, divisibility and bit-copy rules as seq2head.
+ */
+cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                              int64_t H, int64_t D, cp_dtype dtype, void* stream);
+
+/* Text describing the last failed call on this thread ("" after a successful
+ * call). Valid until the next cp_* call on the same thread. */
+const char* cp_last_error(void);
+
+/* ABI version of this header (incremented on incompatible changes). */
+#define CP_ATTN_ABI_VERSION 1
+int cp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

@@ -1,0 +1,162 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before anything reaches the GPU.
+
+No call here launches work: every call either fails validation or is a
+zero-sized no-op, both of which return before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cp_attn.h")
+
+cp = pytest.importorskip("context_attention_dit_amd")
+lib = ctypes.CDLL(cp.LIB_PATH)
+
+OK, INVALID, UNSUPPORTED, DIVISIBILITY, WORKSPACE = 0, 1, 2, 3, 4
+BF16, F32 = 0, 1
+FAKE = 0x7f0000000000      # a 16-byte aligned address that is never dereferenced
+FAKE2 = 0x7f1000000000
+FAKE3 = 0x7f2000000000
+FAKE4 = 0x7f3000000000
+FAKE5 = 0x7f4000000000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(cp_\w+)\s*\(", text, re.M)))
+
+
+def test_header_functions_exported():
+    names = _declared_functions()
+    assert {"cp_attn_chunk_partial", "cp_lse_merge", "cp_ring_attention",
+            "cp_ring_attention_workspace_bytes", "cp_ulysses_seq2head", "cp_ulysses_head2seq",
+            "cp_last_error", "cp_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in cp_attn.h but not exported"
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define\s+CP_ATTN_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert cp.abi_version() == int(m.group(1))
+
+
+def test_max_chunks_matches_header():
+    m = re.search(r"#define\s+CP_MAX_RING_CHUNKS\s+(\d+)", open(HEADER).read())
+    assert cp.MAX_RING_CHUNKS == int(m.group(1))
+
+
+def _partial(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, Skv=8, D=128,
+             dt=BF16, odt=F32, scale=0.1, causal=0, qp=0, kp=0):
+    return cp._chunk_partial(q, k, v, o, lse, B, H, Sq, Skv, D, dt, odt, scale, causal, qp, kp, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), UNSUPPORTED),
+    (dict(D=0), UNSUPPORTED),
+    (dict(B=-1), INVALID),
+    (dict(Sq=-3), INVALID),
+    (dict(Skv=-1), INVALID),
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(q=FAKE + 8), INVALID),
+    (dict(lse=FAKE5 + 2), INVALID),
+    (dict(o=FAKE + 64), INVALID),           # output overlaps q
+    (dict(lse=FAKE2 + 16), INVALID),        # lse overlaps k
+    (dict(dt=F32, odt=BF16), UNSUPPORTED),
+    (dict(dt=7), INVALID),
+    (dict(odt=9), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(Sq=1 << 30), UNSUPPORTED),
+    (dict(Skv=1 << 30), UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 20), UNSUPPORTED),
+])
+def test_chunk_partial_rejects(kw, status):
+    assert _partial(**kw) == status
+    assert cp.last_error().startswith("cp_attn_chunk_partial")
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Sq=0), dict(Sq=0, q=None, o=None)])
+def test_chunk_partial_zero_size_is_noop(kw):
+    assert _partial(**kw) == OK
+    assert cp.last_error() == ""
+
+
+def _merge(o_parts=FAKE, lse_parts=FAKE2, P=4, o=FAKE3, lse=FAKE4, B=1, H=2, Sq=8, D=128, odt=F32):
+    return cp._lse_merge(o_parts, lse_parts, P, o, lse, B, H, Sq, D, odt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), INVALID), (dict(P=-1), INVALID), (dict(D=6), UNSUPPORTED), (dict(o=None), INVALID),
+    (dict(lse_parts=FAKE2 + 2), INVALID), (dict(o=FAKE + 128), INVALID), (dict(odt=3), INVALID),
+    (dict(B=-2), INVALID),
+])
+def test_merge_rejects(kw, status):
+    assert _merge(**kw) == status
+    assert cp.last_error().startswith("cp_lse_merge")
+
+
+def test_merge_zero_size_is_noop():
+    assert _merge(Sq=0) == OK
+
+
+def _ring(P=4, chunks=None, q=FAKE, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, D=128, dt=BF16, scale=0.1,
+          causal=0, ws=None, ws_bytes=0):
+    if chunks is None:
+        chunks = [(FAKE2 + c * 4096, FAKE3 + c * 4096, 8, 8 * c) for c in range(max(P, 0))]
+    arr = (cp.KVChunk * max(1, len(chunks)))(*[cp.KVChunk(*c) for c in chunks])
+    return cp._ring(q, arr, P, o, lse, B, H, Sq, D, dt, scale, causal, 0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=-1), INVALID), (dict(P=65), UNSUPPORTED), (dict(D=32), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(o=FAKE + 16), INVALID),
+    (dict(chunks=[(FAKE2, None, 8, 0)], P=1), INVALID),
+    (dict(chunks=[(FAKE2, FAKE3, -1, 0)], P=1), INVALID),
+    (dict(chunks=[(FAKE2 + 4, FAKE3, 8, 0)], P=1), INVALID),
+    (dict(chunks=[(FAKE4, FAKE3, 8, 0)], P=1), INVALID),      # output overlaps a chunk
+    (dict(dt=F32, D=96), UNSUPPORTED),
+])
+def test_ring_rejects(kw, status):
+    assert _ring(**kw) == status
+    assert cp.last_error().startswith("cp_ring_attention")
+
+
+def test_ring_zero_size_is_noop_and_workspace_query():
+    assert _ring(Sq=0) == OK
+    n = cp.ring_attention_workspace_bytes(4, 1, 24, 1152, 128)
+    assert n >= 0
+    if n > 0:
+        assert _ring(ws=None, ws_bytes=0) == WORKSPACE
+
+
+def _relayout(fn, inp=FAKE, out=FAKE2, P=4, B=1, S=8, H=8, D=128, dt=BF16):
+    return fn(inp, out, P, B, S, H, D, dt, None)
+
+
+@pytest.mark.parametrize("name", ["_seq2head", "_head2seq"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=6), DIVISIBILITY), (dict(H=10, P=3), DIVISIBILITY), (dict(P=0), INVALID),
+    (dict(B=-1), INVALID), (dict(inp=None), INVALID), (dict(out=FAKE + 256), INVALID),
+    (dict(dt=5), INVALID), (dict(inp=FAKE + 1), INVALID),
+])
+def test_relayout_rejects(name, kw, status):
+    fn = getattr(cp, name)
+    assert _relayout(fn, **kw) == status
+    assert cp.last_error().startswith("cp_ulysses")
+
+
+def test_relayout_zero_size_is_noop():
+    assert _relayout(cp._seq2head, S=0) == OK
+    assert _relayout(cp._head2seq, D=0, inp=None, out=None) == OK
+
+
+def test_error_text_cleared_by_success():
+    assert _partial(D=96) == UNSUPPORTED and cp.last_error() != ""
+    assert _partial(Sq=0) == OK and cp.last_error() == ""

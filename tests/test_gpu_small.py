@@ -1,0 +1,322 @@
+"""GPU parity at small sizes: several tiles, ragged tails, edge cases.
+
+Every case draws seeded inputs from ``synthetic``, runs the HIP library
+through the C ABI, and compares element by element with the fp64 oracle.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests._parity import (check_lse, check_o, kind_of, say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import context_attention_dit_amd as cp
+DEV = "cuda:0"
+
+
+def _qkv(B, Sq, Skv, H, D, dtype, seed):
+    q = synthetic.make_tensor((B, Sq, H, D), dtype, seed)
+    k = synthetic.make_tensor((B, Skv, H, D), dtype, seed + 1)
+    v = synthetic.make_tensor((B, Skv, H, D), dtype, seed + 2)
+    return q, k, v
+
+
+# ------------------------------------------------------------------- relayout
+
+@pytest.mark.parametrize("P,B,S_l,H,D,dtype", [
+    (2, 1, 128, 2, 64, torch.float32),     # the tiny workload's relayout
+    (4, 1, 37, 8, 128, torch.bfloat16),
+    (4, 2, 5, 24, 128, torch.bfloat16),
+    (8, 1, 3, 40, 128, torch.bfloat16),
+    (1, 2, 7, 3, 64, torch.bfloat16),      # P = 1 is a copy
+    (3, 2, 4, 6, 3, torch.bfloat16),       # 2-byte words
+    (2, 1, 9, 4, 5, torch.float32),        # 4-byte words
+    (4, 1, 6, 8, 2, torch.bfloat16),       # 4-byte runs
+])
+def test_relayout_bit_exact(P, B, S_l, H, D, dtype):
+    say(f"relayout P={P} B={B} S_l={S_l} H={H} D={D} {dtype}")
+    isz = 2 if dtype == torch.bfloat16 else 4
+    bits = synthetic.random_bits((P, B, S_l, H, D), isz, seed=P * 100 + D)
+    x = bits.view(dtype).to(DEV)
+    y = cp.ulysses_seq2head(x, P)
+    z = cp.ulysses_head2seq(y, P)
+    torch.cuda.synchronize()
+    want = oracle.seq2head(bits.numpy(), P)
+    assert np.array_equal(y.cpu().view(bits.dtype).numpy(), want)
+    assert np.array_equal(z.cpu().view(bits.dtype).numpy(), bits.numpy())
+    # head2seq on independent random bits against its own oracle
+    bits2 = synthetic.random_bits(tuple(want.shape), isz, seed=P * 100 + D + 1)
+    w2 = cp.ulysses_head2seq(bits2.view(dtype).to(DEV), P)
+    torch.cuda.synchronize()
+    assert np.array_equal(w2.cpu().view(bits.dtype).numpy(), oracle.head2seq(bits2.numpy(), P))
+
+
+def test_relayout_misaligned_base_uses_narrow_words():
+    say("relayout with 2-byte-offset base pointers")
+    P, B, S_l, H, D = 2, 1, 4, 4, 64
+    bits = synthetic.random_bits((P * B * S_l * H * D + 1,), 2, seed=5)
+    buf = bits.view(torch.bfloat16).to(DEV)
+    x = buf[1:].view(P, B, S_l, H, D)           # base is 2 bytes off 16-byte alignment
+    out = torch.empty(P * B * S_l * H * D + 1, dtype=torch.bfloat16, device=DEV)
+    y = out[1:].view(P, B, P * S_l, H // P, D)
+    cp._check("cp_ulysses_seq2head", cp._seq2head(x.data_ptr(), y.data_ptr(), P, B, S_l, H, D,
+                                                  0, torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    want = oracle.seq2head(bits.numpy()[1:].reshape(P, B, S_l, H, D), P)
+    assert np.array_equal(y.cpu().view(torch.int16).numpy(), want)
+
+
+# ---------------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("P", [1, 2, 4, 7])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_matches_oracle(P, out_dtype):
+    say(f"merge P={P} out={out_dtype}")
+    B, Sq, H, D = 2, 77, 3, 128
+    o_parts = synthetic.make_tensor((P, B, Sq, H, D), torch.float32, 10 + P)
+    lse_parts = synthetic.make_tensor((P, B, H, Sq), torch.float32, 20 + P) * 3.0
+    lse_parts[:, 0, 1, :5] = -math.inf           # rows no chunk saw
+    if P > 1:
+        lse_parts[0, 1, 2, 10:20] = -math.inf    # rows one chunk did not see
+    o, lse = cp.lse_merge(o_parts.to(DEV), lse_parts.to(DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    wo, wl = oracle.lse_merge(o_parts.numpy(), lse_parts.numpy())
+    if out_dtype == torch.float32:
+        check_o(o, wo, "f32")
+    else:
+        # bf16 output is the fp32 merge rounded once: within one bf16 ulp of the
+        # oracle rounded to bf16 (the partials here reach |x| ~ 5, where bf16's
+        # own spacing exceeds the attention tolerance)
+        w16 = to_f64(torch.from_numpy(wo).to(torch.bfloat16))
+        ulp = np.maximum(np.abs(w16), 2.0 ** -126) * 2.0 ** -7
+        assert np.all(np.abs(to_f64(o) - w16) <= ulp)
+    check_lse(lse, wl)
+    assert np.all(to_f64(o)[0, :5, 1] == 0)
+
+
+# -------------------------------------------------------- chunk partial attention
+
+CASES = [
+    # B, Sq, Skv, H, D, causal, q_pos0, kv_pos0
+    (1, 256, 256, 2, 64, False, 0, 0),
+    (2, 300, 333, 3, 128, False, 0, 0),
+    (1, 129, 65, 2, 128, True, 64, 0),
+    (1, 200, 200, 2, 128, True, 0, 0),
+    (2, 77, 190, 2, 64, True, 150, 40),
+    (1, 1, 1, 1, 128, False, 0, 0),
+    (1, 130, 70, 1, 128, True, 0, 100),   # many rows see nothing
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("in_dtype,out_dtype", [(torch.bfloat16, torch.float32),
+                                                (torch.bfloat16, torch.bfloat16),
+                                                (torch.float32, torch.float32)])
+def test_chunk_partial(case, in_dtype, out_dtype):
+    B, Sq, Skv, H, D, causal, qp, kp = case
+    say(f"chunk_partial {case} {in_dtype}->{out_dtype}")
+    q, k, v = _qkv(B, Sq, Skv, H, D, in_dtype, seed=Sq * 7 + Skv)
+    scale = 1 / math.sqrt(D)
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal,
+                                   q_pos0=qp, kv_pos0=kp, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    wo, wl = oracle.chunk_partial(to_f64(q), to_f64(k), to_f64(v), scale, causal,
+                                  np.arange(qp, qp + Sq), np.arange(kp, kp + Skv))
+    kind = "bf16" if (in_dtype == torch.bfloat16) else "f32"
+    check_o(o, wo, kind)
+    check_lse(lse, wl)
+
+
+@pytest.mark.parametrize("in_dtype", [torch.bfloat16, torch.float32])
+def test_chunk_partial_no_keys(in_dtype):
+    say(f"chunk_partial Skv=0 {in_dtype}")
+    q = synthetic.make_tensor((1, 70, 2, 128), in_dtype, 3).to(DEV)
+    k = torch.empty((1, 0, 2, 128), dtype=in_dtype, device=DEV)
+    o = torch.full((1, 70, 2, 128), 7.0, device=DEV)
+    lse = torch.full((1, 2, 70), 7.0, device=DEV)
+    cp.attn_chunk_partial(q, k, k, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_stress_inputs():
+    """Peaky softmax (Q x 8) and all-equal keys (uniform closed form)."""
+    w = synthetic.FLUX_RING
+    q, k, v = synthetic.make_qkv(w, S=320, H=2, scale_q=8.0)
+    say("stress: peaky softmax")
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(128))
+    check_o(o, wo, "bf16")
+    check_lse(lse, wl)
+    say("stress: all keys equal")
+    k_eq = k[:, :1].expand_as(k).contiguous()
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k_eq.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mean_v = to_f64(v).mean(axis=1, keepdims=True)
+    check_o(o, np.broadcast_to(mean_v, wo.shape), "bf16")
+
+
+# ------------------------------------------------------------------------ ring
+
+def _chunk_tensors(k, v, lens):
+    out, acc = [], 0
+    for n in lens:
+        out.append((k[:, acc:acc + n].contiguous(), v[:, acc:acc + n].contiguous(), acc))
+        acc += n
+    return out
+
+
+def test_tiny_ring_all_ranks_all_orders():
+    """The tiny fp32 workload: ring degree 4, every rank, all 24 visit orders."""
+    w = synthetic.TINY
+    q, k, v = synthetic.make_qkv(w)
+    scale = 1 / math.sqrt(w.D)
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
+    chunks = _chunk_tensors(k.to(DEV), v.to(DEV), w.chunk_lens)
+    n = w.S // w.P
+    for r in range(w.P):
+        qs = q[:, r * n:(r + 1) * n].contiguous().to(DEV)
+        for order in itertools.permutations(range(w.P)):
+            say(f"tiny ring rank {r} order {order}")
+            o, lse = cp.ring_attention(qs, [chunks[c] for c in order], scale=scale)
+            torch.cuda.synchronize()
+            check_o(o, wo[:, r * n:(r + 1) * n], "f32")
+            check_lse(lse, wl[:, :, r * n:(r + 1) * n])
+    # the whole Q in one call
+    o, lse = cp.ring_attention(q.to(DEV), chunks, scale=scale)
+    torch.cuda.synchronize()
+    check_o(o, wo, "f32")
+    check_lse(lse, wl)
+
+
+@pytest.mark.parametrize("lens,causal,in_dtype", [
+    ((100, 100, 100, 100), False, torch.bfloat16),
+    ((129, 0, 64, 200), True, torch.bfloat16),     # an empty chunk
+    ((7, 300, 1, 65, 33), True, torch.bfloat16),
+    ((250,), False, torch.bfloat16),
+    ((90, 90, 91), True, torch.float32),
+    ((64, 64), False, torch.float32),
+])
+def test_ring_uneven_chunks(lens, causal, in_dtype):
+    S = sum(lens)
+    P = len(lens)
+    H, D = 2, 128
+    q, k, v = _qkv(1, S, S, H, D, in_dtype, seed=S + P)
+    scale = 1 / math.sqrt(D)
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale, causal)
+    chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
+    starts = [0] + list(np.cumsum(lens)[:-1])
+    for r in range(P):
+        if lens[r] == 0:
+            continue
+        s0, n = starts[r], lens[r]
+        order = synthetic.ring_order(r, P)
+        say(f"ring lens={lens} rank={r} causal={causal} {in_dtype}")
+        o, lse = cp.ring_attention(q[:, s0:s0 + n].contiguous().to(DEV), [chunks[c] for c in order],
+                                   scale=scale, causal=causal, q_pos0=int(s0))
+        torch.cuda.synchronize()
+        check_o(o, wo[:, s0:s0 + n], kind_of(in_dtype))
+        check_lse(lse, wl[:, :, s0:s0 + n])
+
+
+def test_ring_zero_chunks():
+    say("ring with P = 0")
+    q = synthetic.make_tensor((1, 40, 2, 64), torch.bfloat16, 1).to(DEV)
+    o, lse = cp.ring_attention(q, [])
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_partials_plus_merge_equal_ring():
+    """Per-hop partials merged by cp_lse_merge agree with the fused ring (bf16)."""
+    lens = (96, 160, 128, 64)
+    S, H, D = sum(lens), 3, 128
+    q, k, v = _qkv(1, S, S, H, D, torch.bfloat16, seed=99)
+    chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
+    qd = q[:, 96:256].contiguous().to(DEV)
+    order = synthetic.ring_order(1, 4)
+    say("partials + merge vs fused ring")
+    parts = [cp.attn_chunk_partial(qd, chunks[c][0], chunks[c][1], causal=True, q_pos0=96,
+                                   kv_pos0=chunks[c][2]) for c in order]
+    po = torch.stack([p[0] for p in parts])
+    pl = torch.stack([p[1] for p in parts])
+    mo, ml = cp.lse_merge(po, pl, out_dtype=torch.bfloat16)
+    ro, rl = cp.ring_attention(qd, [chunks[c] for c in order], causal=True, q_pos0=96)
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), True)
+    for o, l in ((mo, ml), (ro, rl)):
+        check_o(o, wo[:, 96:256], "bf16")
+        check_lse(l, wl[:, :, 96:256])
+    # the GPU partials themselves against the oracle's per-chunk partials
+    for (o_c, l_c), c in zip(parts, order):
+        kc, vc, p0 = chunks[c]
+        w_o, w_l = oracle.chunk_partial(to_f64(q[:, 96:256]), to_f64(kc), to_f64(vc),
+                                        1 / math.sqrt(D), True, np.arange(96, 256),
+                                        np.arange(p0, p0 + lens[c]))
+        check_o(o_c, w_o, "bf16", f"O_{c}")
+        check_lse(l_c, w_l, f"LSE_{c}")
+
+
+# ----------------------------------------------------------- determinism / guards
+
+def test_repeat_runs_are_byte_identical():
+    q, k, v = _qkv(1, 333, 500, 3, 128, torch.bfloat16, seed=7)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    chunks = _chunk_tensors(k, v, (200, 300))
+    say("determinism")
+    a = [cp.attn_chunk_partial(q, k, v, causal=True), cp.ring_attention(q, chunks, causal=True)]
+    b = [cp.attn_chunk_partial(q, k, v, causal=True), cp.ring_attention(q, chunks, causal=True)]
+    parts_o = torch.stack([a[0][0], a[0][0]])
+    parts_l = torch.stack([a[0][1], a[0][1] - 1.0])
+    m1 = cp.lse_merge(parts_o, parts_l)
+    m2 = cp.lse_merge(parts_o, parts_l)
+    torch.cuda.synchronize()
+    for (o1, l1), (o2, l2) in zip(a + [m1], b + [m2]):
+        assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8))
+        assert torch.equal(l1.view(torch.uint8), l2.view(torch.uint8))
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Canary regions around every output are untouched (no out-of-bounds writes)."""
+    B, Sq, Skv, H, D = 1, 157, 201, 2, 128
+    q, k, v = _qkv(B, Sq, Skv, H, D, torch.bfloat16, seed=11)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    pad = 4096
+    n_o, n_l = B * Sq * H * D, B * H * Sq
+    o_buf = torch.full((n_o + 2 * pad,), 12345.0, device=DEV)
+    l_buf = torch.full((n_l + 2 * pad,), 12345.0, device=DEV)
+    o = o_buf[pad:pad + n_o].view(B, Sq, H, D)
+    lse = l_buf[pad:pad + n_l].view(B, H, Sq)
+    say("canaries")
+    cp.attn_chunk_partial(q, k, v, o, lse, causal=True, q_pos0=50)
+    x = synthetic.make_tensor((4, 1, 13, 8, 128), torch.bfloat16, 2).to(DEV)
+    y_buf = torch.full((x.numel() + 2 * pad,), 3.0, dtype=torch.bfloat16, device=DEV)
+    cp.ulysses_seq2head(x, 4, y_buf[pad:pad + x.numel()].view(4, 1, 52, 2, 128))
+    torch.cuda.synchronize()
+    for buf, n, val in ((o_buf, n_o, 12345.0), (l_buf, n_l, 12345.0), (y_buf, x.numel(), 3.0)):
+        assert torch.all(buf[:pad] == val) and torch.all(buf[pad + n:] == val)
+
+
+def test_rejected_call_leaves_outputs_untouched():
+    q = synthetic.make_tensor((1, 64, 6, 128), torch.bfloat16, 1).to(DEV)
+    o = torch.full((1, 64, 6, 128), 5.0, device=DEV)
+    lse = torch.full((1, 6, 64), 5.0, device=DEV)
+    say("rejected calls")
+    with pytest.raises(cp.CpAttnError):
+        cp.attn_chunk_partial(q, q, q, o, lse, scale=float("nan"))
+    x = synthetic.make_tensor((4, 1, 8, 6, 128), torch.bfloat16, 2).to(DEV)
+    y = torch.full((4, 1, 32, 1, 128), 5.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(cp.CpAttnError) as e:
+        cp._check("cp_ulysses_seq2head", cp._seq2head(x.data_ptr(), y.data_ptr(), 4, 1, 8, 6, 128,
+                                                      0, None))
+    assert e.value.status == 3
+    torch.cuda.synchronize()
+    assert torch.all(o == 5.0) and torch.all(lse == 5.0) and torch.all(y == 5.0)

@@ -1,0 +1,125 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
+
+Outputs the oracle can afford are compared in full (FLUX ring rank, the
+ring-anything split of 4099 tokens); for the long Ulysses sequences the oracle
+computes a sample of query rows one by one (first rows, last rows and seeded
+random rows of every local head) against the full K/V, with explicit
+positions. Relayouts are compared bit for bit with the oracle's permutation.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests._parity import check_lse, check_o, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import context_attention_dit_amd as cp
+DEV = "cuda:0"
+
+
+def _rows(S, n_edge, n_rand, seed):
+    rng = np.random.default_rng(seed)
+    r = set(range(min(n_edge, S))) | set(range(max(0, S - n_edge), S))
+    r |= set(rng.choice(S, size=min(n_rand, S), replace=False).tolist())
+    return np.array(sorted(r))
+
+
+def _ring_chunks(w, k, v):
+    starts = w.chunk_starts()
+    return [(k[:, s:s + n].contiguous(), v[:, s:s + n].contiguous(), s)
+            for s, n in zip(starts, w.chunk_lens)]
+
+
+def test_flux_ring_rank0_full():
+    """FLUX 1024x1024 ring rank 0: 1152 query rows over 4 chunks in order [0,3,2,1]."""
+    w = synthetic.FLUX_RING
+    say(f"{w.name}: generating inputs")
+    q, k, v = synthetic.make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    chunks = _ring_chunks(w, kd, vd)
+    order = synthetic.ring_order(0, w.P)
+    assert order == [0, 3, 2, 1]
+    n = w.chunk_lens[0]
+    q0 = qd[:, :n].contiguous()
+    say(f"{w.name}: fused ring")
+    o, lse = cp.ring_attention(q0, [chunks[c] for c in order])
+    say(f"{w.name}: partials + merge")
+    parts = [cp.attn_chunk_partial(q0, chunks[c][0], chunks[c][1]) for c in order]
+    mo, ml = cp.lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
+                          out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    say(f"{w.name}: oracle")
+    wo, wl = oracle.attention(to_f64(q[:, :n]), to_f64(k), to_f64(v), 1 / math.sqrt(w.D))
+    check_o(o, wo, "bf16", "ring O")
+    check_lse(lse, wl, "ring LSE")
+    check_o(mo, wo, "bf16", "merged O")
+    check_lse(ml, wl, "merged LSE")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_anything_4099_all_ranks(causal):
+    """S = 4099 split 1025/1025/1025/1024, every rank in its ring order."""
+    w = synthetic.LLM_RING_ANYTHING
+    say(f"{w.name} causal={causal}: inputs")
+    q, k, v = synthetic.make_qkv(w)
+    kd, vd = k.to(DEV), v.to(DEV)
+    chunks = _ring_chunks(w, kd, vd)
+    starts = w.chunk_starts()
+    outs = []
+    for r in range(w.P):
+        s0, n = starts[r], w.chunk_lens[r]
+        say(f"{w.name} causal={causal}: rank {r}")
+        outs.append(cp.ring_attention(q[:, s0:s0 + n].contiguous().to(DEV),
+                                      [chunks[c] for c in synthetic.ring_order(r, w.P)],
+                                      causal=causal, q_pos0=s0))
+    torch.cuda.synchronize()
+    say(f"{w.name} causal={causal}: oracle")
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(w.D), causal)
+    for r, (o, lse) in enumerate(outs):
+        s0, n = starts[r], w.chunk_lens[r]
+        check_o(o, wo[:, s0:s0 + n], "bf16", f"rank {r} O")
+        check_lse(lse, wl[:, :, s0:s0 + n], f"rank {r} LSE")
+
+
+@pytest.mark.parametrize("wname,n_edge,n_rand", [
+    ("qwen-image-1536-ulysses4-rank0", 192, 384),
+    ("wan-21x30x52-ulysses8-rank0", 96, 192),
+    ("llm-128k-causal-ulysses8-rank0", 96, 160),
+])
+def test_ulysses_rank0(wname, n_edge, n_rand):
+    """seq2head of Q, K, V for all ranks; rank 0's local attention; head2seq back."""
+    w = synthetic.WORKLOADS[wname]
+    P, S_l, H, D = w.P, w.S_local, w.H, w.D
+    say(f"{w.name}: generating inputs")
+    q, k, v = synthetic.make_qkv(w)
+    shards = [x.view(P, 1, S_l, H, D).to(DEV) for x in (q, k, v)]
+    say(f"{w.name}: seq2head x3")
+    qh, kh, vh = (cp.ulysses_seq2head(x, P) for x in shards)
+    torch.cuda.synchronize()
+    say(f"{w.name}: seq2head vs oracle (Q)")
+    want = oracle.seq2head(q.view(torch.int16).numpy().reshape(P, 1, S_l, H, D), P)
+    assert np.array_equal(qh.cpu().view(torch.int16).numpy(), want)
+    del want
+    say(f"{w.name}: rank 0 attention (causal={w.causal})")
+    o, lse = cp.attn_chunk_partial(qh[0], kh[0], vh[0], causal=w.causal, out_dtype=torch.bfloat16)
+    say(f"{w.name}: head2seq")
+    back = cp.ulysses_head2seq(kh, P)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), shards[1].view(torch.int16))
+    del back, shards
+    rows = _rows(w.S, n_edge, n_rand, seed=w.seed)
+    say(f"{w.name}: oracle on {len(rows)} rows x {w.H_local} heads")
+    heads = slice(0, w.H_local)
+    qf = to_f64(q[:, rows][:, :, heads])
+    wo, wl = oracle.attention(qf, to_f64(k[:, :, heads]), to_f64(v[:, :, heads]),
+                              1 / math.sqrt(D), w.causal, q_pos=rows, k_pos=np.arange(w.S))
+    got_o = o[:, torch.from_numpy(rows).to(DEV)]
+    got_l = lse[:, :, torch.from_numpy(rows).to(DEV)]
+    check_o(got_o, wo, "bf16", "rank 0 O (sampled rows)")
+    check_lse(got_l, wl, "rank 0 LSE (sampled rows)")
