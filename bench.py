@@ -129,6 +129,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path "
@@ -142,6 +144,14 @@ def main() -> int:
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 256 MiB x 5 (read 268435456 B, write 268435456 B per launch)")
+        return 0
     flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def flush():
