@@ -21,6 +21,11 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file extra flags. The bf16 attention kernel never produces NaN, so its
+# fmax reductions need no NaN canonicalisation (v_max3_f32 directly).
+FILE_FLAGS = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def _hipcc() -> str:
     h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(h):
@@ -30,7 +35,8 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o",
+           obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

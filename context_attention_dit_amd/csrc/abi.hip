@@ -74,6 +74,9 @@ cp_status check_attn_common(const char* fn, int64_t B, int64_t H, int64_t Sq, in
   if (D != 64 && D != 128)
     return fail(CP_E_UNSUPPORTED, "%s: head dim D=%lld not built (64 or 128)", fn, (long long)D);
   if (Sq >= kMaxSeq) return fail(CP_E_UNSUPPORTED, "%s: Sq=%lld exceeds 2^30", fn, (long long)Sq);
+  // the kernels address a 64-key tile with 32-bit offsets: 64*H*D < 2^31
+  if (H > (int64_t(1) << 24) / D)
+    return fail(CP_E_UNSUPPORTED, "%s: H*D=%lld exceeds 2^24", fn, (long long)(H * D));
   // query tiles x batch x heads must fit one launch grid (64-row tiles worst case)
   if (sat_mul({(Sq + 63) / 64, B, H}) > kMaxGrid / 8)
     return fail(CP_E_UNSUPPORTED, "%s: B*H*Sq too large for one launch", fn);

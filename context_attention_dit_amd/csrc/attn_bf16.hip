@@ -12,13 +12,15 @@
 // How it maps to the hardware:
 //  * A block is 4 wavefronts; each wave owns 32 query rows, so a block covers
 //    128 rows of one (batch, head). K/V tiles of 64 keys are shared by the 4
-//    waves through double-buffered LDS (one barrier per tile).
+//    waves through double-buffered LDS, filled by direct global->LDS loads
+//    (global_load_lds_dwordx4: no staging registers, no LDS store
+//    instructions); one barrier per tile.
 //  * The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = a K
 //    tile from LDS, B = Q^T held in registers for the whole kernel). In the
 //    32x32 accumulator layout lane l holds query column l%32, so every
 //    softmax statistic is a per-lane value: the row max and row sum are
 //    in-lane reductions plus one exchange between the two half-waves.
-//  * K rows are written to LDS with key bits 2 and 3 swapped. With that, the
+//  * K rows sit in LDS with key bits 2 and 3 swapped. With that, the
 //    accumulator registers of lane l hold 8 consecutive keys per half-wave,
 //    which is exactly the B-operand layout of the next product, so P (rounded
 //    to bf16) feeds O^T += V^T P^T without any data movement.
@@ -26,17 +28,17 @@
 //    ds_read_b64_tr_b16 (within each 16-lane group, lane i addresses row
 //    k0 + i/4, columns d0 + 4(i%4) .. +3, and receives column d0 + i of rows
 //    k0 .. k0+3).
-//  * LDS row padding: K rows are D+8 elements (8 consecutive rows read at one
-//    column land on distinct 16-byte bank groups), V rows are D+16 (the 4
-//    rows a transposed read touches land on distinct 32-byte bank groups).
+//  * LDS rows are unpadded and XOR-swizzled in 16-byte units (K: unit ^ row,
+//    so the 8/16 consecutive rows one fragment read touches hit distinct
+//    banks; V: 32-byte chunk ^ (row & 3), so the 4 rows of a transposed read
+//    do). The global->LDS copy applies the swizzle by choosing each lane's
+//    source address.
 //  * Softmax in the log2 domain with scale*log2(e) folded into one FMA per
 //    score. The exponent offset m is only raised when a tile's row max
 //    exceeds it by more than kTau (then O and the row sum are rescaled), so
 //    probabilities stay <= 2^kTau and the rescale is rare; the final
 //    normalisation uses the same offsets, so the result is unchanged up to
 //    rounding.
-//  * Masked and unmasked tiles take separate code paths; only ragged tails
-//    and causal diagonal tiles pay for masking.
 //  * Non-causal grids map blocks to XCDs so that the tiles of one head stay
 //    on one XCD's L2; causal grids launch the heaviest query tiles first.
 #include "cp_internal.h"
@@ -73,139 +75,40 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 
 template <int D>
-struct Tile {
-  static constexpr int kStrideK = D + 8;   // bf16 elements per K row in LDS
-  static constexpr int kStrideV = D + 16;  // bf16 elements per V row in LDS
-  static constexpr int kUPR = D / 8;       // 16-byte units per key row
-  static constexpr int kUnits = kBN * kUPR / kThreads;  // units per thread per tensor
-  static constexpr int kKeyStep = kThreads / kUPR;       // key distance between a thread's units
-  static constexpr int kLdsK = kBN * kStrideK;
-  static constexpr int kLdsV = kBN * kStrideV;
+struct Geo {
+  static constexpr int kUPR = D / 8;                      // 16-byte units per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kBN * kRowBytes;      // one K or V tile
+  static constexpr int kLoadsPerWave = kBN * kUPR / kThreads;  // direct loads per wave per tensor
+  static constexpr int kKMask = kUPR - 1 < 15 ? kUPR - 1 : 15;  // K swizzle row bits
 };
 
+// LDS byte layout of one pipeline stage: [K tile][V tile]; two stages.
 template <int D>
-struct Staged {
-  u32x4 k[Tile<D>::kUnits];
-  u32x4 v[Tile<D>::kUnits];
-};
-
-// Global -> registers for one tile. kp/vp point at this thread's first unit
-// of the tile; rows are `rs` elements apart. Keys at or beyond `n_valid`
-// (relative to the tile) read as 0.
-template <int D, bool TAIL>
-__device__ __forceinline__ void load_tile(Staged<D>& st, const __bf16* kp, const __bf16* vp,
-                                          int64_t rs, int key_t, int n_valid) {
-#pragma unroll
-  for (int r = 0; r < Tile<D>::kUnits; ++r) {
-    const int64_t off = r * Tile<D>::kKeyStep * rs;
-    if (!TAIL || key_t + r * Tile<D>::kKeyStep < n_valid) {
-      st.k[r] = *reinterpret_cast<const u32x4*>(kp + off);
-      st.v[r] = *reinterpret_cast<const u32x4*>(vp + off);
-    } else {
-      st.k[r] = u32x4{0, 0, 0, 0};
-      st.v[r] = u32x4{0, 0, 0, 0};
-    }
-  }
+__device__ __forceinline__ uint32_t k_unit_off(int row, int unit) {
+  return row * Geo<D>::kRowBytes + ((unit ^ (row & Geo<D>::kKMask)) << 4);
+}
+template <int D>
+__device__ __forceinline__ uint32_t v_unit_off(int row, int unit) {
+  return row * Geo<D>::kRowBytes + ((unit ^ ((row & 3) << 1)) << 4);
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const Staged<D>& st, __bf16* k_lds, __bf16* v_lds,
-                                           int key_t, int dg) {
-#pragma unroll
-  for (int r = 0; r < Tile<D>::kUnits; ++r) {
-    const int key = key_t + r * Tile<D>::kKeyStep;
-    *reinterpret_cast<u32x4*>(k_lds + swap_bits23(key) * Tile<D>::kStrideK + dg * 8) = st.k[r];
-    *reinterpret_cast<u32x4*>(v_lds + key * Tile<D>::kStrideV + dg * 8) = st.v[r];
-  }
+__device__ __forceinline__ void lds_load16(const __bf16* g, __bf16* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
 
-__device__ __forceinline__ bf16x4 read_tr(const __bf16* p) {
+__device__ __forceinline__ bf16x4 read_tr(const char* p) {
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Per-wave online-softmax state and accumulators.
-template <int D>
-struct WaveState {
-  f32x16 o[D / 32];
-  float m;  // exponent offset, log2 domain
-  float l;  // this lane's share of the row sum
-};
-
-// One 64-key tile for one wave: S^T = K Q^T, softmax update, O^T += V^T P^T.
-template <int D, bool MASKED, bool CAUSAL>
-__device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8* qf, const __bf16* k_lds,
-                                          const __bf16* v_lds, float sl2, int col, int half,
-                                          int key0, int len, int i, int delta, int vt_off) {
-  f32x16 sacc[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const __bf16* kr = k_lds + (32 * mb + col) * Tile<D>::kStrideK + 8 * half;
-    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(kr), qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int ks = 1; ks < D / 16; ++ks)
-      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], sacc[mb], 0, 0, 0);
-  }
-  // register r of block mb holds key key0 + 32*mb + 16*(r/8) + 8*half + r%8
-  if (MASKED) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = key0 + 32 * mb + 16 * (r >> 3) + 8 * half + (r & 7);
-        bool vis = j < len;
-        if (CAUSAL) vis = vis && (j <= i + delta);
-        sacc[mb][r] = vis ? sacc[mb][r] : -INFINITY;
-      }
-  }
-  float mx = fmaxf(sacc[0][0], sacc[0][1]);
-#pragma unroll
-  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[0][r + 1]));
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[1][r], sacc[1][r + 1]));
-  mx = pair_max(mx) * sl2;
-  if (__ballot(mx > ws.m + kTau)) {
-    asm volatile("" ::: "memory");
-    const float m_new = fmaxf(ws.m, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m - m_new);
-    ws.l *= alpha;
-#pragma unroll
-    for (int md = 0; md < D / 32; ++md) ws.o[md] *= alpha;
-    ws.m = m_new;
-  }
-  const float neg_m = ws.m == -INFINITY ? 0.f : -ws.m;
-  bf16x8 pf[4];
-  float psum = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p =
-          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
-      psum += p;
-      pf[t][e] = static_cast<__bf16>(p);
-    }
-  ws.l += psum;
-#pragma unroll
-  for (int md = 0; md < D / 32; ++md) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const __bf16* vr = v_lds + vt_off + (16 * t) * Tile<D>::kStrideV + 32 * md;
-      const bf16x4 lo = read_tr(vr);
-      const bf16x4 hi = read_tr(vr + 4 * Tile<D>::kStrideV);
-      const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      ws.o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], ws.o[md], 0, 0, 0);
-    }
-  }
-}
-
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][Tile<D>::kLdsK];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][Tile<D>::kLdsV];
+  constexpr int UPR = Geo<D>::kUPR;
+  constexpr int TB = Geo<D>::kTileBytes;
+  constexpr int NL = Geo<D>::kLoadsPerWave;
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -234,8 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- Q^T fragments (B operand), resident for the whole kernel. A negative
   //      scale is folded into Q (bf16 negation is exact).
-  const float scale_abs = fabsf(a.scale);
-  const float sl2 = fmaxf(scale_abs * kLog2e, 1e-30f);
+  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   bf16x8 qf[D / 16];
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
@@ -251,98 +153,172 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  WaveState<D> ws;
+  // ---- direct-load geometry: this lane fills LDS slot s = wave*NL*64 + n*64 + lane
+  //      of each tensor tile; slot s is (row s/UPR, swizzled unit s%UPR).
+  const int rs = a.H * D;  // elements between consecutive keys (host checks 64*rs < 2^31)
+  int ld_row[NL], k_src[NL], v_src[NL];
 #pragma unroll
-  for (int md = 0; md < D / 32; ++md) ws.o[md] = f32x16{};
-  ws.m = -INFINITY;
-  ws.l = 0.f;
+  for (int n = 0; n < NL; ++n) {
+    const int s = (wave * NL + n) * 64 + lane;
+    const int row = s / UPR, pu = s % UPR;
+    ld_row[n] = row;
+    const int k_key = swap_bits23(row), k_unit = pu ^ (row & Geo<D>::kKMask);
+    const int v_unit = pu ^ ((row & 3) << 1);
+    k_src[n] = k_key * rs + k_unit * 8;
+    v_src[n] = row * rs + v_unit * 8;
+  }
+  // issue the direct loads of one tile into stage `stg`; keys >= n_valid are
+  // redirected to the last valid key (their probabilities are exactly 0)
+  auto issue = [&](int stg, int c, int kt, int n_valid) {
+    const __bf16* kb = static_cast<const __bf16*>(a.chunks[c].k) +
+                       (static_cast<int64_t>(b) * a.chunks[c].len + kt * kBN) * rs + h * D;
+    const __bf16* vb = static_cast<const __bf16*>(a.chunks[c].v) +
+                       (static_cast<int64_t>(b) * a.chunks[c].len + kt * kBN) * rs + h * D;
+    char* kl = smem[stg] + wave * NL * 1024;
+    char* vl = smem[stg] + TB + wave * NL * 1024;
+    if (n_valid >= kBN) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        lds_load16(kb + k_src[n], reinterpret_cast<__bf16*>(kl + n * 1024));
+        lds_load16(vb + v_src[n], reinterpret_cast<__bf16*>(vl + n * 1024));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const int kk = swap_bits23(ld_row[n]), vk = ld_row[n];
+        const int kfix = kk < n_valid ? 0 : (n_valid - 1 - kk) * rs;
+        const int vfix = vk < n_valid ? 0 : (n_valid - 1 - vk) * rs;
+        lds_load16(kb + k_src[n] + kfix, reinterpret_cast<__bf16*>(kl + n * 1024));
+        lds_load16(vb + v_src[n] + vfix, reinterpret_cast<__bf16*>(vl + n * 1024));
+      }
+    }
+  };
 
-  // ---- staging geometry of this thread
-  const int dg = tid % Tile<D>::kUPR;
-  const int key_t = tid / Tile<D>::kUPR;
-  const int64_t rs = static_cast<int64_t>(a.H) * D;  // elements between consecutive keys
-  const int64_t thr_off = static_cast<int64_t>(key_t) * rs + static_cast<int64_t>(h) * D + dg * 8;
-  // transposed V read: 16-lane group g, lane-in-group j
+  // ---- fragment read addresses (byte offsets within a stage)
+  // K: row col (+32 for the second block), unit 2*ks + half, swizzled with row bits
+  uint32_t k_rd[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = k_unit_off<D>(col, 2 * ks + half);
+  // V^T: 16-lane group g, lane j -> row 8*(g/2) + j/4, element column 16*(g%2) + 4*(j%4)
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int vt_off = (8 * (g16 >> 1) + (j16 >> 2)) * Tile<D>::kStrideV + 16 * (g16 & 1) +
-                     4 * (j16 & 3);
+  const int v_row = 8 * (g16 >> 1) + (j16 >> 2);
+  const int v_el = 16 * (g16 & 1) + 4 * (j16 & 3);
+  uint32_t v_rd[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+    v_rd[md] = TB + v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY;  // exponent offset, log2 domain
+  float l_run = 0.f;        // this lane's share of the row sum
 
   auto keys_of = [&](int c) {
     int n = a.chunks[c].len;
     if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].delta + 1));
     return n;
   };
-  auto tile_ptr = [&](int c, int kt, bool is_v) {
-    const __bf16* base = static_cast<const __bf16*>(is_v ? a.chunks[c].v : a.chunks[c].k);
-    return base + (static_cast<int64_t>(b) * a.chunks[c].len + kt * kBN) * rs + thr_off;
-  };
-  auto load = [&](Staged<D>& st, int c, int kt) {
-    const int n = keys_of(c) - kt * kBN;
-    if (n >= kBN)
-      load_tile<D, false>(st, tile_ptr(c, kt, false), tile_ptr(c, kt, true), rs, key_t, n);
-    else
-      load_tile<D, true>(st, tile_ptr(c, kt, false), tile_ptr(c, kt, true), rs, key_t, n);
-  };
-  // advance (c, kt) to the next non-empty tile; c == nchunks when done
-  auto advance = [&](int& c, int& kt) {
-    ++kt;
-    if (kt * kBN >= keys_of(c)) {
-      kt = 0;
-      ++c;
-      while (c < a.nchunks && keys_of(c) == 0) ++c;
-    }
-  };
 
   int c = 0, kt = 0;
   while (c < a.nchunks && keys_of(c) == 0) ++c;
-  Staged<D> st;
-  int buf = 0;
-  if (c < a.nchunks) {
-    load(st, c, kt);
-    store_tile<D>(st, k_lds[0], v_lds[0], key_t, dg);
-  }
-  int nc = c, nkt = kt;  // tile staged in registers next
-  if (nc < a.nchunks) {
-    advance(nc, nkt);
-    if (nc < a.nchunks) load(st, nc, nkt);
-  }
+  if (c < a.nchunks) issue(0, c, 0, keys_of(c));
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  int stg = 0;
 
   while (c < a.nchunks) {
+    const int n_keys = keys_of(c);
     const int len = a.chunks[c].len;
     const int delta = a.chunks[c].delta;
     const int key0 = kt * kBN;
-    const bool masked =
-        (key0 + kBN > len) || (CAUSAL && key0 + kBN - 1 > q_first + delta);
-    // The empty asm statements keep the two variants as separate branches
-    // (otherwise both get speculated and merged with selects).
+    // next tile
+    int nc = c, nkt = kt + 1;
+    if (nkt * kBN >= n_keys) {
+      nkt = 0;
+      ++nc;
+      while (nc < a.nchunks && keys_of(nc) == 0) ++nc;
+    }
+    if (nc < a.nchunks) issue(stg ^ 1, nc, nkt, keys_of(nc) - nkt * kBN);
+
+    const char* kl = smem[stg];
+    // ---- S^T = K Q^T for 64 keys x 32 queries
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(kl + k_rd[0] + mb * 32 * Geo<D>::kRowBytes), qf[0],
+          f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < D / 16; ++ks)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(kl + k_rd[ks] + mb * 32 * Geo<D>::kRowBytes),
+            qf[ks], sacc[mb], 0, 0, 0);
+    }
+    // register r of block mb holds key key0 + 32*mb + 16*(r/8) + 8*half + r%8
+    const bool masked = (key0 + kBN > len) || (CAUSAL && key0 + kBN - 1 > q_first + delta);
     if (masked) {
-      asm volatile("" ::: "memory");
-      tile_step<D, true, CAUSAL>(ws, qf, k_lds[buf], v_lds[buf], sl2, col, half, key0, len, i,
-                                 delta, vt_off);
-    } else {
-      asm volatile("" ::: "memory");
-      tile_step<D, false, CAUSAL>(ws, qf, k_lds[buf], v_lds[buf], sl2, col, half, key0, len, i,
-                                  delta, vt_off);
+      asm volatile("" ::: "memory");  // keeps this a real (uniform) branch
+      // visible iff j < lim, with j the key index relative to key0
+      int lim = len - key0;
+      if (CAUSAL) lim = min(lim, i + delta - key0 + 1);
+      lim -= 8 * half;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) sacc[mb][r] = -INFINITY;
     }
-    if (nc < a.nchunks) {
-      store_tile<D>(st, k_lds[buf ^ 1], v_lds[buf ^ 1], key_t, dg);
-      int c2 = nc, kt2 = nkt;
-      advance(c2, kt2);
-      if (c2 < a.nchunks) load(st, c2, kt2);
-      c = nc;
-      kt = nkt;
-      nc = c2;
-      nkt = kt2;
-    } else {
-      c = a.nchunks;
+    float mx = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[0][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    mx = pair_max(mx) * sl2;
+    if (__ballot(mx > m_run + kTau)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md) oacc[md] *= alpha;
+      m_run = m_new;
     }
-    buf ^= 1;
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    bf16x8 pf[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
+        psum += p;
+        pf[t][e] = static_cast<__bf16>(p);
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const char* vr = kl + v_rd[md] + 16 * t * Geo<D>::kRowBytes;
+        const bf16x4 lo = read_tr(vr);
+        const bf16x4 hi = read_tr(vr + 4 * Geo<D>::kRowBytes);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
+      }
+    }
+    c = nc;
+    kt = nkt;
+    stg ^= 1;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // ---- epilogue: normalise, write O and LSE
-  const float l_tot = ws.l + __shfl_xor(ws.l, 32);
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (i >= a.Sq) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
@@ -351,8 +327,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * md + 8 * g + 4 * half;
-      const float x0 = ws.o[md][4 * g] * inv, x1 = ws.o[md][4 * g + 1] * inv;
-      const float x2 = ws.o[md][4 * g + 2] * inv, x3 = ws.o[md][4 * g + 3] * inv;
+      const float x0 = oacc[md][4 * g] * inv, x1 = oacc[md][4 * g + 1] * inv;
+      const float x2 = oacc[md][4 * g + 2] * inv, x3 = oacc[md][4 * g + 3] * inv;
       if (OUT_BF16) {
         bf16x4 r;
         r[0] = static_cast<__bf16>(x0);
@@ -368,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   }
   if (half == 0)
     a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Sq + i] =
-        l_tot > 0.f ? (ws.m + __log2f(l_tot)) * kLn2 : -INFINITY;
+        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool OUT_BF16>
