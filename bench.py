@@ -128,6 +128,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None,
+                    help="run only this detail workload (qwen, wan, llm, ra, merge) after the "
+                         "headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
@@ -170,7 +173,9 @@ def main() -> int:
     vis = [chunks[c] for c in order]
     o = torch.empty_like(q0)
     lse = torch.empty((1, w.H, n), dtype=torch.float32, device=dev)
-    step = lambda: cp.ring_attention(q0, vis, o, lse)
+    ws_bytes = cp.ring_attention_workspace_bytes(w.P, 1, w.H, n, w.D)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    step = lambda: cp.ring_attention(q0, vis, o, lse, workspace=ws)
     flops = attn_flops(n, w.S, w.H, w.D, False)
     log(f"{w.name}: warmup {args.warmup}, timed {args.steps}")
     for _ in range(args.warmup):
@@ -195,7 +200,7 @@ def main() -> int:
     detail = {"flux_ring_rank0": {"us_per_step": ms_step * 1e3, "kernel_us": launch_ms * 1e3,
                                   "tflops": achieved, "gflop": flops / 1e9}}
     if not args.quick:
-        detail.update(other_workloads(torch, cp, synthetic, dev, flush, q0, vis, w))
+        detail.update(other_workloads(torch, cp, synthetic, dev, flush, q0, vis, w, args.only))
     del flush_buf
 
     traffic = traffic_record()
@@ -223,9 +228,24 @@ def main() -> int:
     return 0
 
 
-def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf):
+def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
     out = {}
+    want = (lambda tag: only is None or only == tag)
     # standalone merge of the FLUX ring's 4 fp32 partials (HBM-bound)
+    if want("merge"):
+        out.update(merge_workload(torch, cp, dev, flush, q0, vis, wf))
+    tags = {synthetic.QWEN_ULYSSES.name: "qwen", synthetic.WAN_ULYSSES.name: "wan",
+            synthetic.LLM_ULYSSES.name: "llm"}
+    for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
+        if want(tags[w.name]):
+            out[w.name] = ulysses_workload(torch, cp, synthetic, dev, flush, w)
+    if want("ra"):
+        out[synthetic.LLM_RING_ANYTHING.name] = ring_anything_workload(torch, cp, synthetic, dev)
+    return out
+
+
+def merge_workload(torch, cp, dev, flush, q0, vis, wf):
+    out = {}
     parts = [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis]
     po = torch.stack([p[0] for p in parts])
     pl = torch.stack([p[1] for p in parts])
@@ -241,44 +261,48 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf):
     d = time_launches(torch, lambda: [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis], 2,
                       10)
     out["flux_partials_x4"] = {"us": median(d) * 1e3}
-    del po, pl, mo, ml
+    return out
 
-    for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
-        log(f"{w.name}: inputs")
-        P, S_l, H, D = w.P, w.S_local, w.H, w.D
-        qkv = [x.view(P, 1, S_l, H, D).to(dev) for x in synthetic.make_qkv(w)]
-        heads = [torch.empty((P, 1, w.S, w.H_local, D), dtype=w.dtype, device=dev) for _ in qkv]
-        nbytes = qkv[0].numel() * qkv[0].element_size() * 2    # read + write, one tensor
-        d_s2h = time_launches(torch, lambda: cp.ulysses_seq2head(qkv[0], P, heads[0]), 2, 10,
-                              flush)
-        for x, y in zip(qkv, heads):
-            cp.ulysses_seq2head(x, P, y)
-        rq, rk, rv = (y[0] for y in heads)
-        o = torch.empty_like(rq)
-        lse = torch.empty((1, w.H_local, w.S), dtype=torch.float32, device=dev)
-        flops = 4.0 * D * w.H_local * (causal_pairs_square(w.S) if w.causal else w.S * w.S)
-        reps = 3 if w.causal else 10
-        d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
-            rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)
-        back = torch.empty_like(qkv[0])
-        d_h2s = time_launches(torch, lambda: cp.ulysses_head2seq(heads[1], P, back), 2, 10, flush)
-        out[w.name] = {
-            "attn_us": median(d_att) * 1e3,
-            "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
-            "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "seq2head_us": median(d_s2h) * 1e3,
-            "seq2head_gbs": nbytes / (median(d_s2h) * 1e-3) / 1e9,
-            "head2seq_us": median(d_h2s) * 1e3,
-            "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
-            "relayout_bytes_per_tensor": nbytes,
-            "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "causal": w.causal, "gflop": flops / 1e9,
-        }
-        log(f"{w.name}: attn {out[w.name]['attn_tflops']:.0f} TFLOP/s, seq2head "
-            f"{out[w.name]['seq2head_gbs']:.0f} GB/s, head2seq {out[w.name]['head2seq_gbs']:.0f}")
-        del qkv, heads, rq, rk, rv, o, lse, back
-        torch.cuda.empty_cache()
 
+def ulysses_workload(torch, cp, synthetic, dev, flush, w):
+    log(f"{w.name}: inputs")
+    P, S_l, H, D = w.P, w.S_local, w.H, w.D
+    qkv = [x.view(P, 1, S_l, H, D).to(dev) for x in synthetic.make_qkv(w)]
+    heads = [torch.empty((P, 1, w.S, w.H_local, D), dtype=w.dtype, device=dev) for _ in qkv]
+    nbytes = qkv[0].numel() * qkv[0].element_size() * 2    # read + write, one tensor
+    d_s2h = time_launches(torch, lambda: cp.ulysses_seq2head(qkv[0], P, heads[0]), 2, 10,
+                          flush)
+    for x, y in zip(qkv, heads):
+        cp.ulysses_seq2head(x, P, y)
+    rq, rk, rv = (y[0] for y in heads)
+    o = torch.empty_like(rq)
+    lse = torch.empty((1, w.H_local, w.S), dtype=torch.float32, device=dev)
+    flops = 4.0 * D * w.H_local * (causal_pairs_square(w.S) if w.causal else w.S * w.S)
+    reps = 3 if w.causal else 10
+    d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
+        rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)
+    back = torch.empty_like(qkv[0])
+    d_h2s = time_launches(torch, lambda: cp.ulysses_head2seq(heads[1], P, back), 2, 10, flush)
+    res = {
+        "attn_us": median(d_att) * 1e3,
+        "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
+        "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "seq2head_us": median(d_s2h) * 1e3,
+        "seq2head_gbs": nbytes / (median(d_s2h) * 1e-3) / 1e9,
+        "head2seq_us": median(d_h2s) * 1e3,
+        "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
+        "relayout_bytes_per_tensor": nbytes,
+        "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "causal": w.causal, "gflop": flops / 1e9,
+    }
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
+        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
+    del qkv, heads, rq, rk, rv, o, lse, back
+    torch.cuda.empty_cache()
+    return res
+
+
+def ring_anything_workload(torch, cp, synthetic, dev):
     w = synthetic.LLM_RING_ANYTHING
     log(f"{w.name}: ranks")
     q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
@@ -299,8 +323,7 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf):
         res["causal" if causal else "noncausal"] = {
             "us_all_ranks": tot_us, "tflops": tot_flops / (tot_us * 1e-6) / 1e12,
             "gflop": tot_flops / 1e9}
-    out[w.name] = res
-    return out
+    return res
 
 
 if __name__ == "__main__":

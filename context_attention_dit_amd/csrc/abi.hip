@@ -149,6 +149,7 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
   a.D = static_cast<int32_t>(D);
   a.scale = scale;
   a.nchunks = 1;
+  a.nsplit = 1;
   a.chunks[0].k = k;
   a.chunks[0].v = v;
   a.chunks[0].len = static_cast<int32_t>(Skv);
@@ -188,11 +189,12 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
 
 size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D) {
   (void)P;
-  (void)B;
-  (void)H;
-  (void)Sq;
-  (void)D;
-  return 0;
+  if (B <= 0 || H <= 0 || Sq <= 0 || (D != 64 && D != 128) || Sq >= kMaxSeq ||
+      sat_mul({(Sq + 63) / 64, B, H}) > kMaxGrid / 8)
+    return 0;
+  // the most key splits any chunk list can get for these sizes (long chunks)
+  const int s = cpattn::attn_split_count(B, H, Sq, int64_t(1) << 40, false);
+  return static_cast<size_t>(cpattn::attn_split_floats(s, B, H, Sq, D)) * sizeof(float);
 }
 
 cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
@@ -211,6 +213,8 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(CP_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace_bytes);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(CP_E_INVALID, "%s: workspace must be 16-byte aligned", fn);
   const int64_t es = elem_size(in_dtype);
   const int64_t q_bytes = sat_mul({B, Sq, H, D, es}), o_bytes = q_bytes;
   const int64_t l_bytes = sat_mul({B, H, Sq, 4});
@@ -224,9 +228,11 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
   if (!q || !o || !lse) return fail(CP_E_INVALID, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse 4 B)", fn);
+  const int64_t ws_bytes = static_cast<int64_t>(need);
   if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
-      overlap(lse, l_bytes, q, q_bytes))
-    return fail(CP_E_INVALID, "%s: outputs overlap inputs or each other", fn);
+      overlap(lse, l_bytes, q, q_bytes) || overlap(workspace, ws_bytes, q, q_bytes) ||
+      overlap(workspace, ws_bytes, o, o_bytes) || overlap(workspace, ws_bytes, lse, l_bytes))
+    return fail(CP_E_INVALID, "%s: outputs or workspace overlap inputs or each other", fn);
   cpattn::AttnArgs a{};
   for (int64_t c = 0; c < P; ++c) {
     const cp_kv_chunk& ch = chunks[c];
@@ -237,8 +243,9 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
       return fail(CP_E_INVALID, "%s: chunk %lld is misaligned", fn, (long long)c);
     const int64_t kv_bytes = sat_mul({B, ch.len, H, D, es});
     if (overlap(o, o_bytes, ch.k, kv_bytes) || overlap(o, o_bytes, ch.v, kv_bytes) ||
-        overlap(lse, l_bytes, ch.k, kv_bytes) || overlap(lse, l_bytes, ch.v, kv_bytes))
-      return fail(CP_E_INVALID, "%s: outputs overlap chunk %lld", fn, (long long)c);
+        overlap(lse, l_bytes, ch.k, kv_bytes) || overlap(lse, l_bytes, ch.v, kv_bytes) ||
+        overlap(workspace, ws_bytes, ch.k, kv_bytes) || overlap(workspace, ws_bytes, ch.v, kv_bytes))
+      return fail(CP_E_INVALID, "%s: outputs or workspace overlap chunk %lld", fn, (long long)c);
   }
   a.q = q;
   a.o = o;
@@ -249,13 +256,22 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
   a.D = static_cast<int32_t>(D);
   a.scale = scale;
   a.nchunks = static_cast<int32_t>(P);
+  int64_t tiles = 0;
   for (int64_t c = 0; c < P; ++c) {
     a.chunks[c].k = chunks[c].k;
     a.chunks[c].v = chunks[c].v;
     a.chunks[c].len = static_cast<int32_t>(chunks[c].len);
     a.chunks[c].delta = clamp_delta(q_pos0, chunks[c].pos0, Sq, chunks[c].len);
+    tiles += (chunks[c].len + 63) / 64;
   }
-  (void)workspace;
+  a.nsplit = 1;
+  if (in_dtype == CP_BF16) {
+    a.nsplit = cpattn::attn_split_count(B, H, Sq, tiles, causal != 0);
+    if (a.nsplit > 1) {
+      a.part_o = static_cast<float*>(workspace);
+      a.part_lse = a.part_o + a.nsplit * B * Sq * H * D;
+    }
+  }
   return launch_attention(fn, a, in_dtype, in_dtype == CP_BF16, causal,
                           static_cast<hipStream_t>(stream));
 }

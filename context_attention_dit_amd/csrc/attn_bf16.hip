@@ -59,6 +59,7 @@ constexpr int kBN = 64;           // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;      // log2 headroom before the exponent offset is raised
+constexpr int kMaxSplit = 2;      // key splits per query tile on small grids
 
 __device__ __forceinline__ int swap_bits23(int k) {
   return k ^ ((((k >> 2) ^ (k >> 3)) & 1) * 12);
@@ -114,21 +115,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
 
-  // ---- block -> (batch*head, query tile)
+  // ---- block -> (batch*head, query tile, key split)
   const int nqt = (a.Sq + kBM - 1) / kBM;
   const int BH = a.B * a.H;
-  const int ntiles = nqt * BH;
-  int bh, qt;
+  const int nsplit = CAUSAL ? 1 : a.nsplit;
+  const int nitems = nqt * BH * nsplit;
+  int bh, qt, sp = 0;
   if (CAUSAL) {
     const int L = blockIdx.x;  // heaviest (last) query tiles first
     qt = nqt - 1 - L / BH;
     bh = L % BH;
   } else {
-    const int per_xcd = (ntiles + 7) / 8;  // consecutive block ids go to different XCDs
+    const int per_xcd = (nitems + 7) / 8;  // consecutive block ids go to different XCDs
     const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (L >= ntiles) return;
-    bh = L / nqt;
-    qt = L % nqt;
+    if (L >= nitems) return;
+    const int unit = L / nsplit;
+    sp = L - unit * nsplit;
+    bh = unit / nqt;
+    qt = unit % nqt;
   }
   const int b = bh / a.H, h = bh - b * a.H;
   const int i = qt * kBM + wave * 32 + col;  // this lane's query row
@@ -170,6 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // issue the direct loads of one tile into stage `stg`; keys >= n_valid are
   // redirected to the last valid key (their probabilities are exactly 0)
   auto issue = [&](int stg, int c, int kt, int n_valid) {
+    c = __builtin_amdgcn_readfirstlane(c);
     const __bf16* kb = static_cast<const __bf16*>(a.chunks[c].k) +
                        (static_cast<int64_t>(b) * a.chunks[c].len + kt * kBN) * rs + h * D;
     const __bf16* vb = static_cast<const __bf16*>(a.chunks[c].v) +
@@ -214,27 +219,51 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY;  // exponent offset, log2 domain
   float l_run = 0.f;        // this lane's share of the row sum
 
+  // Chunk descriptors are read with a provably uniform index, so they come
+  // in through scalar loads and never wait behind the vector-memory counter
+  // that tracks the in-flight tile prefetch.
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   auto keys_of = [&](int c) {
+    c = uni(c);
     int n = a.chunks[c].len;
     if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].delta + 1));
     return n;
   };
 
-  int c = 0, kt = 0;
-  while (c < a.nchunks && keys_of(c) == 0) ++c;
-  if (c < a.nchunks) issue(0, c, 0, keys_of(c));
+  // this block's share of the query tile's tiles: [t_begin, t_end) in chunk order
+  int c = 0, kt = 0, left;
+  {
+    int total = 0;
+    for (int cc = 0; cc < a.nchunks; ++cc) total += (keys_of(cc) + kBN - 1) / kBN;
+    const int t_begin = static_cast<int>(static_cast<int64_t>(total) * sp / nsplit);
+    const int t_end = static_cast<int>(static_cast<int64_t>(total) * (sp + 1) / nsplit);
+    left = t_end - t_begin;
+    int skip = t_begin;
+    while (c < a.nchunks) {
+      const int nt = (keys_of(c) + kBN - 1) / kBN;
+      if (skip < nt) break;
+      skip -= nt;
+      ++c;
+    }
+    kt = skip;
+    if (left == 0) c = a.nchunks;
+  }
+  if (c < a.nchunks) issue(0, c, kt, keys_of(c) - kt * kBN);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int stg = 0;
 
   while (c < a.nchunks) {
+    c = uni(c);
     const int n_keys = keys_of(c);
     const int len = a.chunks[c].len;
     const int delta = a.chunks[c].delta;
     const int key0 = kt * kBN;
-    // next tile
+    // next tile of this block's share
     int nc = c, nkt = kt + 1;
-    if (nkt * kBN >= n_keys) {
+    if (--left == 0) {
+      nc = a.nchunks;
+    } else if (nkt * kBN >= n_keys) {
       nkt = 0;
       ++nc;
       while (nc < a.nchunks && keys_of(nc) == 0) ++nc;
@@ -322,6 +351,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   if (i >= a.Sq) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
+  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
+  const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (nsplit > 1) {  // fp32 partial of split sp
+    float* po = a.part_o + static_cast<int64_t>(sp) * a.B * a.Sq * a.H * D + orow;
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + 32 * md + 8 * g + 4 * half) =
+            make_float4(oacc[md][4 * g] * inv, oacc[md][4 * g + 1] * inv,
+                        oacc[md][4 * g + 2] * inv, oacc[md][4 * g + 3] * inv);
+    if (half == 0) a.part_lse[static_cast<int64_t>(sp) * a.B * a.H * a.Sq + lrow] = lse_val;
+    return;
+  }
 #pragma unroll
   for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
@@ -342,19 +385,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   }
-  if (half == 0)
-    a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Sq + i] =
-        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (half == 0) a.lse[lrow] = lse_val;
 }
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBM - 1) / kBM;
-  const int64_t ntiles = nqt * a.B * a.H;
-  const int64_t blocks = CAUSAL ? ntiles : (ntiles + 7) / 8 * 8;
+  const int64_t nsplit = CAUSAL ? 1 : a.nsplit;
+  const int64_t nitems = nqt * a.B * a.H * nsplit;
+  const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
   hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, OUT_BF16>), dim3(static_cast<uint32_t>(blocks)),
                      dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  // combine the splits' fp32 partials in split order
+  return launch_lse_merge(a.part_o, a.part_lse, static_cast<int>(nsplit), a.o, a.lse, a.B, a.H,
+                          a.Sq, D, OUT_BF16, stream);
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int D>
@@ -365,6 +425,22 @@ hipError_t launch_d(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t s
 }
 
 }  // namespace
+
+// Blocks of 128 query rows, two resident per CU. A grid that leaves CUs
+// idle is split along the keys until it covers the GPU, keeping at least 8
+// tiles per split (the merge pass costs one fp32 read/write per split).
+int attn_split_count(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal) {
+  if (causal) return 1;
+  const int64_t units = (Sq + kBM - 1) / kBM * B * H;
+  const int64_t slots = 2 * static_cast<int64_t>(device_cus());
+  int s = 1;
+  while (s < kMaxSplit && units * s < slots && tiles / (s + 1) >= 8) ++s;
+  return s;
+}
+
+int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D) {
+  return nsplit <= 1 ? 0 : nsplit * (B * Sq * H * D + B * H * Sq);
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream) {
   return a.D == 64 ? launch_d<64>(a, causal, out_bf16, stream)

@@ -61,8 +61,22 @@ struct AttnArgs {
   int32_t B, H, Sq, D;
   float scale;
   int32_t nchunks;
+  // Split of each query tile's key range over `nsplit` blocks (1 = none). With
+  // nsplit > 1 every split writes a normalised fp32 partial (O, LSE) to
+  // part_o [nsplit][B][Sq][H][D] / part_lse [nsplit][B][H][Sq], and the
+  // launcher merges them into o / lse.
+  int32_t nsplit;
+  float* part_o;
+  float* part_lse;
   ChunkDesc chunks[CP_MAX_RING_CHUNKS];
 };
+
+// Number of key splits the bf16 attention launcher uses for these sizes
+// (non-causal only; 1 when the grid already fills the GPU). `tiles` is the
+// number of 64-key tiles each query tile visits.
+int attn_split_count(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal);
+// fp32 elements of partial output the split needs: nsplit*(B*Sq*H*D + B*H*Sq).
+int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D);
 
 // out_bf16: write O as bf16 (else fp32). causal: position-based masking.
 hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream);

@@ -112,8 +112,12 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
 
 /*
  * cp_ring_attention_workspace_bytes — device workspace cp_ring_attention needs
- * for these sizes (may be 0). Pure host function; never fails (returns 0 for
- * invalid sizes, which cp_ring_attention then rejects).
+ * for these sizes (may be 0). When B*H*ceil(Sq/128) query tiles leave the
+ * GPU's compute units idle, cp_ring_attention splits each tile's keys over
+ * two blocks; the splits' fp32 (O, LSE) partials live in the workspace and
+ * are merged exactly as cp_lse_merge does. Host function; queries the current
+ * device's compute-unit count; returns 0 for invalid sizes (which
+ * cp_ring_attention then rejects).
  */
 size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D);
 
@@ -135,10 +139,10 @@ size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_
  *   o [B][Sq][H][D] in in_dtype; lse [B][H][Sq] fp32.
  *   causal != 0: key j of chunk c is visible to query i iff
  *   chunks[c].pos0 + j <= q_pos0 + i.
- *   workspace: device buffer of at least
+ *   workspace: 16-byte aligned device buffer of at least
  *   cp_ring_attention_workspace_bytes(P, B, H, Sq, D) bytes (NULL if 0), owned
  *   by the caller, contents need no initialisation and are scratch afterwards;
- *   concurrent calls must not share one workspace.
+ *   concurrent calls must not share one workspace. Too small: CP_E_WORKSPACE.
  *
  * 0 <= P <= CP_MAX_RING_CHUNKS; chunk lengths may differ and may be 0. Same D
  * and dtype support as cp_attn_chunk_partial (O in in_dtype).

@@ -23,6 +23,7 @@ FAKE2 = 0x7f1000000000
 FAKE3 = 0x7f2000000000
 FAKE4 = 0x7f3000000000
 FAKE5 = 0x7f4000000000
+FAKE6 = 0x7f5000000000     # fake workspace
 
 
 def _declared_functions():
@@ -107,7 +108,7 @@ def test_merge_zero_size_is_noop():
 
 
 def _ring(P=4, chunks=None, q=FAKE, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, D=128, dt=BF16, scale=0.1,
-          causal=0, ws=None, ws_bytes=0):
+          causal=0, ws=FAKE6, ws_bytes=1 << 30):
     if chunks is None:
         chunks = [(FAKE2 + c * 4096, FAKE3 + c * 4096, 8, 8 * c) for c in range(max(P, 0))]
     arr = (cp.KVChunk * max(1, len(chunks)))(*[cp.KVChunk(*c) for c in chunks])
@@ -122,6 +123,8 @@ def _ring(P=4, chunks=None, q=FAKE, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, D=128, d
     (dict(chunks=[(FAKE2 + 4, FAKE3, 8, 0)], P=1), INVALID),
     (dict(chunks=[(FAKE4, FAKE3, 8, 0)], P=1), INVALID),      # output overlaps a chunk
     (dict(dt=F32, D=96), UNSUPPORTED),
+    (dict(ws=FAKE6 + 8), INVALID),                             # misaligned workspace
+    (dict(ws=FAKE4 + 64), INVALID),                            # workspace overlaps the output
 ])
 def test_ring_rejects(kw, status):
     assert _ring(**kw) == status

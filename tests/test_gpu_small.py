@@ -227,6 +227,29 @@ def test_ring_uneven_chunks(lens, causal, in_dtype):
         check_lse(lse, wl[:, :, s0:s0 + n])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_ring_key_splits(causal):
+    """A small grid (2 query tiles x 2 heads) is split along the keys; splits merge exactly."""
+    lens = (700, 513, 0, 811)
+    S, H, D = sum(lens), 2, 128
+    q, k, v = _qkv(1, S, S, H, D, torch.bfloat16, seed=321)
+    chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
+    q0, n = 900, 200
+    ws = cp.ring_attention_workspace_bytes(4, 1, H, n, D)
+    assert ws > 0, "expected a split for this small grid"
+    say(f"ring with key splits causal={causal}, workspace {ws} bytes")
+    o, lse = cp.ring_attention(q[:, q0:q0 + n].contiguous().to(DEV), [chunks[c] for c in (3, 1, 0, 2)],
+                               causal=causal, q_pos0=q0)
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal)
+    check_o(o, wo[:, q0:q0 + n], "bf16")
+    check_lse(lse, wl[:, :, q0:q0 + n])
+    with pytest.raises(cp.CpAttnError) as e:
+        cp.ring_attention(q[:, q0:q0 + n].contiguous().to(DEV), chunks, causal=causal,
+                          workspace=torch.empty(ws - 16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 4
+
+
 def test_ring_zero_chunks():
     say("ring with P = 0")
     q = synthetic.make_tensor((1, 40, 2, 64), torch.bfloat16, 1).to(DEV)
