@@ -41,6 +41,8 @@
 //    rounding.
 //  * Non-causal grids map blocks to XCDs so that the tiles of one head stay
 //    on one XCD's L2; causal grids launch the heaviest query tiles first.
+#include <type_traits>
+
 #include "cp_internal.h"
 
 namespace cpattn {
@@ -109,10 +111,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int UPR = Geo<D>::kUPR;
   constexpr int TB = Geo<D>::kTileBytes;
   constexpr int NL = Geo<D>::kLoadsPerWave;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2 * TB];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // [K0][K1][V0][V1]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   // ---- block -> (batch*head, query tile, key split)
@@ -158,9 +160,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- direct-load geometry: this lane fills LDS slot s = wave*NL*64 + n*64 + lane
-  //      of each tensor tile; slot s is (row s/UPR, swizzled unit s%UPR).
+  //      of each tensor tile; slot s is (row s/UPR, swizzled unit s%UPR). The
+  //      lane's source offsets (bytes from the tile's first key) are fixed.
   const int rs = a.H * D;  // elements between consecutive keys (host checks 64*rs < 2^31)
-  int ld_row[NL], k_src[NL], v_src[NL];
+  int ld_row[NL];
+  uint32_t k_src[NL], v_src[NL];
 #pragma unroll
   for (int n = 0; n < NL; ++n) {
     const int s = (wave * NL + n) * 64 + lane;
@@ -168,56 +172,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     ld_row[n] = row;
     const int k_key = swap_bits23(row), k_unit = pu ^ (row & Geo<D>::kKMask);
     const int v_unit = pu ^ ((row & 3) << 1);
-    k_src[n] = k_key * rs + k_unit * 8;
-    v_src[n] = row * rs + v_unit * 8;
+    k_src[n] = 2u * static_cast<uint32_t>(k_key * rs + k_unit * 8);
+    v_src[n] = 2u * static_cast<uint32_t>(row * rs + v_unit * 8);
   }
-  // issue the direct loads of one tile into stage `stg`; keys >= n_valid are
-  // redirected to the last valid key (their probabilities are exactly 0)
-  auto issue = [&](int stg, int c, int kt, int n_valid) {
-    c = __builtin_amdgcn_readfirstlane(c);
-    const __bf16* kb = static_cast<const __bf16*>(a.chunks[c].k) +
-                       (static_cast<int64_t>(b) * a.chunks[c].len + kt * kBN) * rs + h * D;
-    const __bf16* vb = static_cast<const __bf16*>(a.chunks[c].v) +
-                       (static_cast<int64_t>(b) * a.chunks[c].len + kt * kBN) * rs + h * D;
-    char* kl = smem[stg] + wave * NL * 1024;
-    char* vl = smem[stg] + TB + wave * NL * 1024;
-    if (n_valid >= kBN) {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        lds_load16(kb + k_src[n], reinterpret_cast<__bf16*>(kl + n * 1024));
-        lds_load16(vb + v_src[n], reinterpret_cast<__bf16*>(vl + n * 1024));
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int kk = swap_bits23(ld_row[n]), vk = ld_row[n];
-        const int kfix = kk < n_valid ? 0 : (n_valid - 1 - kk) * rs;
-        const int vfix = vk < n_valid ? 0 : (n_valid - 1 - vk) * rs;
-        lds_load16(kb + k_src[n] + kfix, reinterpret_cast<__bf16*>(kl + n * 1024));
-        lds_load16(vb + v_src[n] + vfix, reinterpret_cast<__bf16*>(vl + n * 1024));
-      }
-    }
-  };
-
-  // ---- fragment read addresses (byte offsets within a stage)
-  // K: row col (+32 for the second block), unit 2*ks + half, swizzled with row bits
-  uint32_t k_rd[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = k_unit_off<D>(col, 2 * ks + half);
-  // V^T: 16-lane group g, lane j -> row 8*(g/2) + j/4, element column 16*(g%2) + 4*(j%4)
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int v_row = 8 * (g16 >> 1) + (j16 >> 2);
-  const int v_el = 16 * (g16 & 1) + 4 * (j16 & 3);
-  uint32_t v_rd[D / 32];
-#pragma unroll
-  for (int md = 0; md < D / 32; ++md)
-    v_rd[md] = TB + v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int md = 0; md < D / 32; ++md) oacc[md] = f32x16{};
-  float m_run = -INFINITY;  // exponent offset, log2 domain
-  float l_run = 0.f;        // this lane's share of the row sum
 
   // Chunk descriptors are read with a provably uniform index, so they come
   // in through scalar loads and never wait behind the vector-memory counter
@@ -229,50 +186,66 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].delta + 1));
     return n;
   };
-
-  // this block's share of the query tile's tiles: [t_begin, t_end) in chunk order
-  int c = 0, kt = 0, left;
-  {
-    int total = 0;
-    for (int cc = 0; cc < a.nchunks; ++cc) total += (keys_of(cc) + kBN - 1) / kBN;
-    const int t_begin = static_cast<int>(static_cast<int64_t>(total) * sp / nsplit);
-    const int t_end = static_cast<int>(static_cast<int64_t>(total) * (sp + 1) / nsplit);
-    left = t_end - t_begin;
-    int skip = t_begin;
-    while (c < a.nchunks) {
-      const int nt = (keys_of(c) + kBN - 1) / kBN;
-      if (skip < nt) break;
-      skip -= nt;
-      ++c;
+  struct Cur {
+    int c, kt;
+  };
+  auto next_of = [&](Cur x) {
+    x.c = uni(x.c);
+    x.kt = uni(x.kt) + 1;
+    if (x.kt * kBN >= keys_of(x.c)) {
+      x.kt = 0;
+      ++x.c;
+      while (x.c < a.nchunks && keys_of(x.c) == 0) ++x.c;
     }
-    kt = skip;
-    if (left == 0) c = a.nchunks;
-  }
-  if (c < a.nchunks) issue(0, c, kt, keys_of(c) - kt * kBN);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int stg = 0;
-
-  while (c < a.nchunks) {
-    c = uni(c);
-    const int n_keys = keys_of(c);
-    const int len = a.chunks[c].len;
-    const int delta = a.chunks[c].delta;
-    const int key0 = kt * kBN;
-    // next tile of this block's share
-    int nc = c, nkt = kt + 1;
-    if (--left == 0) {
-      nc = a.nchunks;
-    } else if (nkt * kBN >= n_keys) {
-      nkt = 0;
-      ++nc;
-      while (nc < a.nchunks && keys_of(nc) == 0) ++nc;
+    return x;
+  };
+  // Direct loads of one K or V tile into `dst`: a uniform base address plus
+  // the lane's fixed byte offset. Keys at or beyond the tile's valid count
+  // are redirected to its last valid key (their probabilities are exactly 0).
+  auto issue = [&](char* dst, Cur x, bool is_v) {
+    const int c = uni(x.c);
+    x.kt = uni(x.kt);
+    const int n_valid = keys_of(c) - x.kt * kBN;
+    const char* base =
+        reinterpret_cast<const char*>(is_v ? a.chunks[c].v : a.chunks[c].k) +
+        2 * ((static_cast<int64_t>(b) * a.chunks[c].len + x.kt * kBN) * rs + h * D);
+    char* l = dst + wave * NL * 1024;
+    if (n_valid >= kBN) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n)
+        lds_load16(reinterpret_cast<const __bf16*>(base + (is_v ? v_src[n] : k_src[n])),
+                   reinterpret_cast<__bf16*>(l + n * 1024));
+    } else {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const int key = is_v ? ld_row[n] : swap_bits23(ld_row[n]);
+        const uint32_t fix = key < n_valid ? 0u : 2u * static_cast<uint32_t>((key - n_valid + 1) * rs);
+        lds_load16(reinterpret_cast<const __bf16*>(base + ((is_v ? v_src[n] : k_src[n]) - fix)),
+                   reinterpret_cast<__bf16*>(l + n * 1024));
+      }
     }
-    if (nc < a.nchunks) issue(stg ^ 1, nc, nkt, keys_of(nc) - nkt * kBN);
+  };
 
-    const char* kl = smem[stg];
-    // ---- S^T = K Q^T for 64 keys x 32 queries
-    f32x16 sacc[2];
+  // ---- fragment read addresses (byte offsets within a tile)
+  // K: row col (+32 for the second block), unit 2*ks + half, swizzled with row bits
+  uint32_t k_rd[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = k_unit_off<D>(col, 2 * ks + half);
+  // V^T: 16-lane group g, lane j -> row 8*(g/2) + j/4, element column 16*(g%2) + 4*(j%4)
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_row = 8 * (g16 >> 1) + (j16 >> 2);
+  const int v_el = 16 * (g16 & 1) + 4 * (j16 & 3);
+  uint32_t v_rd[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+    v_rd[md] = v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+
+  // LDS: K tiles in slots 0/1, V tiles in slots 2/3 (TB bytes each)
+  char* const lds = smem;
+
+  // S^T = K Q^T for the 64 keys of the K tile in slot `ks_slot` (32 queries per wave)
+  auto qk = [&](int k_slot, f32x16* sacc) {
+    const char* kl = lds + k_slot * TB;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -284,11 +257,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
             *reinterpret_cast<const bf16x8*>(kl + k_rd[ks] + mb * 32 * Geo<D>::kRowBytes),
             qf[ks], sacc[mb], 0, 0, 0);
     }
-    // register r of block mb holds key key0 + 32*mb + 16*(r/8) + 8*half + r%8
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY;  // exponent offset, log2 domain
+  float l_run = 0.f;        // this lane's share of the row sum
+
+  // this block's share of the query tile's tiles, in chunk order
+  Cur cur0{0, 0};
+  int left;
+  {
+    int total = 0;
+    for (int cc = 0; cc < a.nchunks; ++cc) total += (keys_of(cc) + kBN - 1) / kBN;
+    const int t_begin = static_cast<int>(static_cast<int64_t>(total) * sp / nsplit);
+    const int t_end = static_cast<int>(static_cast<int64_t>(total) * (sp + 1) / nsplit);
+    left = uni(t_end - t_begin);
+    int skip = t_begin;
+    while (cur0.c < a.nchunks) {
+      const int nt = (keys_of(cur0.c) + kBN - 1) / kBN;
+      if (skip < nt) break;
+      skip -= nt;
+      ++cur0.c;
+    }
+    cur0.kt = skip;
+  }
+
+  // One pipeline step for tile j (cursor cur0; cur1/cur2 are tiles j+1/j+2):
+  // prefetch K of j+2 and V of j+1, then S for tile j+1 on the matrix cores
+  // while the softmax of tile j runs, then O += P V for tile j. Tile j's K
+  // and V sit in slots PAR and 2+PAR; PAR = j & 1 is a compile-time constant
+  // (the loop is unrolled by two), so every LDS offset is an immediate.
+  Cur cur1 = cur0, cur2 = cur0;
+  auto step = [&](auto par_tag, int j, f32x16* s_cur, f32x16* s_next) {
+    constexpr int PAR = decltype(par_tag)::value;
+    if (j + 2 < left) issue(lds + PAR * TB, cur2, false);
+    if (j + 1 < left) issue(lds + (3 - PAR) * TB, cur1, true);
+    const int c0 = uni(cur0.c);
+    const int len = a.chunks[c0].len;
+    const int delta = a.chunks[c0].delta;
+    const int key0 = uni(cur0.kt) * kBN;
+
+    // softmax of tile j (lane = query column; register r of block mb is key
+    // key0 + 32*mb + 16*(r/8) + 8*half + r%8)
     const bool masked = (key0 + kBN > len) || (CAUSAL && key0 + kBN - 1 > q_first + delta);
     if (masked) {
       asm volatile("" ::: "memory");  // keeps this a real (uniform) branch
-      // visible iff j < lim, with j the key index relative to key0
+      // visible iff the key index relative to key0 is < lim
       int lim = len - key0;
       if (CAUSAL) lim = min(lim, i + delta - key0 + 1);
       lim -= 8 * half;
@@ -296,13 +312,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) sacc[mb][r] = -INFINITY;
+          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s_cur[mb][r] = -INFINITY;
     }
-    float mx = fmaxf(sacc[0][0], sacc[0][1]);
+    float mx = fmaxf(fmaxf(s_cur[0][0], s_cur[0][1]), s_cur[0][2]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[0][r + 1]));
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    for (int r = 3; r < 31; r += 2)
+      mx = fmaxf(fmaxf(mx, s_cur[r >> 4][r & 15]), s_cur[(r + 1) >> 4][(r + 1) & 15]);
+    mx = fmaxf(mx, s_cur[1][15]);
     mx = pair_max(mx) * sl2;
     if (__ballot(mx > m_run + kTau)) {
       asm volatile("" ::: "memory");
@@ -314,6 +330,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+
+    // S of tile j+1 on the matrix cores while the exponentials run (for the
+    // last tile this reads a stale slot and the result is never used)
+    qk(1 - PAR, s_next);
     bf16x8 pf[4];
     float psum = 0.f;
 #pragma unroll
@@ -321,29 +341,51 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
         psum += p;
         pf[t][e] = static_cast<__bf16>(p);
       }
     l_run += psum;
 
-    // ---- O^T += V^T P^T
+    // O^T += V^T P^T for tile j
+    const char* vl = lds + (2 + PAR) * TB;
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const char* vr = kl + v_rd[md] + 16 * t * Geo<D>::kRowBytes;
+        const char* vr = vl + v_rd[md] + 16 * t * Geo<D>::kRowBytes;
         const bf16x4 lo = read_tr(vr);
         const bf16x4 hi = read_tr(vr + 4 * Geo<D>::kRowBytes);
         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
       }
     }
-    c = nc;
-    kt = nkt;
-    stg ^= 1;
+    cur0 = cur1;
+    cur1 = cur2;
+    if (j + 3 < left) cur2 = next_of(cur2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  f32x16 s_a[2], s_b[2];
+  if (left > 0) {
+    issue(lds, cur0, false);
+    issue(lds + 2 * TB, cur0, true);
+    if (left > 1) {
+      cur1 = next_of(cur0);
+      issue(lds + TB, cur1, false);
+    }
+    if (left > 2) cur2 = next_of(cur1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(0, s_a);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int j = 0; j < left; j += 2) {
+    step(std::integral_constant<int, 0>{}, j, s_a, s_b);
+    if (j + 1 >= left) break;
+    step(std::integral_constant<int, 1>{}, j + 1, s_b, s_a);
   }
 
   // ---- epilogue: normalise, write O and LSE
