@@ -292,6 +292,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   Cur cur1 = cur0, cur2 = cur0;
   auto step = [&](auto par_tag, int j, f32x16* s_cur, f32x16* s_next) {
     constexpr int PAR = decltype(par_tag)::value;
+    // cursors: cur0 = tile j, cur1 = j+1, cur2 = j+2 (the prologue set them for j = 0)
+    if (j > 0) {
+      cur0 = cur1;
+      cur1 = cur2;
+      if (j + 2 < left) cur2 = next_of(cur2);
+    }
     if (j + 2 < left) issue(lds + PAR * TB, cur2, false);
     if (j + 1 < left) issue(lds + (3 - PAR) * TB, cur1, true);
     const int c0 = uni(cur0.c);
@@ -360,9 +366,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
       }
     }
-    cur0 = cur1;
-    cur1 = cur2;
-    if (j + 3 < left) cur2 = next_of(cur2);
+    // Instruction interleave for the block above: S of tile j+1 (one MFMA
+    // per K-fragment read) with the exponentials of tile j in between, then
+    // P*V (one MFMA per two transposed V reads) with the row-sum additions.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS reads run ahead
+#pragma unroll
+    for (int k = 0; k < 2 * (D / 16); ++k) {               // S MFMAs of qk()
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);    // VALU
+    }
+#pragma unroll
+    for (int k = 0; k < 4 * (D / 32); ++k) {               // P*V MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
