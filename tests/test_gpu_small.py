@@ -250,6 +250,35 @@ def test_ring_key_splits(causal):
     assert e.value.status == 4
 
 
+@pytest.mark.parametrize("Sq,H,D,lens", [
+    (1, 1, 64, (4000,)),                   # one query row
+    (300, 3, 128, (1025, 1025, 1024)),     # 9 ragged query tiles
+    (130, 2, 64, (64, 0, 900, 77)),        # empty and one-tile chunks
+])
+def test_ring_small_grids(Sq, H, D, lens):
+    """Grids smaller than the GPU split each query tile's keys over several
+    blocks whose fp32 partials are merged. Checked against the oracle, with a
+    garbage-filled workspace, and for byte-identical repeats."""
+    S = sum(lens)
+    q, k, v = _qkv(1, Sq, S, H, D, torch.bfloat16, seed=Sq + S)
+    chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
+    qd = q.to(DEV)
+    need = cp.ring_attention_workspace_bytes(len(lens), 1, H, Sq, D)
+    assert need > 0
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    say(f"small grid Sq={Sq} H={H} D={D} lens={lens}")
+    o1, l1 = cp.ring_attention(qd, chunks, workspace=ws)
+    o2, l2 = cp.ring_attention(qd, chunks, workspace=ws)
+    o3, l3 = cp.ring_attention(qd, chunks, workspace=torch.zeros_like(ws))
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D))
+    check_o(o1, wo, "bf16")
+    check_lse(l1, wl)
+    for o, l in ((o2, l2), (o3, l3)):
+        assert torch.equal(o.view(torch.uint8), o1.view(torch.uint8))
+        assert torch.equal(l.view(torch.uint8), l1.view(torch.uint8))
+
+
 def test_ring_zero_chunks():
     say("ring with P = 0")
     q = synthetic.make_tensor((1, 40, 2, 64), torch.bfloat16, 1).to(DEV)
