@@ -70,3 +70,79 @@ def head2seq_loop(y: np.ndarray, P: int) -> np.ndarray:
                         for d in range(D):
                             out[q, b, s, p * H_l + h, d] = y[p, b, q * S_l + s, h, d]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Ulysses Anything: per-rank token counts and head counts need not be equal
+# (Context parallelism guide (diffusers), section Ulysses Anything Attention:
+# the mode drops both divisibility requirements; diffusers parallel API,
+# ContextParallelConfig: ulysses_anything). Source rank q holds tokens
+# [off_q, off_q + S_q) of the sequence, destination rank p receives the
+# contiguous heads [h0_p, h0_p + H_p):
+#
+#   seq2head:  out[p][b][off_q + s][h][d] = in[q][b][s][h0_p + h][d]
+#   head2seq:  out[q][b][s][h0_p + h][d] = in[p][b][off_q + s][h][d]
+#
+# Shards are given as lists, one array per rank.
+
+
+def even_split(n: int, P: int) -> list:
+    """Split n items over P ranks: the first n mod P ranks get one more."""
+    return [n // P + (1 if r < n % P else 0) for r in range(P)]
+
+
+def _offsets(sizes) -> list:
+    out = [0]
+    for x in sizes:
+        out.append(out[-1] + int(x))
+    return out
+
+
+def anything_seq2head(shards, h_counts):
+    """list of ``[B][S_q][H][D]`` -> list of ``[B][S][H_p][D]`` (sum S_q = S, sum H_p = H)."""
+    h0 = _offsets(h_counts)
+    return [np.ascontiguousarray(np.concatenate([x[:, :, h0[p]:h0[p + 1], :] for x in shards],
+                                                axis=1))
+            for p in range(len(h_counts))]
+
+
+def anything_head2seq(groups, s_lens):
+    """list of ``[B][S][H_p][D]`` -> list of ``[B][S_q][H][D]``, the inverse of anything_seq2head."""
+    off = _offsets(s_lens)
+    return [np.ascontiguousarray(np.concatenate([y[:, off[q]:off[q + 1], :, :] for y in groups],
+                                                axis=2))
+            for q in range(len(s_lens))]
+
+
+def anything_seq2head_loop(shards, h_counts):
+    """Explicit-loop form of anything_seq2head (tiny shapes only)."""
+    B, _, H, D = shards[0].shape
+    s_lens = [x.shape[1] for x in shards]
+    S = sum(s_lens)
+    off, h0 = _offsets(s_lens), _offsets(h_counts)
+    out = [np.empty((B, S, hp, D), dtype=shards[0].dtype) for hp in h_counts]
+    for p in range(len(h_counts)):
+        for q in range(len(shards)):
+            for b in range(B):
+                for s in range(s_lens[q]):
+                    for h in range(h_counts[p]):
+                        for d in range(D):
+                            out[p][b, off[q] + s, h, d] = shards[q][b, s, h0[p] + h, d]
+    return out
+
+
+def anything_head2seq_loop(groups, s_lens):
+    """Explicit-loop form of anything_head2seq (tiny shapes only)."""
+    B, S, _, D = groups[0].shape
+    h_counts = [y.shape[2] for y in groups]
+    H = sum(h_counts)
+    off, h0 = _offsets(s_lens), _offsets(h_counts)
+    out = [np.empty((B, sq, H, D), dtype=groups[0].dtype) for sq in s_lens]
+    for q in range(len(s_lens)):
+        for p in range(len(groups)):
+            for b in range(B):
+                for s in range(s_lens[q]):
+                    for h in range(h_counts[p]):
+                        for d in range(D):
+                            out[q][b, s, h0[p] + h, d] = groups[p][b, off[q] + s, h, d]
+    return out

@@ -330,6 +330,78 @@ def test_relayout_shard_semantics():
         assert np.array_equal(y[p], full[:, :, p * 2:(p + 1) * 2, :])
 
 
+# ------------------------------------------------------ relayout: Ulysses Anything
+
+def test_anything_golden():
+    g = _golden("tiny_relayout_anything.json")
+    ins = [np.array(x, dtype=np.int64) for x in g["in"]]
+    want = [np.array(x, dtype=np.int64) for x in g["seq2head"]]
+    for f in (oracle.anything_seq2head, oracle.anything_seq2head_loop):
+        got = f(ins, g["h_counts"])
+        assert all(np.array_equal(a, b) for a, b in zip(got, want))
+    for f in (oracle.anything_head2seq, oracle.anything_head2seq_loop):
+        back = f(want, g["s_lens"])
+        assert all(np.array_equal(a, b) for a, b in zip(back, ins))
+
+
+@pytest.mark.parametrize("s_lens,h_counts,B,D", [
+    ([3, 2, 2], [2, 1, 1], 1, 2),      # uneven tokens and heads
+    ([1, 0, 4], [0, 3, 1], 2, 1),      # empty shard, empty head group
+    ([5], [3], 2, 3),                  # one rank: a plain copy
+    ([2, 2, 1, 1], [1, 1, 1, 1], 1, 2),
+])
+def test_anything_loops_and_roundtrip(s_lens, h_counts, B, D):
+    H = sum(h_counts)
+    rng = np.random.default_rng(sum(s_lens) * 7 + H)
+    ins = [rng.integers(0, 1 << 16, size=(B, sq, H, D)) for sq in s_lens]
+    out = oracle.anything_seq2head(ins, h_counts)
+    assert [o.shape for o in out] == [(B, sum(s_lens), hp, D) for hp in h_counts]
+    assert all(np.array_equal(a, b) for a, b in zip(out, oracle.anything_seq2head_loop(ins, h_counts)))
+    back = oracle.anything_head2seq(out, s_lens)
+    assert all(np.array_equal(a, b) for a, b in zip(back, ins))
+    assert all(np.array_equal(a, b) for a, b in zip(oracle.anything_head2seq_loop(out, s_lens), ins))
+    if len(s_lens) == 1:
+        assert np.array_equal(out[0], ins[0])
+
+
+def test_anything_even_split_is_standard_ulysses():
+    """With equal shards and head groups the mode is ordinary Ulysses."""
+    P, S_l, H, D = 4, 3, 8, 2
+    x = np.arange(P * 1 * S_l * H * D).reshape(P, 1, S_l, H, D)
+    got = oracle.anything_seq2head([x[q] for q in range(P)], [H // P] * P)
+    want = oracle.seq2head(x, P)
+    assert all(np.array_equal(got[p], want[p]) for p in range(P))
+
+
+def test_anything_shard_semantics_and_split_rule():
+    """Rank p's group is heads [h0_p, h0_p + H_p) of the full sequence; the
+    default split gives the first n mod P ranks one extra item."""
+    assert oracle.even_split(4481, 4) == [1121, 1120, 1120, 1120]
+    assert oracle.even_split(30, 4) == [8, 8, 7, 7]
+    assert oracle.even_split(3, 5) == [1, 1, 1, 0, 0]
+    S, H, D = 11, 7, 2
+    full = _rand((1, S, H, D), 62)
+    s_lens, h_counts = oracle.even_split(S, 3), oracle.even_split(H, 3)
+    off = np.cumsum([0] + s_lens)
+    ins = [full[:, off[q]:off[q + 1]] for q in range(3)]
+    out = oracle.anything_seq2head(ins, h_counts)
+    h0 = np.cumsum([0] + h_counts)
+    for p in range(3):
+        assert np.array_equal(out[p], full[:, :, h0[p]:h0[p + 1], :])
+
+
+def test_anything_pins_catch_planted_mistakes():
+    g = _golden("tiny_relayout_anything.json")
+    ins = [np.array(x, dtype=np.int64) for x in g["in"]]
+    want = [np.array(x, dtype=np.int64) for x in g["seq2head"]]
+    # head groups assigned in reverse rank order
+    bad = oracle.anything_seq2head(ins, g["h_counts"][::-1])
+    assert not all(a.shape == b.shape and np.array_equal(a, b) for a, b in zip(bad, want))
+    # tokens concatenated in reverse source-rank order
+    bad = oracle.anything_seq2head(ins[::-1], g["h_counts"])
+    assert not all(np.array_equal(a, b) for a, b in zip(bad, want))
+
+
 # ---------------------------------------- planted mistakes are caught by the pins
 
 def _mutant(kind):
