@@ -131,7 +131,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
-                    help="run only this detail workload (qwen, wan, llm, ra, merge) after the "
+                    help="run only this detail workload (qwen, wan, llm, ra, merge, anything) "
+                         "after the "
                          "headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -243,6 +244,9 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
             out[w.name] = ulysses_workload(torch, cp, synthetic, dev, flush, w)
     if want("ra"):
         out[synthetic.LLM_RING_ANYTHING.name] = ring_anything_workload(torch, cp, synthetic, dev)
+    if want("anything"):
+        out[synthetic.FLUX_ANYTHING.name] = ulysses_anything_workload(torch, cp, synthetic, dev,
+                                                                      flush)
     return out
 
 
@@ -301,6 +305,44 @@ def ulysses_workload(torch, cp, synthetic, dev, flush, w):
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
     del qkv, heads, rq, rk, rv, o, lse, back
     torch.cuda.empty_cache()
+    return res
+
+
+def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
+    """FLUX 1008x1008 over a Ulysses degree of 4 with uneven shards (Ulysses Anything)."""
+    w = synthetic.FLUX_ANYTHING
+    log(f"{w.name}: inputs")
+    s_lens, h_counts, S, D = list(w.chunk_lens), list(w.head_counts), w.S, w.D
+    qkv = [x.to(dev).reshape(-1) for x in synthetic.make_qkv(w)]
+    groups = [torch.empty_like(x) for x in qkv]
+    nbytes = qkv[0].numel() * qkv[0].element_size() * 2
+    d_s2h = time_launches(torch, lambda: cp.ulysses_anything_seq2head(
+        qkv[0], s_lens, h_counts, 1, D, groups[0]), 2, 10, flush)
+    for x, y in zip(qkv, groups):
+        cp.ulysses_anything_seq2head(x, s_lens, h_counts, 1, D, y)
+    h0 = h_counts[0]
+    rq, rk, rv = (y[:S * h0 * D].view(1, S, h0, D) for y in groups)
+    o = torch.empty_like(rq)
+    lse = torch.empty((1, h0, S), dtype=torch.float32, device=dev)
+    flops = 4.0 * D * h0 * S * S
+    d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
+        rq, rk, rv, o, lse, out_dtype=torch.bfloat16), 2, 10)
+    back = torch.empty_like(qkv[0])
+    d_h2s = time_launches(torch, lambda: cp.ulysses_anything_head2seq(
+        groups[1], s_lens, h_counts, 1, D, back), 2, 10, flush)
+    res = {
+        "seq_split": s_lens, "head_split": h_counts,
+        "attn_us": median(d_att) * 1e3,
+        "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
+        "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "seq2head_gbs": nbytes / (median(d_s2h) * 1e-3) / 1e9,
+        "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
+        "relayout_bytes_per_tensor": nbytes,
+        "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "gflop": flops / 1e9,
+    }
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
+        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
     return res
 
 

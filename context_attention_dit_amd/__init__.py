@@ -11,6 +11,8 @@ Entry points (same names as the C ABI, without the ``cp_`` prefix):
   ring_attention       one ring rank: Q over P chunks in visit order, fused fp32 merge
   ulysses_seq2head     Ulysses regrouping before attention (all P ranks)
   ulysses_head2seq     Ulysses regrouping after attention (inverse)
+  ulysses_anything_seq2head / ulysses_anything_head2seq
+                       the same with uneven per-rank token and head counts
 """
 from __future__ import annotations
 
@@ -58,6 +60,10 @@ _ring = _sig("cp_ring_attention", [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp,
                                    _i64, _int, _f32, _int, _i64, _vp, ctypes.c_size_t, _vp])
 _seq2head = _sig("cp_ulysses_seq2head", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _head2seq = _sig("cp_ulysses_head2seq", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
+_any_seq2head = _sig("cp_ulysses_anything_seq2head",
+                     [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
+_any_head2seq = _sig("cp_ulysses_anything_head2seq",
+                     [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
 _last_error = _sig("cp_last_error", [], ctypes.c_char_p)
 _abi_version = _sig("cp_abi_version", [])
 
@@ -217,6 +223,44 @@ def ulysses_head2seq(y: torch.Tensor, P: int, out: Optional[torch.Tensor] = None
     return out
 
 
+def _counts(xs):
+    arr = (ctypes.c_int64 * max(1, len(xs)))(*[int(v) for v in xs])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _anything(name, fn, x, s_lens, h_counts, B, D, out, stream):
+    P = len(s_lens)
+    if len(h_counts) != P:
+        raise ValueError("s_lens and h_counts need one entry per rank")
+    n = B * sum(s_lens) * sum(h_counts) * D
+    if not x.is_contiguous() or x.numel() != n:
+        raise ValueError(f"expected a contiguous packed tensor of {n} elements")
+    if out is None:
+        out = torch.empty(n, dtype=x.dtype, device=x.device)
+    sa, sp = _counts(s_lens)
+    ha, hp = _counts(h_counts)
+    _check(name, fn(_ptr(x), _ptr(out), P, B, sp, hp, D, _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
+def ulysses_anything_seq2head(x: torch.Tensor, s_lens, h_counts, B: int, D: int,
+                              out: Optional[torch.Tensor] = None, *, stream=None) -> torch.Tensor:
+    """Packed sequence shards (shard q = [B][s_lens[q]][H][D]) -> packed head
+    groups (group p = [B][S][h_counts[p]][D]); see cp_ulysses_anything_seq2head.
+    Returns a flat tensor of B*S*H*D elements."""
+    return _anything("cp_ulysses_anything_seq2head", _any_seq2head, x, s_lens, h_counts, B, D,
+                     out, stream)
+
+
+def ulysses_anything_head2seq(y: torch.Tensor, s_lens, h_counts, B: int, D: int,
+                              out: Optional[torch.Tensor] = None, *, stream=None) -> torch.Tensor:
+    """Packed head groups -> packed sequence shards; the inverse of
+    ulysses_anything_seq2head (see cp_ulysses_anything_head2seq)."""
+    return _anything("cp_ulysses_anything_head2seq", _any_head2seq, y, s_lens, h_counts, B, D,
+                     out, stream)
+
+
 __all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
-           "ulysses_seq2head", "ulysses_head2seq", "last_error", "abi_version", "CpAttnError",
-           "KVChunk", "LIB_PATH"]
+           "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
+           "ulysses_anything_head2seq", "last_error", "abi_version", "CpAttnError", "KVChunk",
+           "LIB_PATH"]

@@ -310,4 +310,60 @@ cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, i
   return relayout("cp_ulysses_head2seq", in, out, P, B, S_local, H, D, dtype, stream, false);
 }
 
+static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t P, int64_t B,
+                              const int64_t* s_lens, const int64_t* h_counts, int64_t D,
+                              cp_dtype dtype, void* stream, bool seq2head) {
+  if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
+  if (P > CP_MAX_RING_CHUNKS)
+    return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d ranks", fn, (long long)P,
+                CP_MAX_RING_CHUNKS);
+  if (!s_lens || !h_counts) return fail(CP_E_INVALID, "%s: null count array", fn);
+  if (B < 0 || D < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
+  if (!valid_dtype(dtype)) return fail(CP_E_INVALID, "%s: unknown dtype %d", fn, dtype);
+  cpattn::AnyRelayoutDesc d{};
+  d.P = static_cast<int32_t>(P);
+  for (int64_t r = 0; r < P; ++r) {
+    if (s_lens[r] < 0 || h_counts[r] < 0)
+      return fail(CP_E_INVALID, "%s: negative count for rank %lld", fn, (long long)r);
+    if (s_lens[r] >= kMaxSeq || h_counts[r] >= kMaxSeq)
+      return fail(CP_E_UNSUPPORTED, "%s: count for rank %lld too large", fn, (long long)r);
+    d.s_off[r + 1] = d.s_off[r] + s_lens[r];
+    d.h_off[r + 1] = d.h_off[r] + h_counts[r];
+  }
+  d.B = B;
+  d.S = d.s_off[P];
+  d.H = d.h_off[P];
+  d.D = D;
+  d.seq2head = seq2head;
+  if (B == 0 || d.S == 0 || d.H == 0 || D == 0) return ok();
+  if (!in || !out) return fail(CP_E_INVALID, "%s: null pointer", fn);
+  const int es = elem_size(dtype);
+  d.elem_bytes = es;
+  if (!aligned(in, es) || !aligned(out, es))
+    return fail(CP_E_INVALID, "%s: pointer not aligned to the element size", fn);
+  const int64_t bytes = sat_mul({B, d.S, d.H, D, es});
+  if (overlap(in, bytes, out, bytes)) return fail(CP_E_INVALID, "%s: out overlaps in", fn);
+  // one launch: every (rank pair, batch) block of words, and all offsets, fit 32 bits
+  const int w = cpattn::any_relayout_word_bytes(in, out, d);
+  if (B >= 65536 || sat_mul({d.S, d.H, D, es}) / w >= (int64_t(1) << 32) ||
+      sat_mul({B, d.S, d.H}) >= (int64_t(1) << 32))
+    return fail(CP_E_UNSUPPORTED, "%s: tensor of %lld bytes too large for one launch", fn,
+                (long long)bytes);
+  return hip_status(cpattn::launch_any_relayout(in, out, d, static_cast<hipStream_t>(stream)), fn);
+}
+
+cp_status cp_ulysses_anything_seq2head(const void* in, void* out, int64_t P, int64_t B,
+                                       const int64_t* s_lens, const int64_t* h_counts, int64_t D,
+                                       cp_dtype dtype, void* stream) {
+  return any_relayout("cp_ulysses_anything_seq2head", in, out, P, B, s_lens, h_counts, D, dtype,
+                      stream, true);
+}
+
+cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int64_t B,
+                                       const int64_t* s_lens, const int64_t* h_counts, int64_t D,
+                                       cp_dtype dtype, void* stream) {
+  return any_relayout("cp_ulysses_anything_head2seq", in, out, P, B, s_lens, h_counts, D, dtype,
+                      stream, false);
+}
+
 }  // extern "C"

@@ -41,6 +41,21 @@ struct RelayoutDesc {
 int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d);
 hipError_t launch_relayout(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream);
 
+// Ulysses Anything: uneven per-rank token counts and head counts. The P
+// sequence shards (shard q = [B][S_q][H][D]) and the P head groups (group p
+// = [B][S][H_p][D]) are each packed back to back in rank order.
+struct AnyRelayoutDesc {
+  int32_t P;
+  int64_t B, S, H, D;
+  int elem_bytes;
+  bool seq2head;
+  int64_t s_off[CP_MAX_RING_CHUNKS + 1];  // token offsets: shard q = [s_off[q], s_off[q+1])
+  int64_t h_off[CP_MAX_RING_CHUNKS + 1];  // head offsets: group p = [h_off[p], h_off[p+1])
+};
+int any_relayout_word_bytes(const void* in, void* out, const AnyRelayoutDesc& d);
+hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc& d,
+                               hipStream_t stream);
+
 // ----- merge (lse_merge.hip)
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, void* o,
                             float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, bool out_bf16,

@@ -11,6 +11,8 @@
 // the run length and both pointers allow it), consecutive lanes touch
 // consecutive words of a run, and loads/stores are non-temporal because each
 // byte is read once and written once.
+#include <algorithm>
+
 #include "cp_internal.h"
 
 namespace cpattn {
@@ -112,7 +114,118 @@ hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStre
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- anything
+// Every (destination group p, source shard q, batch b) pair is one 2-D copy:
+// S_q rows of H_p*D elements, contiguous on the head-group side and at a row
+// stride of H*D on the sequence-shard side. Block (x, y, z) takes words
+// [1024x, 1024x + 1024) of pair (p, q) = (y / P, y % P) for batch z.
+struct AnyGeometry {
+  int32_t P;
+  uint32_t B, S, H, wd;           // wd: words per head row (D elements)
+  uint32_t s_off[CP_MAX_RING_CHUNKS + 1];
+  uint32_t h_off[CP_MAX_RING_CHUNKS + 1];
+  FastDiv row[CP_MAX_RING_CHUNKS];  // words per copied row of group p: H_p * wd
+};
+
+template <int UNIT, bool SEQ2HEAD>
+__global__ __launch_bounds__(kThreads) void any_relayout_kernel(const void* __restrict__ in_,
+                                                                void* __restrict__ out_,
+                                                                AnyGeometry g) {
+  using T = typename Word<UNIT>::T;
+  const T* in = static_cast<const T*>(in_);
+  T* out = static_cast<T*>(out_);
+  const int p = blockIdx.y / g.P, q = blockIdx.y - p * g.P;
+  const uint32_t b = blockIdx.z;
+  const uint32_t sq = g.s_off[q + 1] - g.s_off[q];
+  const uint32_t hp = g.h_off[p + 1] - g.h_off[p];
+  const uint32_t row_words = hp * g.wd;
+  const uint32_t n = sq * row_words;  // words of this pair and batch
+  // word offsets of the pair's first element on both sides
+  const uint64_t shard_base =
+      (static_cast<uint64_t>(g.B) * g.s_off[q] * g.H + static_cast<uint64_t>(b) * sq * g.H +
+       g.h_off[p]) * g.wd;
+  const uint64_t group_base =
+      (static_cast<uint64_t>(g.B) * g.S * g.h_off[p] +
+       (static_cast<uint64_t>(b) * g.S + g.s_off[q]) * hp) * g.wd;
+  const uint32_t first = blockIdx.x * (kThreads * kUnitsPerThread) + threadIdx.x;
+  T v[kUnitsPerThread];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const uint32_t u = first + i * kThreads;
+    if (u < n) {
+      const uint32_t r = g.row[p].div(u), w = u - r * row_words;
+      const uint64_t sh = shard_base + static_cast<uint64_t>(r) * g.H * g.wd + w;
+      const uint64_t gr = group_base + u;
+      v[i] = __builtin_nontemporal_load(in + (SEQ2HEAD ? sh : gr));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const uint32_t u = first + i * kThreads;
+    if (u < n) {
+      const uint32_t r = g.row[p].div(u), w = u - r * row_words;
+      const uint64_t sh = shard_base + static_cast<uint64_t>(r) * g.H * g.wd + w;
+      const uint64_t gr = group_base + u;
+      __builtin_nontemporal_store(v[i], out + (SEQ2HEAD ? gr : sh));
+    }
+  }
+}
+
+template <int UNIT>
+hipError_t launch_any_unit(const void* in, void* out, const AnyRelayoutDesc& d,
+                           hipStream_t stream) {
+  AnyGeometry g;
+  g.P = d.P;
+  g.B = static_cast<uint32_t>(d.B);
+  g.S = static_cast<uint32_t>(d.S);
+  g.H = static_cast<uint32_t>(d.H);
+  g.wd = static_cast<uint32_t>(d.D * d.elem_bytes / UNIT);
+  uint64_t max_s = 0, max_h = 0;
+  for (int r = 0; r <= d.P; ++r) {
+    g.s_off[r] = static_cast<uint32_t>(d.s_off[r]);
+    g.h_off[r] = static_cast<uint32_t>(d.h_off[r]);
+  }
+  for (int r = 0; r < d.P; ++r) {
+    const uint32_t hp = g.h_off[r + 1] - g.h_off[r];
+    g.row[r].init(hp > 0 ? hp * g.wd : 1u);
+    max_s = std::max<uint64_t>(max_s, g.s_off[r + 1] - g.s_off[r]);
+    max_h = std::max<uint64_t>(max_h, hp);
+  }
+  const uint64_t max_words = max_s * max_h * g.wd;
+  const uint32_t per_block = kThreads * kUnitsPerThread;
+  const dim3 grid(static_cast<uint32_t>((max_words + per_block - 1) / per_block),
+                  static_cast<uint32_t>(d.P * d.P), g.B);
+  if (d.seq2head)
+    hipLaunchKernelGGL((any_relayout_kernel<UNIT, true>), grid, dim3(kThreads), 0, stream, in,
+                       out, g);
+  else
+    hipLaunchKernelGGL((any_relayout_kernel<UNIT, false>), grid, dim3(kThreads), 0, stream, in,
+                       out, g);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Widest word that divides a head row (D elements) and both base addresses.
+int any_relayout_word_bytes(const void* in, void* out, const AnyRelayoutDesc& d) {
+  const int64_t row_bytes = d.D * d.elem_bytes;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out);
+  for (int w = 16; w > 2; w /= 2)
+    if (row_bytes % w == 0 && align % w == 0) return w;
+  return 2;
+}
+
+// The caller has checked: 1 <= P <= CP_MAX_RING_CHUNKS, every pair's words
+// and the grid fit 32 bits, B < 65536.
+hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc& d,
+                               hipStream_t stream) {
+  switch (any_relayout_word_bytes(in, out, d)) {
+    case 16: return launch_any_unit<16>(in, out, d, stream);
+    case 8: return launch_any_unit<8>(in, out, d, stream);
+    case 4: return launch_any_unit<4>(in, out, d, stream);
+    default: return launch_any_unit<2>(in, out, d, stream);
+  }
+}
 
 // Widest word that divides the run length and both base addresses.
 int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d) {

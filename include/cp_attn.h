@@ -185,6 +185,48 @@ cp_status cp_ulysses_seq2head(const void* in, void* out, int64_t P, int64_t B, i
 cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
                               int64_t H, int64_t D, cp_dtype dtype, void* stream);
 
+/*
+ * cp_ulysses_anything_seq2head — the Ulysses regrouping when neither the
+ * sequence nor the heads divide by the degree.
+ *
+ * Defined by: the Context parallelism guide (diffusers), section Ulysses
+ * Anything Attention (the mode removes both divisibility requirements of
+ * Ulysses), and the diffusers parallel API, ContextParallelConfig
+ * (ulysses_anything). Source rank q holds s_lens[q] tokens, tokens
+ * [off_q, off_q + s_lens[q]) of the sequence with off_q = s_lens[0] + ... +
+ * s_lens[q-1]; destination rank p receives the h_counts[p] contiguous heads
+ * starting at h0_p = h_counts[0] + ... + h_counts[p-1]:
+ *   out_p[b][off_q + s][h][d] = in_q[b][s][h0_p + h][d]
+ *
+ *   in:  the P sequence shards packed back to back in rank order; shard q is
+ *        [B][s_lens[q]][H][D] and starts at element B*off_q*H*D, where
+ *        H = sum of h_counts.
+ *   out: the P head groups packed back to back in rank order; group p is
+ *        [B][S][h_counts[p]][D] and starts at element B*S*h0_p*D, where
+ *        S = sum of s_lens.
+ *   s_lens, h_counts: HOST arrays of P counts (>= 0, zero allowed), read
+ *        during the call only.
+ * 1 <= P <= CP_MAX_RING_CHUNKS, any D >= 1, B < 65536. Same bit-copy and
+ * dtype rules as cp_ulysses_seq2head. Negative counts or a null array are
+ * CP_E_INVALID. With equal counts the result equals cp_ulysses_seq2head's.
+ */
+cp_status cp_ulysses_anything_seq2head(const void* in, void* out, int64_t P, int64_t B,
+                                       const int64_t* s_lens, const int64_t* h_counts, int64_t D,
+                                       cp_dtype dtype, void* stream);
+
+/*
+ * cp_ulysses_anything_head2seq — the exact inverse of
+ * cp_ulysses_anything_seq2head (the second regrouping, by token; same
+ * passages):
+ *   out_q[b][s][h0_p + h][d] = in_p[b][off_q + s][h][d]
+ *
+ *   in: the packed head groups, out: the packed sequence shards, with the
+ *   layouts and count rules described for cp_ulysses_anything_seq2head.
+ */
+cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int64_t B,
+                                       const int64_t* s_lens, const int64_t* h_counts, int64_t D,
+                                       cp_dtype dtype, void* stream);
+
 /* Text describing the last failed call on this thread ("" after a successful
  * call). Valid until the next cp_* call on the same thread. */
 const char* cp_last_error(void);

@@ -12,8 +12,9 @@ even) for the bf16 workloads. A Ulysses rank's input is the same full-sequence
 tensor viewed as ``[P][1][S/P][H][D]`` (P contiguous sequence shards).
 
 Shapes follow the workloads the pages benchmark: FLUX 1024x1024 (4096 image +
-512 text tokens), Qwen-Image 1536x1536 (96x96 latent + 256 text tokens), a
-Wan video of 21x30x52 latent patches, and a 128K-token causal LLM.
+512 text tokens) and 1008x1008 (63x63 + 512 = 4481 tokens, which only Ulysses
+Anything splits over 4 ranks), Qwen-Image 1536x1536 (96x96 latent + 256 text
+tokens), a Wan video of 21x30x52 latent patches, and a 128K-token causal LLM.
 """
 from __future__ import annotations
 
@@ -35,8 +36,9 @@ class Workload:
     dtype: torch.dtype
     causal: bool
     P: int  # ring degree (ring workloads) or Ulysses degree (Ulysses workloads)
-    kind: str  # "ring" or "ulysses"
-    chunk_lens: Tuple[int, ...] = ()  # ring: K/V chunk lengths in sequence order
+    kind: str  # "ring", "ulysses" or "ulysses_anything"
+    # ring: K/V chunk lengths in sequence order; ulysses_anything: tokens per rank
+    chunk_lens: Tuple[int, ...] = ()
 
     @property
     def seed(self) -> int:
@@ -49,6 +51,11 @@ class Workload:
     @property
     def S_local(self) -> int:
         return self.S // self.P
+
+    @property
+    def head_counts(self) -> Tuple[int, ...]:
+        """Heads per Ulysses rank (contiguous groups, the first H mod P get one more)."""
+        return even_split(self.H, self.P)
 
     def chunk_starts(self) -> List[int]:
         starts, acc = [], 0
@@ -79,8 +86,14 @@ LLM_RING_ANYTHING = Workload(5, "llm-ring-anything-4099", S=4099, H=32, D=128,
                              dtype=torch.bfloat16, causal=True, P=4, kind="ring",
                              chunk_lens=even_split(4099, 4))
 
+# FLUX at 1008x1008: 63x63 latent patches + 512 text tokens = 4481, which no
+# Ulysses degree of 4 divides (the Ulysses Anything case of the diffusers guide)
+FLUX_ANYTHING = Workload(6, "flux-1008-ulysses-anything4-rank0", S=63 * 63 + 512, H=24, D=128,
+                         dtype=torch.bfloat16, causal=False, P=4, kind="ulysses_anything",
+                         chunk_lens=even_split(63 * 63 + 512, 4))
+
 WORKLOADS = {w.name: w for w in (TINY, FLUX_RING, QWEN_ULYSSES, WAN_ULYSSES, LLM_ULYSSES,
-                                 LLM_RING_ANYTHING)}
+                                 LLM_RING_ANYTHING, FLUX_ANYTHING)}
 
 
 def ring_order(rank: int, P: int) -> List[int]:

@@ -160,6 +160,34 @@ def test_relayout_zero_size_is_noop():
     assert _relayout(cp._head2seq, D=0, inp=None, out=None) == OK
 
 
+def _anything(fn, inp=FAKE, out=FAKE2, P=3, B=1, s_lens=(4, 3, 3), h_counts=(2, 2, 1), D=128,
+              dt=BF16):
+    sa, sp = cp._counts(s_lens) if s_lens is not None else (None, None)
+    ha, hp = cp._counts(h_counts) if h_counts is not None else (None, None)
+    return fn(inp, out, P, B, sp, hp, D, dt, None)
+
+
+@pytest.mark.parametrize("name", ["_any_seq2head", "_any_head2seq"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), INVALID), (dict(P=65, s_lens=[1] * 65, h_counts=[1] * 65), UNSUPPORTED),
+    (dict(s_lens=None), INVALID), (dict(h_counts=None), INVALID),
+    (dict(s_lens=(4, -1, 3)), INVALID), (dict(h_counts=(2, 2, -3)), INVALID),
+    (dict(B=-1), INVALID), (dict(D=-2), INVALID), (dict(dt=5), INVALID),
+    (dict(inp=None), INVALID), (dict(out=FAKE + 512), INVALID), (dict(inp=FAKE + 1), INVALID),
+    (dict(B=1 << 16), UNSUPPORTED),
+])
+def test_anything_relayout_rejects(name, kw, status):
+    assert _anything(getattr(cp, name), **kw) == status
+    assert cp.last_error().startswith("cp_ulysses_anything")
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(D=0), dict(s_lens=(0, 0, 0)),
+                                dict(h_counts=(0, 0, 0), inp=None, out=None)])
+def test_anything_relayout_zero_size_is_noop(kw):
+    assert _anything(cp._any_seq2head, **kw) == OK
+    assert _anything(cp._any_head2seq, **kw) == OK
+
+
 def test_error_text_cleared_by_success():
     assert _partial(D=96) == UNSUPPORTED and cp.last_error() != ""
     assert _partial(Sq=0) == OK and cp.last_error() == ""

@@ -73,6 +73,72 @@ def test_relayout_misaligned_base_uses_narrow_words():
     assert np.array_equal(y.cpu().view(torch.int16).numpy(), want)
 
 
+# ------------------------------------------------------- relayout: Ulysses Anything
+
+def _shard_sizes(B, s_lens, h_counts, D):
+    S, H = sum(s_lens), sum(h_counts)
+    return [B * sq * H * D for sq in s_lens], [B * S * hp * D for hp in h_counts]
+
+
+def _split(flat, sizes, shapes):
+    out, o = [], 0
+    for n, shp in zip(sizes, shapes):
+        out.append(flat[o:o + n].reshape(shp))
+        o += n
+    return out
+
+
+@pytest.mark.parametrize("s_lens,h_counts,B,D,itemsize", [
+    ((5, 3, 4), (3, 2, 3), 2, 128, 2),          # uneven tokens and heads
+    ((7, 0, 2), (0, 4, 1), 1, 64, 2),           # a rank with no tokens, a rank with no heads
+    ((3, 3), (1, 2), 1, 12, 4),                 # fp32, D not a multiple of 16 bytes
+    ((9,), (5,), 2, 32, 2),                     # one rank: a plain copy
+    ((1121, 1120, 1120, 1120), (8, 8, 7, 7), 1, 128, 2),  # 4481 tokens, 30 heads over 4
+])
+def test_anything_relayout_bit_exact(s_lens, h_counts, B, D, itemsize):
+    say(f"anything relayout s={s_lens} h={h_counts} B={B} D={D} bytes={itemsize}")
+    S, H = sum(s_lens), sum(h_counts)
+    ssz, gsz = _shard_sizes(B, s_lens, h_counts, D)
+    bits = synthetic.random_bits((B * S * H * D,), itemsize, seed=S + H)
+    dt = torch.bfloat16 if itemsize == 2 else torch.float32
+    x = bits.view(dt).to(DEV)
+    y = cp.ulysses_anything_seq2head(x, s_lens, h_counts, B, D)
+    back = cp.ulysses_anything_head2seq(y, s_lens, h_counts, B, D)
+    torch.cuda.synchronize()
+    ints = torch.int16 if itemsize == 2 else torch.int32
+    shards = _split(bits.numpy(), ssz, [(B, sq, H, D) for sq in s_lens])
+    want = oracle.anything_seq2head(shards, list(h_counts))
+    got = _split(y.cpu().view(ints).numpy(), gsz, [(B, S, hp, D) for hp in h_counts])
+    assert all(np.array_equal(a, b) for a, b in zip(got, want))
+    assert torch.equal(back.view(ints).cpu(), bits)
+
+
+def test_anything_relayout_even_split_matches_standard():
+    P, B, S_l, H, D = 4, 2, 6, 8, 128
+    x = synthetic.random_bits((P, B, S_l, H, D), 2, seed=33).view(torch.bfloat16).to(DEV)
+    say("anything relayout with even counts vs standard Ulysses")
+    a = cp.ulysses_anything_seq2head(x.reshape(-1), [S_l] * P, [H // P] * P, B, D)
+    b = cp.ulysses_seq2head(x, P)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.reshape(-1).view(torch.int16))
+
+
+def test_anything_relayout_misaligned_base_uses_narrow_words():
+    s_lens, h_counts, B, D = (3, 2), (2, 1), 1, 64
+    S, H = sum(s_lens), sum(h_counts)
+    n = B * S * H * D
+    bits = synthetic.random_bits((n + 1,), 2, seed=6)
+    say("anything relayout with 2-byte-offset base pointers")
+    buf = bits.view(torch.bfloat16).to(DEV)
+    out = torch.empty(n + 1, dtype=torch.bfloat16, device=DEV)
+    cp.ulysses_anything_seq2head(buf[1:], s_lens, h_counts, B, D, out[1:])
+    torch.cuda.synchronize()
+    ssz, gsz = _shard_sizes(B, s_lens, h_counts, D)
+    shards = _split(bits.numpy()[1:], ssz, [(B, sq, H, D) for sq in s_lens])
+    want = np.concatenate([w.ravel() for w in oracle.anything_seq2head(shards, list(h_counts))])
+    assert np.array_equal(out[1:].cpu().view(torch.int16).numpy(), want)
+
+
 # ---------------------------------------------------------------------- merge
 
 @pytest.mark.parametrize("P,D", [(1, 128), (2, 128), (4, 128), (7, 128), (8, 64),

@@ -123,3 +123,40 @@ def test_ulysses_rank0(wname, n_edge, n_rand):
     got_l = lse[:, :, torch.from_numpy(rows).to(DEV)]
     check_o(got_o, wo, "bf16", "rank 0 O (sampled rows)")
     check_lse(got_l, wl, "rank 0 LSE (sampled rows)")
+
+
+def test_ulysses_anything_flux1008_rank0():
+    """FLUX 1008x1008 (4481 tokens) over a Ulysses degree of 4: uneven sequence
+    shards 1121/1120/1120/1120. The packed shards of a batch-1 sequence are the
+    full tensor itself; rank 0's head group is the first slice of the output."""
+    w = synthetic.FLUX_ANYTHING
+    s_lens, h_counts = list(w.chunk_lens), list(w.head_counts)
+    S, H, D = w.S, w.H, w.D
+    say(f"{w.name}: generating inputs")
+    q, k, v = synthetic.make_qkv(w)
+    say(f"{w.name}: anything seq2head x3")
+    qh, kh, vh = (cp.ulysses_anything_seq2head(x.to(DEV).reshape(-1), s_lens, h_counts, 1, D)
+                  for x in (q, k, v))
+    torch.cuda.synchronize()
+    shards = []
+    for s0, n in zip(w.chunk_starts(), s_lens):
+        shards.append(q[:, s0:s0 + n].contiguous().view(torch.int16).numpy())
+    want = np.concatenate([g.ravel() for g in oracle.anything_seq2head(shards, h_counts)])
+    assert np.array_equal(qh.cpu().view(torch.int16).numpy(), want)
+    del want, shards
+    n0 = S * h_counts[0] * D
+    say(f"{w.name}: rank 0 attention over {h_counts[0]} heads")
+    o, lse = cp.attn_chunk_partial(qh[:n0].view(1, S, h_counts[0], D), kh[:n0].view(1, S, h_counts[0], D),
+                                   vh[:n0].view(1, S, h_counts[0], D), out_dtype=torch.bfloat16)
+    say(f"{w.name}: anything head2seq")
+    back = cp.ulysses_anything_head2seq(kh, s_lens, h_counts, 1, D)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16).cpu(), k.reshape(-1).view(torch.int16))
+    rows = _rows(S, 64, 192, seed=w.seed)
+    heads = slice(0, h_counts[0])
+    say(f"{w.name}: oracle on {len(rows)} rows x {h_counts[0]} heads")
+    wo, wl = oracle.attention(to_f64(q[:, rows][:, :, heads]), to_f64(k[:, :, heads]),
+                              to_f64(v[:, :, heads]), 1 / math.sqrt(D))
+    idx = torch.from_numpy(rows).to(DEV)
+    check_o(o[:, idx], wo, "bf16", "rank 0 O (sampled rows)")
+    check_lse(lse[:, :, idx], wl, "rank 0 LSE (sampled rows)")
