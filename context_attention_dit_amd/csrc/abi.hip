@@ -150,6 +150,7 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
   a.scale = scale;
   a.nchunks = 1;
   a.nsplit = 1;
+  a.groups = in_dtype == CP_BF16 ? cpattn::attn_groups(B, H, Sq, (Skv + 63) / 64) : 1;
   a.chunks[0].k = k;
   a.chunks[0].v = v;
   a.chunks[0].len = static_cast<int32_t>(Skv);
@@ -265,8 +266,10 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
     tiles += (chunks[c].len + 63) / 64;
   }
   a.nsplit = 1;
+  a.groups = 1;
   if (in_dtype == CP_BF16) {
-    a.nsplit = cpattn::attn_split_count(B, H, Sq, tiles, causal != 0);
+    a.groups = cpattn::attn_groups(B, H, Sq, tiles);
+    a.nsplit = a.groups == 2 ? 1 : cpattn::attn_split_count(B, H, Sq, tiles, causal != 0);
     if (a.nsplit > 1) {
       a.part_o = static_cast<float*>(workspace);
       a.part_lse = a.part_o + a.nsplit * B * Sq * H * D;

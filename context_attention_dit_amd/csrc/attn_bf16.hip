@@ -106,21 +106,29 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+// G = 1: a block is 4 waves over one query tile. G = 2: a block is two such
+// groups of 4 waves over the same query tile, group g taking half g of the
+// tile's keys with its own LDS stages; the halves are merged through LDS at
+// the end (grids with fewer query tiles than CUs: every tile gets a whole CU).
+template <int D, bool CAUSAL, bool OUT_BF16, int G>
+__global__ __launch_bounds__(kThreads * G, G == 1 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int UPR = Geo<D>::kUPR;
   constexpr int TB = Geo<D>::kTileBytes;
   constexpr int NL = Geo<D>::kLoadsPerWave;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // [K0][K1][V0][V1]
+  // per group [K0][K1][V0][V1]
+  __shared__ __attribute__((aligned(1024))) char smem[G * 4 * TB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int grp = G == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);  // key half (G = 2)
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wave within the group
   const int col = lane & 31, half = lane >> 5;
+  const uint32_t gbase = static_cast<uint32_t>(grp * 4 * TB);  // the group's LDS stages
 
   // ---- block -> (batch*head, query tile, key split)
   const int nqt = (a.Sq + kBM - 1) / kBM;
   const int BH = a.B * a.H;
-  const int nsplit = CAUSAL ? 1 : a.nsplit;
+  const int nsplit = (CAUSAL || G == 2) ? 1 : a.nsplit;  // key splits across blocks
   const int nitems = nqt * BH * nsplit;
   int bh, qt, sp = 0;
   if (CAUSAL) {
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const char* base =
         reinterpret_cast<const char*>(is_v ? a.chunks[c].v : a.chunks[c].k) +
         2 * ((static_cast<int64_t>(b) * a.chunks[c].len + x.kt * kBN) * rs + h * D);
-    char* l = dst + wave * NL * 1024;
+    char* l = dst + gbase + wave * NL * 1024;
     if (n_valid >= kBN) {
 #pragma unroll
       for (int n = 0; n < NL; ++n)
@@ -228,9 +236,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- fragment read addresses (byte offsets within a tile)
   // K: row col (+32 for the second block), unit 2*ks + half, swizzled with row bits
+  // (the group's LDS base is folded into these per-lane offsets, so every
+  // slot offset below stays an immediate)
   uint32_t k_rd[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = k_unit_off<D>(col, 2 * ks + half);
+  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = gbase + k_unit_off<D>(col, 2 * ks + half);
   // V^T: 16-lane group g, lane j -> row 8*(g/2) + j/4, element column 16*(g%2) + 4*(j%4)
   const int g16 = lane >> 4, j16 = lane & 15;
   const int v_row = 8 * (g16 >> 1) + (j16 >> 2);
@@ -238,9 +248,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   uint32_t v_rd[D / 32];
 #pragma unroll
   for (int md = 0; md < D / 32; ++md)
-    v_rd[md] = v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+    v_rd[md] = gbase + v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
 
-  // LDS: K tiles in slots 0/1, V tiles in slots 2/3 (TB bytes each)
+  // LDS: K tiles in slots 0/1, V tiles in slots 2/3 (TB bytes each), per group
   char* const lds = smem;
 
   // S^T = K Q^T for the 64 keys of the K tile in slot `ks_slot` (32 queries per wave)
@@ -267,13 +277,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // this block's share of the query tile's tiles, in chunk order
   Cur cur0{0, 0};
-  int left;
+  int left, steps;
   {
     int total = 0;
     for (int cc = 0; cc < a.nchunks; ++cc) total += (keys_of(cc) + kBN - 1) / kBN;
-    const int t_begin = static_cast<int>(static_cast<int64_t>(total) * sp / nsplit);
-    const int t_end = static_cast<int>(static_cast<int64_t>(total) * (sp + 1) / nsplit);
+    const int nparts = G == 2 ? 2 : nsplit, part = G == 2 ? grp : sp;
+    const int t_begin = static_cast<int>(static_cast<int64_t>(total) * part / nparts);
+    const int t_end = static_cast<int>(static_cast<int64_t>(total) * (part + 1) / nparts);
     left = uni(t_end - t_begin);
+    // both groups step together (block-wide barriers): the second half is the longer
+    steps = uni(G == 2 ? total - total / 2 : left);
     int skip = t_begin;
     while (cur0.c < a.nchunks) {
       const int nt = (keys_of(cur0.c) + kBN - 1) / kBN;
@@ -292,6 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   Cur cur1 = cur0, cur2 = cur0;
   auto step = [&](auto par_tag, int j, f32x16* s_cur, f32x16* s_next) {
     constexpr int PAR = decltype(par_tag)::value;
+    if (G == 1 || j < left) {  // (a group out of tiles still joins the barrier below)
     // cursors: cur0 = tile j, cur1 = j+1, cur2 = j+2 (the prologue set them for j = 0)
     if (j > 0) {
       cur0 = cur1;
@@ -382,33 +396,64 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
   f32x16 s_a[2], s_b[2];
-  if (left > 0) {
-    issue(lds, cur0, false);
-    issue(lds + 2 * TB, cur0, true);
-    if (left > 1) {
-      cur1 = next_of(cur0);
-      issue(lds + TB, cur1, false);
+  if (steps > 0) {
+    if (G == 1 || left > 0) {
+      issue(lds, cur0, false);
+      issue(lds + 2 * TB, cur0, true);
+      if (left > 1) {
+        cur1 = next_of(cur0);
+        issue(lds + TB, cur1, false);
+      }
+      if (left > 2) cur2 = next_of(cur1);
     }
-    if (left > 2) cur2 = next_of(cur1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    qk(0, s_a);
+    if (G == 1 || left > 0) qk(0, s_a);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int j = 0; j < left; j += 2) {
+  for (int j = 0; j < steps; j += 2) {
     step(std::integral_constant<int, 0>{}, j, s_a, s_b);
-    if (j + 1 >= left) break;
+    if (j + 1 >= steps) break;
     step(std::integral_constant<int, 1>{}, j + 1, s_b, s_a);
   }
 
-  // ---- epilogue: normalise, write O and LSE
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- epilogue: merge the two key halves (G = 2), normalise, write O and LSE
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (G == 2) {
+    // group 1 hands its running max, row sum and unnormalised O to group 0
+    // through LDS (every wave is past its last tile read after this barrier)
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(smem + 4 * TB);  // [wave][md][r][lane]
+    float* xs = reinterpret_cast<float*>(smem);           // [wave][m, l][lane]
+    if (grp == 1) {
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[((wave * (D / 32) + md) * 16 + r) * 64 + lane] = oacc[md][r];
+      xs[(wave * 2) * 64 + lane] = m_run;
+      xs[(wave * 2 + 1) * 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[(wave * 2) * 64 + lane], l1 = xs[(wave * 2 + 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    l_tot = a0 * l_tot + a1 * l1;
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[md][r] = a0 * oacc[md][r] + a1 * xo[((wave * (D / 32) + md) * 16 + r) * 64 + lane];
+    m_run = mm;
+  }
   if (i >= a.Sq) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
@@ -449,19 +494,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   if (half == 0) a.lse[lrow] = lse_val;
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
-hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, bool OUT_BF16, int G>
+hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBM - 1) / kBM;
-  const int64_t nsplit = CAUSAL ? 1 : a.nsplit;
+  const int64_t nsplit = (CAUSAL || G == 2) ? 1 : a.nsplit;
   const int64_t nitems = nqt * a.B * a.H * nsplit;
   const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, OUT_BF16>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, OUT_BF16, G>),
+                     dim3(static_cast<uint32_t>(blocks)), dim3(kThreads * G), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   // combine the splits' fp32 partials in split order
   return launch_lse_merge(a.part_o, a.part_lse, static_cast<int>(nsplit), a.o, a.lse, a.B, a.H,
                           a.Sq, D, OUT_BF16, stream);
+}
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+  return a.groups == 2 ? launch_g<D, CAUSAL, OUT_BF16, 2>(a, stream)
+                       : launch_g<D, CAUSAL, OUT_BF16, 1>(a, stream);
 }
 
 int device_cus() {
@@ -487,12 +538,21 @@ hipError_t launch_d(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t s
 
 }  // namespace
 
-// Blocks of 128 query rows, two resident per CU. A grid that leaves CUs
-// idle is split along the keys until it covers the GPU, keeping at least 8
-// tiles per split (the merge pass costs one fp32 read/write per split).
+// Blocks of 128 query rows, two resident per CU. A grid of at most one query
+// tile per CU runs two-group blocks: eight waves per tile, its keys split
+// between the groups and merged in LDS. A grid between one and two tiles per
+// CU (ring calls, which have a workspace) is split along the keys across
+// blocks until it covers the GPU, keeping at least 8 tiles per split (the
+// merge pass costs one fp32 read/write per split).
+int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles) {
+  const int64_t units = (Sq + kBM - 1) / kBM * B * H;
+  return units <= device_cus() && tiles >= 4 ? 2 : 1;
+}
+
 int attn_split_count(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal) {
   if (causal) return 1;
   const int64_t units = (Sq + kBM - 1) / kBM * B * H;
+  if (units <= device_cus()) return 1;  // two-group blocks split the keys in LDS instead
   const int64_t slots = 2 * static_cast<int64_t>(device_cus());
   int s = 1;
   while (s < kMaxSplit && units * s < slots && tiles / (s + 1) >= 8) ++s;

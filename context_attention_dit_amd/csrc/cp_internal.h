@@ -83,6 +83,9 @@ struct AttnArgs {
   int32_t nsplit;
   float* part_o;
   float* part_lse;
+  // bf16 kernel: 1 = four waves per query tile; 2 = eight waves per query tile,
+  // its keys split between two groups and merged in LDS (no workspace)
+  int32_t groups;
   ChunkDesc chunks[CP_MAX_RING_CHUNKS];
 };
 
@@ -90,6 +93,9 @@ struct AttnArgs {
 // (non-causal only; 1 when the grid already fills the GPU). `tiles` is the
 // number of 64-key tiles each query tile visits.
 int attn_split_count(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal);
+// Groups per block (1 or 2) of the bf16 kernel: 2 when there are no more
+// query tiles than CUs and at least 4 key tiles to split.
+int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles);
 // fp32 elements of partial output the split needs: nsplit*(B*Sq*H*D + B*H*Sq).
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D);
 

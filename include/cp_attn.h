@@ -112,12 +112,14 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
 
 /*
  * cp_ring_attention_workspace_bytes — device workspace cp_ring_attention needs
- * for these sizes (may be 0). When B*H*ceil(Sq/128) query tiles leave the
- * GPU's compute units idle, cp_ring_attention splits each tile's keys over
- * two blocks; the splits' fp32 (O, LSE) partials live in the workspace and
- * are merged exactly as cp_lse_merge does. Host function; queries the current
- * device's compute-unit count; returns 0 for invalid sizes (which
- * cp_ring_attention then rejects).
+ * for these sizes (may be 0). With at most one query tile (128 rows of one
+ * batch and head) per compute unit, each tile's keys are split inside its
+ * block and no workspace is needed. Between one and two tiles per compute
+ * unit, cp_ring_attention splits each tile's keys over two blocks; the
+ * splits' fp32 (O, LSE) partials live in the workspace and are merged exactly
+ * as cp_lse_merge does. Host function; queries the current device's
+ * compute-unit count; returns 0 for invalid sizes (which cp_ring_attention
+ * then rejects).
  */
 size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D);
 

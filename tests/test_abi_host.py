@@ -123,8 +123,9 @@ def _ring(P=4, chunks=None, q=FAKE, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, D=128, d
     (dict(chunks=[(FAKE2 + 4, FAKE3, 8, 0)], P=1), INVALID),
     (dict(chunks=[(FAKE4, FAKE3, 8, 0)], P=1), INVALID),      # output overlaps a chunk
     (dict(dt=F32, D=96), UNSUPPORTED),
-    (dict(ws=FAKE6 + 8), INVALID),                             # misaligned workspace
-    (dict(ws=FAKE4 + 64), INVALID),                            # workspace overlaps the output
+    # 300 query tiles (between one and two per CU): the grid needs a workspace
+    (dict(H=300, ws=FAKE6 + 8), INVALID),                      # misaligned workspace
+    (dict(H=300, ws=FAKE4 + 64), INVALID),                     # workspace overlaps the output
 ])
 def test_ring_rejects(kw, status):
     assert _ring(**kw) == status
@@ -133,10 +134,13 @@ def test_ring_rejects(kw, status):
 
 def test_ring_zero_size_is_noop_and_workspace_query():
     assert _ring(Sq=0) == OK
-    n = cp.ring_attention_workspace_bytes(4, 1, 24, 1152, 128)
-    assert n >= 0
-    if n > 0:
-        assert _ring(ws=None, ws_bytes=0) == WORKSPACE
+    # at most one query tile per CU: keys are split inside the block, no workspace
+    assert cp.ring_attention_workspace_bytes(4, 1, 24, 1152, 128) == 0
+    # 300 query tiles: split across blocks through the workspace
+    n = cp.ring_attention_workspace_bytes(4, 1, 300, 8, 128)
+    assert n > 0
+    assert _ring(H=300, ws=None, ws_bytes=0) == WORKSPACE
+    assert _ring(H=300, ws_bytes=n - 16) == WORKSPACE
 
 
 def _relayout(fn, inp=FAKE, out=FAKE2, P=4, B=1, S=8, H=8, D=128, dt=BF16):

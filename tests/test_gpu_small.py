@@ -296,24 +296,63 @@ def test_ring_uneven_chunks(lens, causal, in_dtype):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_ring_key_splits(causal):
-    """A small grid (2 query tiles x 2 heads) is split along the keys; splits merge exactly."""
+def test_ring_small_grid_two_groups(causal):
+    """2 query tiles x 2 heads: each tile gets a whole CU, its keys split
+    between two wave groups and merged in LDS, so no workspace is needed."""
     lens = (700, 513, 0, 811)
     S, H, D = sum(lens), 2, 128
     q, k, v = _qkv(1, S, S, H, D, torch.bfloat16, seed=321)
     chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
     q0, n = 900, 200
-    ws = cp.ring_attention_workspace_bytes(4, 1, H, n, D)
-    assert ws > 0, "expected a split for this small grid"
-    say(f"ring with key splits causal={causal}, workspace {ws} bytes")
+    assert cp.ring_attention_workspace_bytes(4, 1, H, n, D) == 0
+    say(f"ring with two-group blocks causal={causal}")
     o, lse = cp.ring_attention(q[:, q0:q0 + n].contiguous().to(DEV), [chunks[c] for c in (3, 1, 0, 2)],
                                causal=causal, q_pos0=q0)
     torch.cuda.synchronize()
     wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal)
     check_o(o, wo[:, q0:q0 + n], "bf16")
     check_lse(lse, wl[:, :, q0:q0 + n])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Skv,H,D", [(200, 2000, 2, 128), (1, 700, 3, 64), (300, 256, 1, 128),
+                                        (129, 1111, 4, 128)])
+def test_chunk_partial_small_grid_two_groups(causal, Sq, Skv, H, D):
+    """A single chunk over few query tiles: each tile's keys are split between
+    the two wave groups of one block and merged in LDS (no workspace)."""
+    q, k, v = _qkv(1, Sq, Skv, H, D, torch.bfloat16, seed=Sq + Skv)
+    say(f"chunk partial two groups Sq={Sq} Skv={Skv} H={H} D={D} causal={causal}")
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal,
+                                   q_pos0=Skv - Sq if causal else 0)
+    torch.cuda.synchronize()
+    qp = np.arange(Sq) + (Skv - Sq if causal else 0)
+    wo, wl = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(D), causal,
+                              q_pos=qp, k_pos=np.arange(Skv))
+    check_o(o, wo, "bf16")
+    check_lse(lse, wl)
+
+
+def test_ring_key_splits_across_blocks():
+    """Between one and two query tiles per CU (300 tiles): each tile's keys are
+    split over two blocks whose fp32 partials go through the workspace."""
+    lens = (1024, 1040)
+    S, H, D = sum(lens), 4, 128
+    Sq = 128 * 75
+    q = synthetic.make_tensor((1, Sq, H, D), torch.bfloat16, 41)
+    k = synthetic.make_tensor((1, S, H, D), torch.bfloat16, 42)
+    v = synthetic.make_tensor((1, S, H, D), torch.bfloat16, 43)
+    chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
+    ws = cp.ring_attention_workspace_bytes(2, 1, H, Sq, D)
+    assert ws > 0, "expected a split across blocks for this grid"
+    say(f"ring with key splits across blocks, workspace {ws} bytes")
+    o, lse = cp.ring_attention(q.to(DEV), chunks)
+    torch.cuda.synchronize()
+    rows = np.arange(0, Sq, 37)
+    wo, wl = oracle.attention(to_f64(q[:, rows]), to_f64(k), to_f64(v), 1 / math.sqrt(D))
+    check_o(o[:, torch.from_numpy(rows).to(DEV)], wo, "bf16")
+    check_lse(lse[:, :, torch.from_numpy(rows).to(DEV)], wl)
     with pytest.raises(cp.CpAttnError) as e:
-        cp.ring_attention(q[:, q0:q0 + n].contiguous().to(DEV), chunks, causal=causal,
+        cp.ring_attention(q.to(DEV), chunks,
                           workspace=torch.empty(ws - 16, dtype=torch.uint8, device=DEV))
     assert e.value.status == 4
 
@@ -324,16 +363,15 @@ def test_ring_key_splits(causal):
     (130, 2, 64, (64, 0, 900, 77)),        # empty and one-tile chunks
 ])
 def test_ring_small_grids(Sq, H, D, lens):
-    """Grids smaller than the GPU split each query tile's keys over several
-    blocks whose fp32 partials are merged. Checked against the oracle, with a
-    garbage-filled workspace, and for byte-identical repeats."""
+    """Grids smaller than the GPU: each query tile's keys are split between the
+    two wave groups of its block and merged in LDS. Checked against the oracle,
+    with a garbage-filled workspace, and for byte-identical repeats."""
     S = sum(lens)
     q, k, v = _qkv(1, Sq, S, H, D, torch.bfloat16, seed=Sq + S)
     chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
     qd = q.to(DEV)
     need = cp.ring_attention_workspace_bytes(len(lens), 1, H, Sq, D)
-    assert need > 0
-    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    ws = torch.full((max(need, 16),), 255, dtype=torch.uint8, device=DEV)
     say(f"small grid Sq={Sq} H={H} D={D} lens={lens}")
     o1, l1 = cp.ring_attention(qd, chunks, workspace=ws)
     o2, l2 = cp.ring_attention(qd, chunks, workspace=ws)
