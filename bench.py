@@ -184,17 +184,20 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # One event pair on the launch stream brackets the whole timed region: the
+    # steps run back to back, so the per-launch duration is the bracket / K
+    # (a pair of events around every launch would add its own overhead).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
+    ev0.record()
+    for _ in range(args.steps):
         step()
-        b.record()
+    ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
     log(f"{w.name}: {ms_step * 1e3:.1f} us/step, kernel {launch_ms * 1e3:.1f} us, "
