@@ -25,6 +25,10 @@ Functions and the passages they follow:
   relayout.anything_seq2head / anything_head2seq (and *_loop forms)
                             the same with uneven per-rank token and head counts
                             (diffusers guide, Ulysses Anything Attention)
+  relayout.kv_gather (and kv_gather_loop)
+                            the K/V all-gather's unpack (SGLang Diffusion
+                            Sequence Parallelism, Choosing The Attention
+                            Exchange: kv_gather)
 
 Every function is pinned in ``tests/test_oracle.py`` against closed forms,
 hand-derived golden values (``tests/golden/``), identities, a library
@@ -33,10 +37,10 @@ routine (torch's fp64 scaled_dot_product_attention) and explicit loops.
 from .attention import (attention, bf16_bits_to_f64, chunk_partial, chunk_positions,
                         lse_merge, ring_attention, softmax_matrix)
 from .relayout import (anything_head2seq, anything_head2seq_loop, anything_seq2head,
-                       anything_seq2head_loop, even_split, head2seq, head2seq_loop, seq2head,
-                       seq2head_loop)
+                       anything_seq2head_loop, even_split, head2seq, head2seq_loop, kv_gather,
+                       kv_gather_loop, seq2head, seq2head_loop)
 
 __all__ = ["attention", "chunk_partial", "lse_merge", "ring_attention", "softmax_matrix",
            "bf16_bits_to_f64", "chunk_positions", "seq2head", "head2seq", "seq2head_loop",
            "head2seq_loop", "anything_seq2head", "anything_head2seq", "anything_seq2head_loop",
-           "anything_head2seq_loop", "even_split"]
+           "anything_head2seq_loop", "even_split", "kv_gather", "kv_gather_loop"]

@@ -146,3 +146,31 @@ def anything_head2seq_loop(groups, s_lens):
                         for d in range(D):
                             out[q][b, s, h0[p] + h, d] = groups[p][b, off[q] + s, h, d]
     return out
+
+
+# ---------------------------------------------------------------------------
+# K/V gather: queries stay sequence-sharded, keys and values are all-gathered
+# and each rank attends its own query shard to the full K/V (Sequence
+# Parallelism page (SGLang Diffusion), section Choosing The Attention
+# Exchange, kv_gather). On one GPU the all-gather's unpack joins the P
+# sequence shards into one sequence:  out[b][off_q + s][h][d] = in_q[b][s][h][d]
+
+
+def kv_gather(shards):
+    """list of ``[B][S_q][H][D]`` -> ``[B][S][H][D]`` (shards joined in rank order)."""
+    return np.ascontiguousarray(np.concatenate(shards, axis=1))
+
+
+def kv_gather_loop(shards):
+    """Explicit-loop form of kv_gather (tiny shapes only)."""
+    B, _, H, D = shards[0].shape
+    s_lens = [x.shape[1] for x in shards]
+    off = _offsets(s_lens)
+    out = np.empty((B, off[-1], H, D), dtype=shards[0].dtype)
+    for q, x in enumerate(shards):
+        for b in range(B):
+            for s in range(s_lens[q]):
+                for h in range(H):
+                    for d in range(D):
+                        out[b, off[q] + s, h, d] = x[b, s, h, d]
+    return out

@@ -402,6 +402,34 @@ def test_anything_pins_catch_planted_mistakes():
     assert not all(np.array_equal(a, b) for a, b in zip(bad, want))
 
 
+# ----------------------------------------------------------- relayout: K/V gather
+
+@pytest.mark.parametrize("s_lens,B,H,D", [([3, 1, 2], 2, 2, 3), ([4], 1, 3, 2), ([0, 2, 0, 1], 1, 1, 1)])
+def test_kv_gather_loop_and_special_case(s_lens, B, H, D):
+    rng = np.random.default_rng(len(s_lens) * 11 + H)
+    shards = [rng.integers(0, 1 << 16, size=(B, sq, H, D)) for sq in s_lens]
+    out = oracle.kv_gather(shards)
+    assert np.array_equal(out, oracle.kv_gather_loop(shards))
+    # the gather is the uneven regrouping with one destination holding every head
+    one_group = oracle.anything_seq2head(shards, [H] + [0] * (len(s_lens) - 1))
+    assert np.array_equal(out, one_group[0])
+
+
+def test_kv_gather_rank_share_is_full_attention_rows():
+    """A K/V-gather rank's output is full attention restricted to its query shard."""
+    S, H, D, P = 12, 2, 4, 3
+    q, k, v = (_rand((1, S, H, D), 70 + i) for i in range(3))
+    lens = oracle.even_split(S, P)
+    off = np.cumsum([0] + lens)
+    full_o, full_l = oracle.attention(q, k, v, 0.5)
+    kg = oracle.kv_gather([k[:, off[r]:off[r + 1]] for r in range(P)])
+    vg = oracle.kv_gather([v[:, off[r]:off[r + 1]] for r in range(P)])
+    for r in range(P):
+        o, l = oracle.attention(q[:, off[r]:off[r + 1]], kg, vg, 0.5)
+        assert np.allclose(o, full_o[:, off[r]:off[r + 1]], atol=1e-12)
+        assert np.allclose(l, full_l[:, :, off[r]:off[r + 1]], atol=1e-12)
+
+
 # ---------------------------------------- planted mistakes are caught by the pins
 
 def _mutant(kind):
