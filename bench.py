@@ -131,7 +131,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
-                    help="run only this detail workload (qwen, wan, llm, ra, merge, anything) "
+                    help="run only this detail workload (qwen, wan, llm, ra, merge, anything, "
+                         "kvgather) "
                          "after the "
                          "headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -250,6 +251,8 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
     if want("anything"):
         out[synthetic.FLUX_ANYTHING.name] = ulysses_anything_workload(torch, cp, synthetic, dev,
                                                                       flush)
+    if want("kvgather"):
+        out[synthetic.WAN_KV_GATHER.name] = kv_gather_workload(torch, cp, synthetic, dev, flush)
     return out
 
 
@@ -346,6 +349,38 @@ def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
+    return res
+
+
+def kv_gather_workload(torch, cp, synthetic, dev, flush):
+    """Wan over a K/V-gather degree of 4: rank 0's query shard over the gathered K/V."""
+    w = synthetic.WAN_KV_GATHER
+    log(f"{w.name}: inputs")
+    S, H, D, lens = w.S, w.H, w.D, list(w.chunk_lens)
+    q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
+    kg = torch.empty_like(k)
+    nbytes = k.numel() * k.element_size() * 2
+    d_g = time_launches(torch, lambda: cp.kv_gather(k.reshape(-1), lens, 1, H, D, kg), 2, 10,
+                        flush)
+    vg = cp.kv_gather(v.reshape(-1), lens, 1, H, D)
+    n0 = lens[0]
+    q0 = q[:, :n0].contiguous()
+    o = torch.empty_like(q0)
+    lse = torch.empty((1, H, n0), dtype=torch.float32, device=dev)
+    flops = 4.0 * D * H * n0 * S
+    d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
+        q0, kg, vg, o, lse, out_dtype=torch.bfloat16), 1, 5)
+    res = {
+        "rank_rows": n0, "attn_us": median(d_att) * 1e3,
+        "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
+        "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gather_gbs": nbytes / (median(d_g) * 1e-3) / 1e9,
+        "gather_hbm_frac": nbytes / (median(d_g) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "gather_bytes_per_tensor": nbytes, "gflop": flops / 1e9,
+    }
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, gather {res['gather_gbs']:.0f} GB/s")
+    del q, k, v, kg, vg, q0, o, lse
+    torch.cuda.empty_cache()
     return res
 
 

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI, without the ``cp_`` prefix):
   ulysses_head2seq     Ulysses regrouping after attention (inverse)
   ulysses_anything_seq2head / ulysses_anything_head2seq
                        the same with uneven per-rank token and head counts
+  kv_gather            the K/V all-gather's unpack (sequence shards joined)
 """
 from __future__ import annotations
 
@@ -64,6 +65,7 @@ _any_seq2head = _sig("cp_ulysses_anything_seq2head",
                      [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
 _any_head2seq = _sig("cp_ulysses_anything_head2seq",
                      [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
+_kv_gather = _sig("cp_kv_gather", [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp])
 _last_error = _sig("cp_last_error", [], ctypes.c_char_p)
 _abi_version = _sig("cp_abi_version", [])
 
@@ -260,7 +262,23 @@ def ulysses_anything_head2seq(y: torch.Tensor, s_lens, h_counts, B: int, D: int,
                      out, stream)
 
 
+def kv_gather(x: torch.Tensor, s_lens, B: int, H: int, D: int,
+              out: Optional[torch.Tensor] = None, *, stream=None) -> torch.Tensor:
+    """Packed sequence shards (shard q = [B][s_lens[q]][H][D]) -> the gathered
+    [B][S][H][D] tensor; see cp_kv_gather."""
+    S = sum(s_lens)
+    n = B * S * H * D
+    if not x.is_contiguous() or x.numel() != n:
+        raise ValueError(f"expected a contiguous packed tensor of {n} elements")
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=x.dtype, device=x.device)
+    sa, sp = _counts(s_lens)
+    _check("cp_kv_gather", _kv_gather(_ptr(x), _ptr(out), len(s_lens), B, sp, H, D,
+                                      _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
 __all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
            "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
-           "ulysses_anything_head2seq", "last_error", "abi_version", "CpAttnError", "KVChunk",
-           "LIB_PATH"]
+           "ulysses_anything_head2seq", "kv_gather", "last_error", "abi_version", "CpAttnError",
+           "KVChunk", "LIB_PATH"]

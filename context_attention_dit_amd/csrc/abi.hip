@@ -369,4 +369,18 @@ cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int
                       stream, false);
 }
 
+cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const int64_t* s_lens,
+                       int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  const char* fn = "cp_kv_gather";
+  if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
+  if (P > CP_MAX_RING_CHUNKS)
+    return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d ranks", fn, (long long)P,
+                CP_MAX_RING_CHUNKS);
+  if (H < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
+  // one destination group holding every head
+  int64_t h_counts[CP_MAX_RING_CHUNKS] = {0};
+  h_counts[0] = H;
+  return any_relayout(fn, in, out, P, B, s_lens, h_counts, D, dtype, stream, true);
+}
+
 }  // extern "C"

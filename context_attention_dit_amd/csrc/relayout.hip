@@ -117,10 +117,12 @@ hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStre
 // ---------------------------------------------------------------- anything
 // Every (destination group p, source shard q, batch b) pair is one 2-D copy:
 // S_q rows of H_p*D elements, contiguous on the head-group side and at a row
-// stride of H*D on the sequence-shard side. Block (x, y, z) takes words
-// [1024x, 1024x + 1024) of pair (p, q) = (y / P, y % P) for batch z.
+// stride of H*D on the sequence-shard side. Only pairs with rows and heads are
+// launched: block (x, y, z) takes words [1024x, 1024x + 1024) of pair
+// (act_p[y / nq], act_q[y % nq]) for batch z.
 struct AnyGeometry {
-  int32_t P;
+  int32_t P, nq;                  // nq: shards with tokens
+  uint8_t act_p[CP_MAX_RING_CHUNKS], act_q[CP_MAX_RING_CHUNKS];
   uint32_t B, S, H, wd;           // wd: words per head row (D elements)
   uint32_t s_off[CP_MAX_RING_CHUNKS + 1];
   uint32_t h_off[CP_MAX_RING_CHUNKS + 1];
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void any_relayout_kernel(const void* __re
   using T = typename Word<UNIT>::T;
   const T* in = static_cast<const T*>(in_);
   T* out = static_cast<T*>(out_);
-  const int p = blockIdx.y / g.P, q = blockIdx.y - p * g.P;
+  const int p = g.act_p[blockIdx.y / g.nq], q = g.act_q[blockIdx.y % g.nq];
   const uint32_t b = blockIdx.z;
   const uint32_t sq = g.s_off[q + 1] - g.s_off[q];
   const uint32_t hp = g.h_off[p + 1] - g.h_off[p];
@@ -181,6 +183,12 @@ hipError_t launch_any_unit(const void* in, void* out, const AnyRelayoutDesc& d,
   g.H = static_cast<uint32_t>(d.H);
   g.wd = static_cast<uint32_t>(d.D * d.elem_bytes / UNIT);
   uint64_t max_s = 0, max_h = 0;
+  int np = 0, nq = 0;
+  for (int r = 0; r < d.P; ++r) {
+    if (d.h_off[r + 1] > d.h_off[r]) g.act_p[np++] = static_cast<uint8_t>(r);
+    if (d.s_off[r + 1] > d.s_off[r]) g.act_q[nq++] = static_cast<uint8_t>(r);
+  }
+  g.nq = nq;
   for (int r = 0; r <= d.P; ++r) {
     g.s_off[r] = static_cast<uint32_t>(d.s_off[r]);
     g.h_off[r] = static_cast<uint32_t>(d.h_off[r]);
@@ -193,8 +201,9 @@ hipError_t launch_any_unit(const void* in, void* out, const AnyRelayoutDesc& d,
   }
   const uint64_t max_words = max_s * max_h * g.wd;
   const uint32_t per_block = kThreads * kUnitsPerThread;
+  // (the caller guarantees S > 0 and H > 0, so np, nq >= 1)
   const dim3 grid(static_cast<uint32_t>((max_words + per_block - 1) / per_block),
-                  static_cast<uint32_t>(d.P * d.P), g.B);
+                  static_cast<uint32_t>(np * nq), g.B);
   if (d.seq2head)
     hipLaunchKernelGGL((any_relayout_kernel<UNIT, true>), grid, dim3(kThreads), 0, stream, in,
                        out, g);

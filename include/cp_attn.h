@@ -229,6 +229,31 @@ cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int
                                        const int64_t* s_lens, const int64_t* h_counts, int64_t D,
                                        cp_dtype dtype, void* stream);
 
+/*
+ * cp_kv_gather — the unpack of the K/V all-gather: P sequence shards joined
+ * into one sequence, all heads kept.
+ *
+ * Defined by: the Sequence Parallelism page (SGLang Diffusion), section
+ * Choosing The Attention Exchange (kv_gather: queries and outputs stay
+ * sequence-sharded, K and V are all-gathered, each rank computes its own
+ * output directly; non-causal, ring degree 1). A rank's share is then
+ * cp_attn_chunk_partial of its query shard over the gathered K and V, or
+ * cp_ring_attention over the P shards in place (same result).
+ *   out[b][off_q + s][h][d] = in_q[b][s][h][d],
+ *   off_q = s_lens[0] + ... + s_lens[q-1]
+ *
+ *   in:  the P shards packed back to back in rank order; shard q is
+ *        [B][s_lens[q]][H][D] and starts at element B*off_q*H*D.
+ *   out: [B][S][H][D], S = sum of s_lens.
+ *   s_lens: HOST array of P counts (>= 0), read during the call only.
+ * For B = 1 the packed shards already are the gathered tensor and this is a
+ * plain copy. Same limits, bit-copy and error rules as
+ * cp_ulysses_anything_seq2head (it is that regrouping with a single head
+ * group holding all H heads).
+ */
+cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const int64_t* s_lens,
+                       int64_t H, int64_t D, cp_dtype dtype, void* stream);
+
 /* Text describing the last failed call on this thread ("" after a successful
  * call). Valid until the next cp_* call on the same thread. */
 const char* cp_last_error(void);

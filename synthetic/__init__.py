@@ -36,7 +36,7 @@ class Workload:
     dtype: torch.dtype
     causal: bool
     P: int  # ring degree (ring workloads) or Ulysses degree (Ulysses workloads)
-    kind: str  # "ring", "ulysses" or "ulysses_anything"
+    kind: str  # "ring", "ulysses", "ulysses_anything" or "kv_gather"
     # ring: K/V chunk lengths in sequence order; ulysses_anything: tokens per rank
     chunk_lens: Tuple[int, ...] = ()
 
@@ -92,8 +92,15 @@ FLUX_ANYTHING = Workload(6, "flux-1008-ulysses-anything4-rank0", S=63 * 63 + 512
                          dtype=torch.bfloat16, causal=False, P=4, kind="ulysses_anything",
                          chunk_lens=even_split(63 * 63 + 512, 4))
 
+# Wan 21x30x52 over a K/V-gather degree of 4 (the fastest tested topology for
+# Wan2.2 on the SGLang Diffusion page): rank r keeps its query shard and
+# attends to the K/V gathered from all 4 shards
+WAN_KV_GATHER = Workload(7, "wan-21x30x52-kvgather4-rank0", S=32760, H=40, D=128,
+                         dtype=torch.bfloat16, causal=False, P=4, kind="kv_gather",
+                         chunk_lens=even_split(32760, 4))
+
 WORKLOADS = {w.name: w for w in (TINY, FLUX_RING, QWEN_ULYSSES, WAN_ULYSSES, LLM_ULYSSES,
-                                 LLM_RING_ANYTHING, FLUX_ANYTHING)}
+                                 LLM_RING_ANYTHING, FLUX_ANYTHING, WAN_KV_GATHER)}
 
 
 def ring_order(rank: int, P: int) -> List[int]:

@@ -192,6 +192,23 @@ def test_anything_relayout_zero_size_is_noop(kw):
     assert _anything(cp._any_head2seq, **kw) == OK
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), INVALID), (dict(P=65), UNSUPPORTED), (dict(H=-1), INVALID),
+    (dict(s_lens=None), INVALID), (dict(inp=None), INVALID), (dict(dt=9), INVALID),
+    (dict(out=FAKE + 64), INVALID),
+])
+def test_kv_gather_rejects(kw, status):
+    args = dict(inp=FAKE, out=FAKE2, P=3, B=1, s_lens=(4, 3, 3), H=4, D=128, dt=BF16)
+    args.update(kw)
+    lens = args["s_lens"]
+    if lens is not None and len(lens) != args["P"] and args["P"] > 0:
+        lens = [1] * args["P"]
+    arr, ptr = cp._counts(lens) if lens is not None else (None, None)
+    assert cp._kv_gather(args["inp"], args["out"], args["P"], args["B"], ptr, args["H"], args["D"],
+                         args["dt"], None) == status
+    assert cp.last_error().startswith("cp_kv_gather")
+
+
 def test_error_text_cleared_by_success():
     assert _partial(D=96) == UNSUPPORTED and cp.last_error() != ""
     assert _partial(Sq=0) == OK and cp.last_error() == ""

@@ -139,6 +139,20 @@ def test_anything_relayout_misaligned_base_uses_narrow_words():
     assert np.array_equal(out[1:].cpu().view(torch.int16).numpy(), want)
 
 
+@pytest.mark.parametrize("s_lens,B,H,D", [((5, 3, 4), 2, 3, 128), ((0, 7, 2), 1, 2, 64),
+                                         ((6,), 2, 1, 32)])
+def test_kv_gather_bit_exact(s_lens, B, H, D):
+    say(f"kv gather s={s_lens} B={B} H={H} D={D}")
+    S = sum(s_lens)
+    bits = synthetic.random_bits((B * S * H * D,), 2, seed=S * 3 + H)
+    x = bits.view(torch.bfloat16).to(DEV)
+    y = cp.kv_gather(x, s_lens, B, H, D)
+    torch.cuda.synchronize()
+    sizes = [B * sq * H * D for sq in s_lens]
+    shards = _split(bits.numpy(), sizes, [(B, sq, H, D) for sq in s_lens])
+    assert np.array_equal(y.cpu().view(torch.int16).numpy(), oracle.kv_gather(shards))
+
+
 # ---------------------------------------------------------------------- merge
 
 @pytest.mark.parametrize("P,D", [(1, 128), (2, 128), (4, 128), (7, 128), (8, 64),

@@ -160,3 +160,36 @@ def test_ulysses_anything_flux1008_rank0():
     idx = torch.from_numpy(rows).to(DEV)
     check_o(o[:, idx], wo, "bf16", "rank 0 O (sampled rows)")
     check_lse(lse[:, :, idx], wl, "rank 0 LSE (sampled rows)")
+
+
+def test_kv_gather_wan_rank0():
+    """Wan 21x30x52 with a K/V-gather degree of 4: rank 0 keeps its 8190 query
+    rows and attends to the K/V gathered from all shards. Computed both from
+    the gathered tensors and from the shards in place (ring call); each is
+    checked against the oracle on sampled rows."""
+    w = synthetic.WAN_KV_GATHER
+    S, H, D, lens = w.S, w.H, w.D, list(w.chunk_lens)
+    say(f"{w.name}: generating inputs")
+    q, k, v = synthetic.make_qkv(w)
+    kd, vd = k.to(DEV), v.to(DEV)
+    say(f"{w.name}: gather K and V")
+    kg = cp.kv_gather(kd.reshape(-1), lens, 1, H, D)
+    vg = cp.kv_gather(vd.reshape(-1), lens, 1, H, D)
+    torch.cuda.synchronize()
+    assert torch.equal(kg.view(torch.int16), kd.view(torch.int16))
+    n0 = lens[0]
+    q0 = q[:, :n0].contiguous().to(DEV)
+    say(f"{w.name}: rank 0 attention over the gathered K/V")
+    o1, l1 = cp.attn_chunk_partial(q0, kg, vg, out_dtype=torch.bfloat16)
+    say(f"{w.name}: rank 0 attention over the shards in place")
+    shards = [(kd[:, s:s + n].contiguous(), vd[:, s:s + n].contiguous(), s)
+              for s, n in zip(w.chunk_starts(), lens)]
+    o2, l2 = cp.ring_attention(q0, shards)
+    torch.cuda.synchronize()
+    rows = _rows(n0, 32, 96, seed=w.seed)
+    say(f"{w.name}: oracle on {len(rows)} rows x {H} heads")
+    wo, wl = oracle.attention(to_f64(q[:, rows]), to_f64(k), to_f64(v), 1 / math.sqrt(D))
+    idx = torch.from_numpy(rows).to(DEV)
+    for o, lse, tag in ((o1, l1, "gathered"), (o2, l2, "shards")):
+        check_o(o[:, idx], wo, "bf16", f"rank 0 O ({tag})")
+        check_lse(lse[:, :, idx], wl, f"rank 0 LSE ({tag})")
