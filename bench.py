@@ -132,7 +132,7 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run only this detail workload (qwen, wan, llm, ra, merge, anything, "
-                         "kvgather) "
+                         "kvgather, unified) "
                          "after the "
                          "headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,6 +253,8 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
                                                                       flush)
     if want("kvgather"):
         out[synthetic.WAN_KV_GATHER.name] = kv_gather_workload(torch, cp, synthetic, dev, flush)
+    if want("unified"):
+        out[synthetic.FLUX_UNIFIED.name] = unified_workload(torch, cp, synthetic, dev)
     return out
 
 
@@ -381,6 +383,56 @@ def kv_gather_workload(torch, cp, synthetic, dev, flush):
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, gather {res['gather_gbs']:.0f} GB/s")
     del q, k, v, kg, vg, q0, o, lse
     torch.cuda.empty_cache()
+    return res
+
+
+def unified_workload(torch, cp, synthetic, dev):
+    """FLUX 1024x1024 as Ulysses 2 x ring 2: one rank's whole step (Ulysses regrouping of
+    Q, K, V inside both segments, ring attention, inverse regrouping of O)."""
+    w = synthetic.FLUX_UNIFIED
+    log(f"{w.name}: inputs")
+    R = len(w.chunk_lens)
+    U = w.P // R
+    S, H, D, seg = w.S, w.H, w.D, w.chunk_lens[0]
+    sub = seg // U
+    q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
+    shards = {n: [x[:, r * seg:(r + 1) * seg].reshape(U, 1, sub, H, D) for r in range(R)]
+              for n, x in (("q", q), ("k", k), ("v", v))}
+    grp = {n: [torch.empty((U, 1, seg, H // U, D), dtype=w.dtype, device=dev) for _ in range(R)]
+           for n in ("q", "k", "v")}
+    o_all = torch.empty((U, 1, seg, H // U, D), dtype=w.dtype, device=dev)
+    back = torch.empty((U, 1, sub, H, D), dtype=w.dtype, device=dev)
+    lse = torch.empty((1, H // U, seg), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(cp.ring_attention_workspace_bytes(R, 1, H // U, seg, D), 16),
+                     dtype=torch.uint8, device=dev)
+    r, u = 0, 0
+
+    def regroup():
+        for n in ("q", "k", "v"):
+            for c in range(R):
+                cp.ulysses_seq2head(shards[n][c], U, grp[n][c])
+
+    def attend():
+        chunks = [(grp["k"][c][u], grp["v"][c][u], c * seg) for c in range(R)]
+        cp.ring_attention(grp["q"][r][u], [chunks[c] for c in synthetic.ring_order(r, R)],
+                          o_all[u], lse, workspace=ws)
+
+    def step():
+        regroup()
+        attend()
+        cp.ulysses_head2seq(o_all, U, back)
+
+    flops = 4.0 * D * (H // U) * seg * S
+    d_att = time_launches(torch, attend, 3, 20)
+    d_step = time_launches(torch, step, 3, 20)
+    res = {"ulysses": U, "ring": R, "attn_us": median(d_att) * 1e3,
+           "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
+           "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "step_us": median(d_step) * 1e3,
+           "step_tflops": flops / (median(d_step) * 1e-3) / 1e12, "gflop": flops / 1e9,
+           "note": "step = Ulysses regrouping of Q, K, V for the rank's segment group and "
+                   "the other segment's K/V, ring attention, inverse regrouping of O"}
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, whole step {res['step_tflops']:.0f}")
     return res
 
 

@@ -36,8 +36,9 @@ class Workload:
     dtype: torch.dtype
     causal: bool
     P: int  # ring degree (ring workloads) or Ulysses degree (Ulysses workloads)
-    kind: str  # "ring", "ulysses", "ulysses_anything" or "kv_gather"
-    # ring: K/V chunk lengths in sequence order; ulysses_anything: tokens per rank
+    kind: str  # "ring", "ulysses", "ulysses_anything", "kv_gather" or "unified"
+    # ring: K/V chunk lengths in sequence order; ulysses_anything: tokens per rank;
+    # unified: ring segment lengths (each spread over P / len(chunk_lens) Ulysses ranks)
     chunk_lens: Tuple[int, ...] = ()
 
     @property
@@ -99,8 +100,15 @@ WAN_KV_GATHER = Workload(7, "wan-21x30x52-kvgather4-rank0", S=32760, H=40, D=128
                          dtype=torch.bfloat16, causal=False, P=4, kind="kv_gather",
                          chunk_lens=even_split(32760, 4))
 
+# FLUX 1024x1024 on 4 ranks as Ulysses 2 x ring 2 (the unified mode of the
+# diffusers guide's 4-GPU benchmark): 2 ring segments of 2304 tokens, each
+# spread over 2 Ulysses ranks
+FLUX_UNIFIED = Workload(8, "flux-1024-unified-u2r2-rank0", S=4608, H=24, D=128,
+                        dtype=torch.bfloat16, causal=False, P=4, kind="unified",
+                        chunk_lens=(2304, 2304))
+
 WORKLOADS = {w.name: w for w in (TINY, FLUX_RING, QWEN_ULYSSES, WAN_ULYSSES, LLM_ULYSSES,
-                                 LLM_RING_ANYTHING, FLUX_ANYTHING, WAN_KV_GATHER)}
+                                 LLM_RING_ANYTHING, FLUX_ANYTHING, WAN_KV_GATHER, FLUX_UNIFIED)}
 
 
 def ring_order(rank: int, P: int) -> List[int]:

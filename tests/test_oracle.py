@@ -430,6 +430,42 @@ def test_kv_gather_rank_share_is_full_attention_rows():
         assert np.allclose(l, full_l[:, :, off[r]:off[r + 1]], atol=1e-12)
 
 
+# -------------------------------------------------- unified (Ulysses x ring) composition
+
+@pytest.mark.parametrize("U,R,causal", [(2, 2, False), (2, 3, True), (3, 2, False)])
+def test_unified_sp_composition_is_full_attention(U, R, causal):
+    """Unified SP (Context parallelism guide (diffusers), section Unified
+    Attention): the sequence is cut into R ring segments, each spread over U
+    Ulysses ranks. Within a segment the Ulysses regrouping gives each rank the
+    whole segment for H/U heads; ring attention over the R segments (same head
+    group) then the inverse regrouping give every rank full attention for its
+    tokens."""
+    S_sub, H, D = 2, 2 * U, 3
+    S = U * R * S_sub
+    q, k, v = (_rand((1, S, H, D), 80 + i) for i in range(3))
+    full_o, _ = oracle.attention(q, k, v, 0.5, causal)
+    seg = U * S_sub
+
+    def regroup(x, r):  # segment r's U sub-shards -> U head groups over the segment
+        shards = x[:, r * seg:(r + 1) * seg].reshape(1, U, S_sub, H, D).transpose(1, 0, 2, 3, 4)
+        return oracle.seq2head(np.ascontiguousarray(shards), U)     # [U][1][seg][H/U][D]
+
+    qh = [regroup(q, r) for r in range(R)]
+    kh = [regroup(k, r) for r in range(R)]
+    vh = [regroup(v, r) for r in range(R)]
+    for r in range(R):
+        outs = []
+        for u in range(U):
+            chunks = [(kh[c][u], vh[c][u], np.arange(c * seg, (c + 1) * seg)) for c in range(R)]
+            order = [(r - t) % R for t in range(R)]
+            o, _ = oracle.ring_attention(qh[r][u], chunks, order, 0.5, causal,
+                                         q_pos=np.arange(r * seg, (r + 1) * seg))
+            outs.append(o)
+        back = oracle.head2seq(np.stack(outs), U)                    # [U][1][S_sub][H][D]
+        got = np.concatenate([back[u] for u in range(U)], axis=1)    # the segment's tokens
+        assert np.allclose(got, full_o[:, r * seg:(r + 1) * seg], atol=1e-12)
+
+
 # ---------------------------------------- planted mistakes are caught by the pins
 
 def _mutant(kind):
