@@ -29,13 +29,22 @@ Functions and the passages they follow:
                             the K/V all-gather's unpack (SGLang Diffusion
                             Sequence Parallelism, Choosing The Attention
                             Exchange: kv_gather)
+  backward.attention_grad   dQ, dK, dV of full attention by the chain rule
+  backward.backward_delta   Delta_i = <dO_i, O_i>
+  backward.chunk_grad       one K/V chunk's share of the backward from the saved
+                            LSE and Delta (Ulysses SP article: training with long
+                            contexts, notes 2: no stored score matrix; diffusers
+                            guide, Ring Attention, for the chunk decomposition)
 
-Every function is pinned in ``tests/test_oracle.py`` against closed forms,
+Every function is pinned in ``tests/test_oracle.py`` and
+``tests/test_oracle_backward.py`` against closed forms,
 hand-derived golden values (``tests/golden/``), identities, a library
-routine (torch's fp64 scaled_dot_product_attention) and explicit loops.
+routine (torch's fp64 scaled_dot_product_attention, and its autograd for the
+backward), finite differences and explicit loops.
 """
 from .attention import (attention, bf16_bits_to_f64, chunk_partial, chunk_positions,
                         lse_merge, ring_attention, softmax_matrix)
+from .backward import attention_grad, backward_delta, chunk_grad
 from .relayout import (anything_head2seq, anything_head2seq_loop, anything_seq2head,
                        anything_seq2head_loop, even_split, head2seq, head2seq_loop, kv_gather,
                        kv_gather_loop, seq2head, seq2head_loop)
@@ -43,4 +52,5 @@ from .relayout import (anything_head2seq, anything_head2seq_loop, anything_seq2h
 __all__ = ["attention", "chunk_partial", "lse_merge", "ring_attention", "softmax_matrix",
            "bf16_bits_to_f64", "chunk_positions", "seq2head", "head2seq", "seq2head_loop",
            "head2seq_loop", "anything_seq2head", "anything_head2seq", "anything_seq2head_loop",
-           "anything_head2seq_loop", "even_split", "kv_gather", "kv_gather_loop"]
+           "anything_head2seq_loop", "even_split", "kv_gather", "kv_gather_loop",
+           "attention_grad", "backward_delta", "chunk_grad"]
