@@ -14,6 +14,8 @@ Entry points (same names as the C ABI, without the ``cp_`` prefix):
   ulysses_anything_seq2head / ulysses_anything_head2seq
                        the same with uneven per-rank token and head counts
   kv_gather            the K/V all-gather's unpack (sequence shards joined)
+  attn_backward_delta  Delta_i = <dO_i, O_i>, the backward's per-row statistic
+  attn_chunk_backward  one K/V chunk's share of dQ, dK, dV from the saved LSE
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ CP_BF16, CP_F32 = 0, 1
 STATUS = {0: "CP_OK", 1: "CP_E_INVALID", 2: "CP_E_UNSUPPORTED", 3: "CP_E_DIVISIBILITY",
           4: "CP_E_WORKSPACE", 5: "CP_E_HIP"}
 MAX_RING_CHUNKS = 64
+BWD_ACCUMULATE_DQ, BWD_ACCUMULATE_DKV = 1, 2
 
 _i64, _vp, _f32, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
 
@@ -66,6 +69,9 @@ _any_seq2head = _sig("cp_ulysses_anything_seq2head",
 _any_head2seq = _sig("cp_ulysses_anything_head2seq",
                      [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
 _kv_gather = _sig("cp_kv_gather", [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp])
+_bwd_delta = _sig("cp_attn_backward_delta", [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp])
+_chunk_bwd = _sig("cp_attn_chunk_backward", [_vp] * 9 + [_i64] * 5 +
+                  [_int, _f32, _int, _i64, _i64, _int, _vp])
 _last_error = _sig("cp_last_error", [], ctypes.c_char_p)
 _abi_version = _sig("cp_abi_version", [])
 
@@ -278,7 +284,60 @@ def kv_gather(x: torch.Tensor, s_lens, B: int, H: int, D: int,
     return out
 
 
+def attn_backward_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None,
+                        *, stream=None) -> torch.Tensor:
+    """``delta [B][H][Sq]`` fp32 = <dO_i, O_i> per row; see cp_attn_backward_delta."""
+    B, Sq, H, D = _bshd(o, "o")
+    if tuple(dout.shape) != tuple(o.shape) or dout.dtype != o.dtype:
+        raise ValueError("o and dout must share shape and dtype")
+    if delta is None:
+        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=o.device)
+    _check("cp_attn_backward_delta", _bwd_delta(_ptr(o), _ptr(dout), _ptr(delta), B, H, Sq, D,
+                                                _dtype_code(o.dtype), _stream(stream)))
+    return delta
+
+
+def attn_chunk_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                        lse: torch.Tensor, delta: torch.Tensor, dq: Optional[torch.Tensor] = None,
+                        dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, *,
+                        scale: Optional[float] = None, causal: bool = False, q_pos0: int = 0,
+                        kv_pos0: int = 0, accumulate_dq: bool = False,
+                        accumulate_dkv: bool = False,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """One K/V chunk's share of (dQ, dK, dV) in fp32; see cp_attn_chunk_backward.
+
+    With ``accumulate_dq`` / ``accumulate_dkv`` the given buffers hold running
+    sums and the share is added to them; otherwise they are overwritten (and
+    allocated when not given)."""
+    B, Sq, H, D = _bshd(q, "q")
+    Bk, Skv, Hk, Dk = _bshd(k, "k")
+    if (Bk, Hk, Dk) != (B, H, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v shapes disagree")
+    if tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout must have q's shape")
+    if tuple(lse.shape) != (B, H, Sq) or tuple(delta.shape) != (B, H, Sq):
+        raise ValueError("lse and delta must be [B][H][Sq]")
+    if (accumulate_dq and dq is None) or (accumulate_dkv and (dk is None or dv is None)):
+        raise ValueError("accumulating needs the running-sum buffers")
+    f32 = torch.float32
+    dq = torch.empty((B, Sq, H, D), dtype=f32, device=q.device) if dq is None else dq
+    dk = torch.empty((B, Skv, H, D), dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty((B, Skv, H, D), dtype=f32, device=q.device) if dv is None else dv
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
+        if t.dtype != f32 or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must be float32 of shape {tuple(shape)}")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    flags = (BWD_ACCUMULATE_DQ if accumulate_dq else 0) | \
+        (BWD_ACCUMULATE_DKV if accumulate_dkv else 0)
+    _check("cp_attn_chunk_backward", _chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk),
+        _ptr(dv), B, H, Sq, Skv, D, _dtype_code(q.dtype), scale, int(causal), q_pos0, kv_pos0,
+        flags, _stream(stream)))
+    return dq, dk, dv
+
+
 __all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
            "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
-           "ulysses_anything_head2seq", "kv_gather", "last_error", "abi_version", "CpAttnError",
+           "ulysses_anything_head2seq", "kv_gather", "attn_backward_delta",
+           "attn_chunk_backward", "BWD_ACCUMULATE_DQ", "BWD_ACCUMULATE_DKV", "last_error", "abi_version", "CpAttnError",
            "KVChunk", "LIB_PATH"]

@@ -383,4 +383,90 @@ cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const in
   return any_relayout(fn, in, out, P, B, s_lens, h_counts, D, dtype, stream, true);
 }
 
+cp_status cp_attn_backward_delta(const void* o, const void* dout, float* delta, int64_t B,
+                                 int64_t H, int64_t Sq, int64_t D, cp_dtype dtype, void* stream) {
+  const char* fn = "cp_attn_backward_delta";
+  cp_status s = check_attn_common(fn, B, H, Sq, D, dtype, 0, 1.f);
+  if (s != CP_OK) return s;
+  if (B == 0 || H == 0 || Sq == 0) return ok();
+  const int64_t t_bytes = sat_mul({B, Sq, H, D, elem_size(dtype)});
+  const int64_t l_bytes = sat_mul({B, H, Sq, 4});
+  if (sat_mul({B, Sq, H}) > kMaxGrid / 2)
+    return fail(CP_E_UNSUPPORTED, "%s: B*Sq*H too large for one launch", fn);
+  if (!o || !dout || !delta) return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(delta, 4))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, delta 4 B)", fn);
+  if (overlap(delta, l_bytes, o, t_bytes) || overlap(delta, l_bytes, dout, t_bytes))
+    return fail(CP_E_INVALID, "%s: delta overlaps an input", fn);
+  return hip_status(cpattn::launch_bwd_delta(o, dout, delta, B, H, Sq, D, dtype == CP_BF16,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+cp_status cp_attn_chunk_backward(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* lse, const float* delta, float* dq, float* dk,
+                                 float* dv, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                 int64_t D, cp_dtype in_dtype, float scale, int causal,
+                                 int64_t q_pos0, int64_t kv_pos0, int flags, void* stream) {
+  const char* fn = "cp_attn_chunk_backward";
+  cp_status s = check_attn_common(fn, B, H, Sq, D, in_dtype, causal, scale);
+  if (s != CP_OK) return s;
+  if (Skv < 0) return fail(CP_E_INVALID, "%s: negative Skv", fn);
+  if (Skv >= kMaxSeq) return fail(CP_E_UNSUPPORTED, "%s: Skv exceeds 2^30", fn);
+  if (flags & ~(CP_BWD_ACCUMULATE_DQ | CP_BWD_ACCUMULATE_DKV))
+    return fail(CP_E_INVALID, "%s: unknown flag bits 0x%x", fn, flags);
+  if (in_dtype != CP_BF16)
+    return fail(CP_E_UNSUPPORTED, "%s: only bf16 inputs are built", fn);
+  if (sat_mul({(Skv + 63) / 64, B, H}) > kMaxGrid / 8)
+    return fail(CP_E_UNSUPPORTED, "%s: B*H*Skv too large for one launch", fn);
+  if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ok();
+  const int64_t q_bytes = sat_mul({B, Sq, H, D, 2}), kv_bytes = sat_mul({B, Skv, H, D, 2});
+  const int64_t dq_bytes = sat_mul({B, Sq, H, D, 4}), dkv_bytes = sat_mul({B, Skv, H, D, 4});
+  const int64_t l_bytes = sat_mul({B, H, Sq, 4});
+  const bool has_q = Sq > 0, has_kv = Skv > 0;
+  if ((has_q && (!q || !dout || !lse || !delta || !dq)) || (has_kv && (!k || !v || !dk || !dv)))
+    return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if ((has_q && (!aligned(q, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+                 !aligned(lse, 4) || !aligned(delta, 4))) ||
+      (has_kv && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse/delta 4 B)", fn);
+  {
+    const void* outs[3] = {dq, dk, dv};
+    const int64_t out_n[3] = {has_q ? dq_bytes : 0, has_kv ? dkv_bytes : 0,
+                              has_kv ? dkv_bytes : 0};
+    const void* ins[6] = {q, dout, k, v, lse, delta};
+    const int64_t in_n[6] = {has_q ? q_bytes : 0, has_q ? q_bytes : 0, has_kv ? kv_bytes : 0,
+                             has_kv ? kv_bytes : 0, has_q ? l_bytes : 0, has_q ? l_bytes : 0};
+    for (int x = 0; x < 3; ++x) {
+      for (int y = 0; y < 6; ++y)
+        if (overlap(outs[x], out_n[x], ins[y], in_n[y]))
+          return fail(CP_E_INVALID, "%s: an output overlaps an input", fn);
+      for (int y = x + 1; y < 3; ++y)
+        if (overlap(outs[x], out_n[x], outs[y], out_n[y]))
+          return fail(CP_E_INVALID, "%s: outputs overlap each other", fn);
+    }
+  }
+  cpattn::BwdArgs a{};
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = static_cast<int32_t>(B);
+  a.H = static_cast<int32_t>(H);
+  a.Sq = static_cast<int32_t>(Sq);
+  a.Skv = static_cast<int32_t>(Skv);
+  a.scale = scale;
+  a.diag = clamp_delta(q_pos0, kv_pos0, Sq, Skv);
+  a.accum_dq = (flags & CP_BWD_ACCUMULATE_DQ) ? 1 : 0;
+  a.accum_dkv = (flags & CP_BWD_ACCUMULATE_DKV) ? 1 : 0;
+  return hip_status(cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,577 @@
+// Backward of bf16 attention over one K/V chunk on CDNA4 matrix cores (gfx950).
+//
+// What it computes: the gradients of O = softmax(scale * Q K^T) V against an
+// upstream gradient dO, restricted to one K/V chunk, from the row statistics
+// the forward saved (the row log-sum-exp LSE, and Delta_i = <dO_i, O_i>):
+//   P_ij  = exp(scale <q_i, k_j> - LSE_i)         (0 for masked pairs)
+//   dS_ij = P_ij (<dO_i, v_j> - Delta_i)
+//   dQ_i  = scale * sum_j dS_ij k_j,  dK_j = scale * sum_i dS_ij q_i,
+//   dV_j  = sum_i P_ij dO_i.
+// With the full rows' LSE and Delta this is one chunk's exact share, so a ring
+// rank sums dQ over the chunks it visits and adds its dK, dV share into the
+// chunk's travelling accumulators (Context parallelism guide (diffusers),
+// section Ring Attention, run backwards); one chunk over the whole sequence is
+// a Ulysses rank's local backward (Ulysses Sequence Parallelism article:
+// training with long contexts; detailed notes 2: the score matrix is never
+// stored, so the weights are recomputed from the saved LSE).
+//
+// How it maps to the hardware. Two kernels, each owning one output and
+// writing it exactly once (no atomics: deterministic, and dQ / dK / dV can be
+// accumulated into the caller's fp32 buffers with a plain read-add-write):
+//  * dq kernel: a block keeps 128 query rows resident (4 waves x 32) and
+//    streams 64-key K/V tiles through double-buffered LDS. Per tile a wave
+//    computes S^T = K Q^T and dP^T = V dO^T (Q^T and dO^T are B operands held
+//    in registers), forms dS^T in the accumulator layout (lane = query), and
+//    adds dQ^T += K^T dS^T with K^T fragments read transposed from the same
+//    K tile (ds_read_b64_tr_b16).
+//  * dkdv kernel: a block keeps 128 keys resident and streams 64-row Q / dO
+//    tiles (plus those rows' LSE and Delta). Per 32-row half-tile a wave
+//    computes S = Q K^T and dP = dO V^T (K^T and V^T are register B
+//    operands), so the accumulators hold P and dS with lane = key, then adds
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+//  * Every streamed tile sits in LDS with row bits 2 and 3 swapped and its
+//    16-byte units XOR-swizzled by the row. With the swap, the 32x32
+//    accumulator registers of lane l hold 8 consecutive tile rows per
+//    half-wave, which is exactly the B-operand layout of the next product, so
+//    P and dS feed the second products without data movement; the transposed
+//    reads of the same tile find those rows as two groups of four.
+//  * Direct global->LDS loads (global_load_lds_dwordx4) fill the tiles with
+//    no staging registers; one barrier per tile.
+//  * The softmax weights use exp2 with scale*log2(e) folded into one FMA per
+//    score and the LSE pre-multiplied by log2(e).
+//  * A row whose LSE is -inf saw no key anywhere: its weights are 0.
+#include "cp_internal.h"
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kBlk = 128;      // resident rows per block (queries or keys)
+constexpr int kTile = 64;      // streamed rows per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int swap_bits23(int r) {
+  return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 12);
+}
+
+template <int D>
+struct Geo {
+  static constexpr int kUPR = D / 8;                            // 16-byte units per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kLoadsPerWave = kTile * kUPR / kThreads;  // direct loads per tile per wave
+  static constexpr int kMask = kUPR - 1 < 15 ? kUPR - 1 : 15;    // swizzle row bits
+};
+
+// Byte offset of 16-byte unit `unit` of LDS row `row` within a tile.
+template <int D>
+__device__ __forceinline__ uint32_t unit_off(int row, int unit) {
+  return row * Geo<D>::kRowBytes + ((unit ^ (row & Geo<D>::kMask)) << 4);
+}
+
+__device__ __forceinline__ void lds_load16(const char* g, char* l) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), reinterpret_cast<void*>(l),
+                                   16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 read_tr(const char* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Per-lane geometry of one streamed tile: direct-load sources and fragment
+// read offsets (bytes within the tile).
+template <int D>
+struct TileGeo {
+  static constexpr int NL = Geo<D>::kLoadsPerWave;
+  int src_row[NL];     // tile row each direct load fetches
+  uint32_t src[NL];    // its byte offset from the tile's first row (row stride rs)
+  uint32_t n_rd[D / 16];                 // normal fragment: LDS row = lane%32, unit 2ks + half
+  uint32_t t_lo[D / 32], t_hi[D / 32];   // transposed fragment, k-step 0 (add 16 t rows)
+
+  __device__ void init(int wave, int lane, int rs) {
+    constexpr int UPR = Geo<D>::kUPR;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      // LDS slot s = (row, unit) holds tile row swap(row), unit s%UPR ^ (row & mask)
+      const int s = (wave * NL + n) * 64 + lane;
+      const int row = s / UPR, pu = s % UPR;
+      src_row[n] = swap_bits23(row);
+      src[n] = 2u * static_cast<uint32_t>(src_row[n] * rs + (pu ^ (row & Geo<D>::kMask)) * 8);
+    }
+    const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) n_rd[ks] = unit_off<D>(col, 2 * ks + half);
+    // ds_read_b64_tr_b16: in each 16-lane group, lane i addresses row r0 + i/4,
+    // elements el .. el+3, and receives element column (group's base) + i of
+    // rows r0 .. r0+3. LDS rows 4h .. 4h+3 hold tile rows 8h .. 8h+3 and rows
+    // 8+4h .. 8+4h+3 hold 8h+4 .. 8h+7 (bits 2/3 swapped), the 8 consecutive
+    // rows half-wave h needs in a 16-row k-step.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int r0 = 4 * (g16 >> 1) + (j16 >> 2);
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) {
+      const int el = 32 * md + 16 * (g16 & 1) + 4 * (j16 & 3);
+      t_lo[md] = unit_off<D>(r0, el >> 3) + ((el & 4) ? 8 : 0);
+      t_hi[md] = unit_off<D>(r0 + 8, el >> 3) + ((el & 4) ? 8 : 0);
+    }
+  }
+
+  // Direct loads of tile rows [row0, row0 + 64) of a [.][rs] bf16 tensor
+  // (`base` points at row 0, head offset included) into the tile at `dst`.
+  // Rows at or beyond n_rows are redirected to the last valid row.
+  __device__ void issue(const char* base, int row0, int n_rows, int rs, char* dst, int wave) const {
+    const char* g = base + 2 * static_cast<int64_t>(row0) * rs;
+    char* l = dst + wave * NL * 1024;
+    const int n_valid = n_rows - row0;
+    if (n_valid >= kTile) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) lds_load16(g + src[n], l + n * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const uint32_t fix =
+            src_row[n] < n_valid ? 0u : 2u * static_cast<uint32_t>((src_row[n] - n_valid + 1) * rs);
+        lds_load16(g + (src[n] - fix), l + n * 1024);
+      }
+    }
+  }
+
+  // A operand: tile^T rows d = 32 md + lane%32, k = tile rows 16 t + 8 half + 0..7
+  __device__ bf16x8 tr_frag(const char* tile, int md, int t) const {
+    const bf16x4 lo = read_tr(tile + t_lo[md] + 16 * t * Geo<D>::kRowBytes);
+    const bf16x4 hi = read_tr(tile + t_hi[md] + 16 * t * Geo<D>::kRowBytes);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // A operand: tile rows 32 mb + lane%32 (tile row swap of it), k = d 16 ks + 8 half + 0..7
+  __device__ bf16x8 frag(const char* tile, int mb, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(tile + n_rd[ks] + mb * 32 * Geo<D>::kRowBytes);
+  }
+};
+
+// One row of a [.][H][D] bf16 tensor as B-operand fragments: lane holds
+// elements 16 ks + 8 half .. +7 of row `row` (zeros if !valid); `flip` XORs
+// the sign bits.
+template <int D>
+__device__ __forceinline__ void load_row_frags(const __bf16* p, bool valid, uint32_t flip,
+                                               int half, bf16x8* f) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * ks + 8 * half);
+    w ^= flip;
+    if (!valid) w = u32x4{0, 0, 0, 0};
+    f[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// -log2(e) * LSE, with a row that saw no key (LSE = -inf) mapped to -inf so
+// that its weights exp2(s * sl2 + nl) are 0.
+__device__ __forceinline__ float neg_lse2(float lse) {
+  return lse == -INFINITY ? -INFINITY : -lse * kLog2e;
+}
+
+// Store 4 consecutive fp32 values scaled by `s`, adding the old values if `acc`.
+__device__ __forceinline__ void store4(float* p, float s, float x0, float x1, float x2, float x3,
+                                      bool acc) {
+  float4 r = make_float4(s * x0, s * x1, s * x2, s * x3);
+  if (acc) {
+    const float4 o = *reinterpret_cast<const float4*>(p);
+    r.x += o.x;
+    r.y += o.y;
+    r.z += o.z;
+    r.w += o.w;
+  }
+  *reinterpret_cast<float4*>(p) = r;
+}
+
+// Block index -> (work item) with consecutive ids spread over the 8 XCDs and
+// each XCD taking a contiguous run of items (the tiles of one head stay in
+// one L2). Returns -1 for the padding blocks of the last round.
+__device__ __forceinline__ int xcd_item(int nitems) {
+  const int per_xcd = (nitems + 7) / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  return L < nitems ? L : -1;
+}
+
+// ---------------------------------------------------------------- dQ kernel
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int TB = Geo<D>::kTileBytes;
+  constexpr int RB = Geo<D>::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // stage s: K at 2s, V at 2s+1
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int BH = a.B * a.H;
+  const int nqt = (a.Sq + kBlk - 1) / kBlk;
+  int bh, qt;
+  if (CAUSAL) {  // the last query tiles see the most keys: launch them first
+    qt = nqt - 1 - static_cast<int>(blockIdx.x) / BH;
+    bh = static_cast<int>(blockIdx.x) % BH;
+  } else {
+    const int L = xcd_item(nqt * BH);
+    if (L < 0) return;
+    bh = L / nqt;
+    qt = L % nqt;
+  }
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int i = qt * kBlk + wave * 32 + col;  // this lane's query row
+  const bool valid = i < a.Sq;
+  const int ic = valid ? i : a.Sq - 1;
+  const int q_first = qt * kBlk, q_last = min(q_first + kBlk - 1, a.Sq - 1);
+  const int rs = a.H * D;
+
+  // resident B operands: Q^T (sign of the scale folded in) and dO^T
+  bf16x8 qf[D / 16], df[D / 16];
+  const int64_t qrow = (static_cast<int64_t>(b) * a.Sq + ic) * a.H + h;
+  load_row_frags<D>(a.q + qrow * D, valid, a.scale < 0.f ? 0x80008000u : 0u, half, qf);
+  load_row_frags<D>(a.dout + qrow * D, valid, 0u, half, df);
+  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + ic;
+  const float nl = valid ? neg_lse2(a.lse[lrow]) : -INFINITY;
+  const float dlt = valid ? a.delta[lrow] : 0.f;
+  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+
+  int nkeys = a.Skv;
+  if (CAUSAL) nkeys = max(0, min(nkeys, q_last + a.diag + 1));
+  const int ntiles = (nkeys + kTile - 1) / kTile;
+
+  TileGeo<D> g;
+  g.init(wave, lane, rs);
+  const char* kbase = reinterpret_cast<const char*>(a.k + (static_cast<int64_t>(b) * a.Skv * a.H + h) * D);
+  const char* vbase = reinterpret_cast<const char*>(a.v + (static_cast<int64_t>(b) * a.Skv * a.H + h) * D);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) acc[md] = f32x16{};
+
+  if (ntiles > 0) {
+    g.issue(kbase, 0, a.Skv, rs, smem, wave);
+    g.issue(vbase, 0, a.Skv, rs, smem + TB, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j & 1;
+    const char* kl = smem + 2 * st * TB;
+    const char* vl = kl + TB;
+    if (j + 1 < ntiles) {
+      char* nk = smem + 2 * (st ^ 1) * TB;
+      g.issue(kbase, (j + 1) * kTile, a.Skv, rs, nk, wave);
+      g.issue(vbase, (j + 1) * kTile, a.Skv, rs, nk + TB, wave);
+    }
+    const int key0 = j * kTile;
+    // S^T and dP^T for the tile's 64 keys (two 32-key blocks); register r of
+    // block mb is key key0 + 32 mb + 16 (r/8) + 8 half + r%8
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = mfma(g.frag(kl, mb, 0), qf[0], f32x16{});
+      dp[mb] = mfma(g.frag(vl, mb, 0), df[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < D / 16; ++ks) {
+        s[mb] = mfma(g.frag(kl, mb, ks), qf[ks], s[mb]);
+        dp[mb] = mfma(g.frag(vl, mb, ks), df[ks], dp[mb]);
+      }
+    }
+    const bool masked = key0 + kTile > a.Skv || (CAUSAL && key0 + kTile - 1 > q_first + a.diag);
+    if (masked) {
+      int lim = a.Skv - key0;
+      if (CAUSAL) lim = min(lim, i + a.diag - key0 + 1);
+      lim -= 8 * half;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s[mb][r] = -INFINITY;
+    }
+    // dS^T, rounded to bf16: B operand of k-step t (keys 16 t + 8 half + e)
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int mb = t >> 1, r = (t & 1) * 8 + e;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, nl));
+        dsf[t][e] = static_cast<__bf16>(p * (dp[mb][r] - dlt));
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[md] = mfma(g.tr_frag(kl, md, t), dsf[t], acc[md]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  (void)RB;
+
+  if (!valid) return;
+  // dQ^T register r of block md is element d = 32 md + 8 (r/4) + 4 half + r%4
+  float* out = a.dq + qrow * D;
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      store4(out + 32 * md + 8 * q4 + 4 * half, a.scale, acc[md][4 * q4], acc[md][4 * q4 + 1],
+             acc[md][4 * q4 + 2], acc[md][4 * q4 + 3], a.accum_dq != 0);
+}
+
+// -------------------------------------------------------------- dK/dV kernel
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int TB = Geo<D>::kTileBytes;
+  // stage s: Q tile at 2s*TB, dO tile at (2s+1)*TB; LSE and Delta rows of
+  // stage s at 4*TB + 512 s (64 floats each)
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 1024];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int BH = a.B * a.H;
+  const int nkt = (a.Skv + kBlk - 1) / kBlk;
+  int bh, kt;
+  if (CAUSAL) {  // the first key tiles are seen by the most queries: launch them first
+    kt = static_cast<int>(blockIdx.x) / BH;
+    bh = static_cast<int>(blockIdx.x) % BH;
+  } else {
+    const int L = xcd_item(nkt * BH);
+    if (L < 0) return;
+    bh = L / nkt;
+    kt = L % nkt;
+  }
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int jk = kt * kBlk + wave * 32 + col;  // this lane's key
+  const bool valid = jk < a.Skv;
+  const int jc = valid ? jk : a.Skv - 1;
+  const int k_first = kt * kBlk, k_last = min(k_first + kBlk - 1, a.Skv - 1);
+  const int rs = a.H * D;
+
+  // resident B operands: K^T (sign of the scale folded in) and V^T
+  bf16x8 kf[D / 16], vf[D / 16];
+  const int64_t krow = (static_cast<int64_t>(b) * a.Skv + jc) * a.H + h;
+  load_row_frags<D>(a.k + krow * D, valid, a.scale < 0.f ? 0x80008000u : 0u, half, kf);
+  load_row_frags<D>(a.v + krow * D, valid, 0u, half, vf);
+  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+
+  // query tiles that can see this block's keys
+  int qt0 = 0;
+  if (CAUSAL) {
+    const int qmin = k_first - a.diag;  // first query that sees key k_first
+    qt0 = qmin <= 0 ? 0 : qmin / kTile;
+  }
+  const int nqt = (a.Sq + kTile - 1) / kTile;
+  const int ntiles = max(0, nqt - qt0);
+
+  TileGeo<D> g;
+  g.init(wave, lane, rs);
+  const char* qbase = reinterpret_cast<const char*>(a.q + (static_cast<int64_t>(b) * a.Sq * a.H + h) * D);
+  const char* dbase = reinterpret_cast<const char*>(a.dout + (static_cast<int64_t>(b) * a.Sq * a.H + h) * D);
+  const int64_t lbase = (static_cast<int64_t>(b) * a.H + h) * a.Sq;
+  auto issue = [&](int st, int q0) {
+    char* dst = smem + 2 * st * TB;
+    g.issue(qbase, q0, a.Sq, rs, dst, wave);
+    g.issue(dbase, q0, a.Sq, rs, dst + TB, wave);
+    if (wave == 0) {  // 64 LSE and 64 Delta values, one per lane (clamped to the last row)
+      const int64_t r = lbase + min(q0 + lane, a.Sq - 1);
+      float* ls = reinterpret_cast<float*>(smem + 4 * TB + 512 * st);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.lse + r),
+                                       reinterpret_cast<void*>(ls), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.delta + r),
+                                       reinterpret_cast<void*>(ls + 64), 4, 0, 0);
+    }
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) {
+    dk[md] = f32x16{};
+    dv[md] = f32x16{};
+  }
+
+  if (ntiles > 0) issue(0, qt0 * kTile);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j & 1;
+    const char* ql = smem + 2 * st * TB;
+    const char* dl = ql + TB;
+    const float* ls = reinterpret_cast<const float*>(smem + 4 * TB + 512 * st);
+    const float* dt = ls + 64;
+    if (j + 1 < ntiles) issue(st ^ 1, (qt0 + j + 1) * kTile);
+    const int q0 = (qt0 + j) * kTile;
+    const bool masked = q0 + kTile > a.Sq || (CAUSAL && q0 + a.diag < k_last);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      // S and dP for 32 query rows; register r is tile row 32 mb + 16 (r/8) + 8 half + r%8
+      f32x16 s = mfma(g.frag(ql, mb, 0), kf[0], f32x16{});
+      f32x16 dp = mfma(g.frag(dl, mb, 0), vf[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < D / 16; ++ks) {
+        s = mfma(g.frag(ql, mb, ks), kf[ks], s);
+        dp = mfma(g.frag(dl, mb, ks), vf[ks], dp);
+      }
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 32 * mb + 16 * (r >> 3) + 8 * half + (r & 7);
+          if (qi >= a.Sq || (CAUSAL && jk > qi + a.diag)) s[r] = -INFINITY;
+        }
+      }
+      bf16x8 pf[2], sf[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int row = 32 * mb + 16 * t2 + 8 * half;
+        const float4 l0 = *reinterpret_cast<const float4*>(ls + row);
+        const float4 l1 = *reinterpret_cast<const float4*>(ls + row + 4);
+        const float4 d0 = *reinterpret_cast<const float4*>(dt + row);
+        const float4 d1 = *reinterpret_cast<const float4*>(dt + row + 4);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * t2 + e;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, neg_lse2(lv[e])));
+          pf[t2][e] = static_cast<__bf16>(p);
+          sf[t2][e] = static_cast<__bf16>(p * (dp[r] - dv8[e]));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (k-steps 2 mb, 2 mb + 1)
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          dv[md] = mfma(g.tr_frag(dl, md, 2 * mb + t2), pf[t2], dv[md]);
+          dk[md] = mfma(g.tr_frag(ql, md, 2 * mb + t2), sf[t2], dk[md]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (!valid) return;
+  // register r of block md is element d = 32 md + 8 (r/4) + 4 half + r%4 of key jk
+  float* ok = a.dk + krow * D;
+  float* ov = a.dv + krow * D;
+  const bool acc = a.accum_dkv != 0;
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * md + 8 * q4 + 4 * half;
+      store4(ok + d0, a.scale, dk[md][4 * q4], dk[md][4 * q4 + 1], dk[md][4 * q4 + 2],
+             dk[md][4 * q4 + 3], acc);
+      store4(ov + d0, 1.f, dv[md][4 * q4], dv[md][4 * q4 + 1], dv[md][4 * q4 + 2],
+             dv[md][4 * q4 + 3], acc);
+    }
+}
+
+// ------------------------------------------------------------- Delta kernel
+// Delta[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d] in fp32; 16 lanes per
+// row, each reading D/16 consecutive elements.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const T* o, const T* dout, float* delta,
+                                                        int64_t rows, int H, int Sq) {
+  constexpr int E = D / 16;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (row >= rows) return;  // whole 16-lane groups leave together
+  const T* po = o + row * D + sub * E;
+  const T* pd = dout + row * D + sub * E;
+  float acc = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 vecE __attribute__((ext_vector_type(E)));
+    const vecE x = *reinterpret_cast<const vecE*>(po);
+    const vecE y = *reinterpret_cast<const vecE*>(pd);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = __builtin_fmaf(static_cast<float>(x[e]), static_cast<float>(y[e]), acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(po + e);
+      const float4 y = *reinterpret_cast<const float4*>(pd + e);
+      acc = __builtin_fmaf(x.x, y.x, acc);
+      acc = __builtin_fmaf(x.y, y.y, acc);
+      acc = __builtin_fmaf(x.z, y.z, acc);
+      acc = __builtin_fmaf(x.w, y.w, acc);
+    }
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (sub == 0) {
+    const int h = static_cast<int>(row % H);
+    const int64_t bi = row / H;
+    const int i = static_cast<int>(bi % Sq);
+    const int64_t bb = bi / Sq;
+    delta[(bb * H + h) * Sq + i] = acc;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int64_t BH = static_cast<int64_t>(a.B) * a.H;
+  const int64_t nqt = (a.Sq + kBlk - 1) / kBlk, nkt = (a.Skv + kBlk - 1) / kBlk;
+  const int64_t dq_blocks = CAUSAL ? nqt * BH : (nqt * BH + 7) / 8 * 8;
+  const int64_t kv_blocks = CAUSAL ? nkt * BH : (nkt * BH + 7) / 8 * 8;
+  if (kv_blocks > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(static_cast<uint32_t>(kv_blocks)),
+                       dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dq_blocks > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<uint32_t>(dq_blocks)),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream) {
+  if (D == 64) return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
+  return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+}
+
+hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t B, int64_t H,
+                            int64_t Sq, int64_t D, bool bf16, hipStream_t stream) {
+  const int64_t rows = B * Sq * H;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>((rows + 15) / 16)), block(256);
+  const int h = static_cast<int>(H), s = static_cast<int>(Sq);
+  if (bf16) {
+    if (D == 64)
+      hipLaunchKernelGGL((bwd_delta_kernel<__bf16, 64>), grid, block, 0, stream,
+                         static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta,
+                         rows, h, s);
+    else
+      hipLaunchKernelGGL((bwd_delta_kernel<__bf16, 128>), grid, block, 0, stream,
+                         static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta,
+                         rows, h, s);
+  } else {
+    if (D == 64)
+      hipLaunchKernelGGL((bwd_delta_kernel<float, 64>), grid, block, 0, stream,
+                         static_cast<const float*>(o), static_cast<const float*>(dout), delta,
+                         rows, h, s);
+    else
+      hipLaunchKernelGGL((bwd_delta_kernel<float, 128>), grid, block, 0, stream,
+                         static_cast<const float*>(o), static_cast<const float*>(dout), delta,
+                         rows, h, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

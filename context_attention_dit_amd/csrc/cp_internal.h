@@ -99,6 +99,26 @@ int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles);
 // fp32 elements of partial output the split needs: nsplit*(B*Sq*H*D + B*H*Sq).
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D);
 
+// ----- backward (attn_bwd.hip)
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dout;
+  const float* lse;    // [B][H][Sq], the full rows' LSE
+  const float* delta;  // [B][H][Sq], <dO_i, O_i>
+  float* dq;           // [B][Sq][H][D]
+  float* dk;           // [B][Skv][H][D]
+  float* dv;           // [B][Skv][H][D]
+  int32_t B, H, Sq, Skv;
+  float scale;
+  int32_t diag;  // causal: key j visible to query i iff j <= i + diag (clamped like ChunkDesc)
+  int32_t accum_dq, accum_dkv;  // add into dq / dk, dv instead of overwriting
+};
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
+hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t B, int64_t H,
+                            int64_t Sq, int64_t D, bool bf16, hipStream_t stream);
+
 // out_bf16: write O as bf16 (else fp32). causal: position-based masking.
 hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, bool causal, hipStream_t stream);

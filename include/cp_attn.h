@@ -254,6 +254,62 @@ cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int
 cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const int64_t* s_lens,
                        int64_t H, int64_t D, cp_dtype dtype, void* stream);
 
+/*
+ * cp_attn_backward_delta — the per-row statistic the backward needs besides LSE:
+ *   delta[b][h][i] = sum_d dout[b][i][h][d] * o[b][i][h][d]   (fp32)
+ *
+ * Defined by: the derivative of softmax attention (the pages' training
+ * context is the Ulysses Sequence Parallelism article, summary and detailed
+ * notes 2 and 6-8): for the exact output, <dO_i, O_i> equals
+ * sum_j P_ij <dO_i, v_j>, the term the softmax Jacobian subtracts. Pass the
+ * FULL attention output (after every ring hop is merged), not a chunk's.
+ *
+ *   o, dout [B][Sq][H][D], both in `dtype` (CP_BF16 or CP_F32); delta [B][H][Sq]
+ *   fp32, caller-allocated. D in {64, 128}. Products and sum in fp32, in a
+ *   fixed order.
+ */
+cp_status cp_attn_backward_delta(const void* o, const void* dout, float* delta, int64_t B,
+                                 int64_t H, int64_t Sq, int64_t D, cp_dtype dtype, void* stream);
+
+/* Flags of cp_attn_chunk_backward. */
+#define CP_BWD_ACCUMULATE_DQ 1  /* dq += this chunk's share (else dq = share)        */
+#define CP_BWD_ACCUMULATE_DKV 2 /* dk, dv += this Q shard's share (else dk, dv = it) */
+
+/*
+ * cp_attn_chunk_backward — one K/V chunk's share of the attention backward.
+ *
+ * Defined by: the derivative of O = softmax(scale Q K^T) V (see
+ * cp_attn_backward_delta for the pages' training context), split by K/V chunk
+ * as the ring splits the forward (Context parallelism guide (diffusers),
+ * section Ring Attention). From the full rows' LSE and delta:
+ *   P_ij  = exp(scale <q_i, k_j> - LSE_i)   (0 for masked pairs and rows with LSE = -inf)
+ *   dS_ij = P_ij (<dO_i, v_j> - delta_i)
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dO_i
+ * Summing dq over a rank's chunks gives its full dQ (CP_BWD_ACCUMULATE_DQ);
+ * adding every rank's dk, dv for a chunk gives that chunk's full dK, dV
+ * (CP_BWD_ACCUMULATE_DKV). One chunk over the whole sequence is a Ulysses
+ * rank's local backward.
+ *
+ *   q, dout [B][Sq][H][D] and k, v [B][Skv][H][D] in in_dtype (CP_BF16 only);
+ *   lse, delta [B][H][Sq] fp32 (lse in the cp_attn_chunk_partial convention);
+ *   dq [B][Sq][H][D] and dk, dv [B][Skv][H][D] fp32, caller-allocated; with an
+ *   ACCUMULATE flag the buffer must hold the running sum, else it is
+ *   overwritten. causal, q_pos0, kv_pos0 and scale as in cp_attn_chunk_partial
+ *   and equal to the forward's.
+ *
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are rounded
+ * to bf16 for their products (as P is in the forward). Each output element is
+ * written once by one block (no atomics), so results are byte-identical on
+ * repeat. Sq == 0 gives dk = dv = 0 (unchanged when accumulating); Skv == 0
+ * gives dq = 0 (unchanged when accumulating). D in {64, 128}; Sq, Skv < 2^30.
+ * Two kernel launches; no workspace.
+ */
+cp_status cp_attn_chunk_backward(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* lse, const float* delta, float* dq, float* dk,
+                                 float* dv, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                 int64_t D, cp_dtype in_dtype, float scale, int causal,
+                                 int64_t q_pos0, int64_t kv_pos0, int flags, void* stream);
+
 /* Text describing the last failed call on this thread ("" after a successful
  * call). Valid until the next cp_* call on the same thread. */
 const char* cp_last_error(void);

@@ -212,3 +212,54 @@ def test_kv_gather_rejects(kw, status):
 def test_error_text_cleared_by_success():
     assert _partial(D=96) == UNSUPPORTED and cp.last_error() != ""
     assert _partial(Sq=0) == OK and cp.last_error() == ""
+
+
+FAKE7, FAKE8, FAKE9, FAKE10 = 0x7f6000000000, 0x7f7000000000, 0x7f8000000000, 0x7f9000000000
+
+
+def _chunk_bwd(q=FAKE, k=FAKE2, v=FAKE3, do=FAKE4, lse=FAKE5, delta=FAKE6, dq=FAKE7, dk=FAKE8,
+               dv=FAKE9, B=1, H=2, Sq=8, Skv=8, D=128, dt=BF16, scale=0.1, causal=0, qp=0, kp=0,
+               flags=0):
+    return cp._chunk_bwd(q, k, v, do, lse, delta, dq, dk, dv, B, H, Sq, Skv, D, dt, scale, causal,
+                         qp, kp, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), UNSUPPORTED), (dict(dt=F32), UNSUPPORTED), (dict(dt=7), INVALID),
+    (dict(B=-1), INVALID), (dict(Skv=-1), INVALID), (dict(Skv=1 << 30), UNSUPPORTED),
+    (dict(Sq=1 << 30), UNSUPPORTED), (dict(causal=2), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(flags=4), INVALID),
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(lse=None), INVALID),
+    (dict(delta=None), INVALID), (dict(dq=None), INVALID), (dict(k=None), INVALID),
+    (dict(dk=None), INVALID), (dict(dv=None), INVALID),
+    (dict(q=FAKE + 8), INVALID), (dict(dq=FAKE7 + 4), INVALID), (dict(lse=FAKE5 + 2), INVALID),
+    (dict(dq=FAKE + 64), INVALID),        # dq overlaps q
+    (dict(dv=FAKE8 + 64), INVALID),       # dv overlaps dk
+    (dict(dk=FAKE5), INVALID),            # dk overlaps lse
+])
+def test_chunk_backward_rejects(kw, status):
+    assert _chunk_bwd(**kw) == status
+    assert cp.last_error().startswith("cp_attn_chunk_backward")
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Sq=0, Skv=0)])
+def test_chunk_backward_zero_size_is_noop(kw):
+    assert _chunk_bwd(**kw) == OK and cp.last_error() == ""
+
+
+def _delta(o=FAKE, do=FAKE2, delta=FAKE3, B=1, H=2, Sq=8, D=128, dt=BF16):
+    return cp._bwd_delta(o, do, delta, B, H, Sq, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=32), UNSUPPORTED), (dict(dt=5), INVALID), (dict(Sq=-2), INVALID),
+    (dict(o=None), INVALID), (dict(delta=None), INVALID), (dict(do=FAKE2 + 8), INVALID),
+    (dict(delta=FAKE + 4), INVALID),
+])
+def test_backward_delta_rejects(kw, status):
+    assert _delta(**kw) == status
+    assert cp.last_error().startswith("cp_attn_backward_delta")
+
+
+def test_backward_delta_zero_size_is_noop():
+    assert _delta(Sq=0, o=None, do=None, delta=None) == OK
