@@ -132,7 +132,7 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run only this detail workload (qwen, wan, llm, ra, merge, anything, "
-                         "kvgather, unified) "
+                         "kvgather, unified, bwd) "
                          "after the "
                          "headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -255,6 +255,64 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
         out[synthetic.WAN_KV_GATHER.name] = kv_gather_workload(torch, cp, synthetic, dev, flush)
     if want("unified"):
         out[synthetic.FLUX_UNIFIED.name] = unified_workload(torch, cp, synthetic, dev)
+    if want("bwd"):
+        out.update(backward_workloads(torch, cp, synthetic, dev, q0, vis, wf))
+    return out
+
+
+def backward_workloads(torch, cp, synthetic, dev, q0, vis, wf):
+    """Attention backward: the FLUX ring rank's share (Delta, then one
+    cp_attn_chunk_backward per chunk in ring order: dQ accumulated over the
+    chunks, each chunk's dK/dV share written for its owner) and the Wan and
+    128K-causal Ulysses ranks (one chunk over the whole sequence). The saved
+    O and LSE come from this library's own forward. FLOP convention: 2.5x the
+    forward's (five D-long products per visible pair: S, dP, dV, dK, dQ); the
+    kernels recompute S and dP in both passes, so they execute 7/5 of that."""
+    out = {}
+    f32 = torch.float32
+    n, H, D = q0.shape[1], wf.H, wf.D
+    o, lse = cp.ring_attention(q0, vis)
+    do = synthetic.make_tensor(tuple(q0.shape), torch.bfloat16, 1077).to(dev)
+    delta = cp.attn_backward_delta(o, do)
+    dq = torch.empty((1, n, H, D), dtype=f32, device=dev)
+    grads = [(torch.empty(k.shape, dtype=f32, device=dev), torch.empty(k.shape, dtype=f32,
+                                                                     device=dev))
+             for k, _, _ in vis]
+
+    def ring_step():
+        cp.attn_backward_delta(o, do, delta)
+        for c, (k, v, p) in enumerate(vis):
+            cp.attn_chunk_backward(q0, k, v, do, lse, delta, dq, grads[c][0], grads[c][1],
+                                   q_pos0=0, kv_pos0=p, accumulate_dq=c > 0)
+
+    flops = 2.5 * attn_flops(n, wf.S, H, D, False)
+    d = time_launches(torch, ring_step, 3, 20)
+    out["flux_ring_rank0_backward"] = {
+        "us": median(d) * 1e3, "tflops": flops / (median(d) * 1e-3) / 1e12,
+        "mfma_frac": flops / (median(d) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "gflop": flops / 1e9,
+        "launches": 1 + 2 * len(vis)}
+    log(f"flux ring rank0 backward: {median(d) * 1e3:.0f} us, "
+        f"{out['flux_ring_rank0_backward']['tflops']:.0f} TFLOP/s")
+    del o, lse, do, delta, dq, grads
+    for w in (synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
+        S, Hl = w.S, w.H_local
+        q, k, v, do = (synthetic.make_tensor((1, S, Hl, D), torch.bfloat16, 1100 + t).to(dev)
+                       for t in range(4))
+        o, lse = cp.attn_chunk_partial(q, k, v, causal=w.causal, out_dtype=torch.bfloat16)
+        delta = cp.attn_backward_delta(o, do)
+        g = [torch.empty((1, S, Hl, D), dtype=f32, device=dev) for _ in range(3)]
+        step = lambda: (cp.attn_backward_delta(o, do, delta),
+                        cp.attn_chunk_backward(q, k, v, do, lse, delta, *g, causal=w.causal))
+        flops = 2.5 * 4.0 * D * Hl * (causal_pairs_square(S) if w.causal else S * S)
+        d = time_launches(torch, step, 1, 3 if w.causal else 5)
+        out[w.name + "_backward"] = {
+            "us": median(d) * 1e3, "tflops": flops / (median(d) * 1e-3) / 1e12,
+            "mfma_frac": flops / (median(d) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "gflop": flops / 1e9, "causal": w.causal}
+        log(f"{w.name} backward: {median(d) * 1e3:.0f} us, "
+            f"{out[w.name + '_backward']['tflops']:.0f} TFLOP/s")
+        del q, k, v, do, o, lse, delta, g
+        torch.cuda.empty_cache()
     return out
 
 
