@@ -92,27 +92,36 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // Per-lane geometry of one streamed tile: direct-load sources and fragment
 // read offsets (bytes within the tile).
-template <int D>
+template <int D, int NT = kThreads>
 struct TileGeo {
-  static constexpr int NL = Geo<D>::kLoadsPerWave;
-  int src_row[NL];     // tile row each direct load fetches
-  uint32_t src[NL];    // its byte offset from the tile's first row (row stride rs)
-  uint32_t n_rd[D / 16];                 // normal fragment: LDS row = lane%32, unit 2ks + half
-  uint32_t t_lo[D / 32], t_hi[D / 32];   // transposed fragment, k-step 0 (add 16 t rows)
+  static constexpr int NL = kTile * Geo<D>::kUPR / NT;  // direct loads per tile per wave
+  // Row r0 + 8 of a transposed read flips swizzle bit 3 of the unit when the
+  // swizzle spans 16 rows (D = 128), not when it spans 8 (D = 64).
+  static constexpr uint32_t kHiX = Geo<D>::kMask >= 8 ? (8u << 4) : 0u;
+  uint32_t src[NL];      // byte offset of each direct load's source from the tile's first row
+  uint32_t n_rd0;        // normal fragment, k-step 0: LDS row = lane%32, unit half
+  uint32_t t_lo[D / 32]; // transposed fragment, k-step 0, rows r0 .. r0+3 (add 16 t rows)
+  int w8, lane;
 
-  __device__ void init(int wave, int lane, int rs) {
+  // Tile row fetched by direct load n of this lane.
+  __device__ int src_row(int n) const {
+    const int s = (w8 * NL + n) * 64 + lane;
+    return swap_bits23(s / Geo<D>::kUPR);
+  }
+
+  __device__ void init(int wave, int ln, int rs) {
     constexpr int UPR = Geo<D>::kUPR;
+    w8 = wave;
+    lane = ln;
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
       // LDS slot s = (row, unit) holds tile row swap(row), unit s%UPR ^ (row & mask)
       const int s = (wave * NL + n) * 64 + lane;
       const int row = s / UPR, pu = s % UPR;
-      src_row[n] = swap_bits23(row);
-      src[n] = 2u * static_cast<uint32_t>(src_row[n] * rs + (pu ^ (row & Geo<D>::kMask)) * 8);
+      src[n] = 2u * static_cast<uint32_t>(swap_bits23(row) * rs + (pu ^ (row & Geo<D>::kMask)) * 8);
     }
     const int col = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) n_rd[ks] = unit_off<D>(col, 2 * ks + half);
+    n_rd0 = unit_off<D>(col, half);
     // ds_read_b64_tr_b16: in each 16-lane group, lane i addresses row r0 + i/4,
     // elements el .. el+3, and receives element column (group's base) + i of
     // rows r0 .. r0+3. LDS rows 4h .. 4h+3 hold tile rows 8h .. 8h+3 and rows
@@ -124,7 +133,6 @@ struct TileGeo {
     for (int md = 0; md < D / 32; ++md) {
       const int el = 32 * md + 16 * (g16 & 1) + 4 * (j16 & 3);
       t_lo[md] = unit_off<D>(r0, el >> 3) + ((el & 4) ? 8 : 0);
-      t_hi[md] = unit_off<D>(r0 + 8, el >> 3) + ((el & 4) ? 8 : 0);
     }
   }
 
@@ -141,8 +149,8 @@ struct TileGeo {
     } else {
 #pragma unroll
       for (int n = 0; n < NL; ++n) {
-        const uint32_t fix =
-            src_row[n] < n_valid ? 0u : 2u * static_cast<uint32_t>((src_row[n] - n_valid + 1) * rs);
+        const int r = src_row(n);
+        const uint32_t fix = r < n_valid ? 0u : 2u * static_cast<uint32_t>((r - n_valid + 1) * rs);
         lds_load16(g + (src[n] - fix), l + n * 1024);
       }
     }
@@ -151,12 +159,15 @@ struct TileGeo {
   // A operand: tile^T rows d = 32 md + lane%32, k = tile rows 16 t + 8 half + 0..7
   __device__ bf16x8 tr_frag(const char* tile, int md, int t) const {
     const bf16x4 lo = read_tr(tile + t_lo[md] + 16 * t * Geo<D>::kRowBytes);
-    const bf16x4 hi = read_tr(tile + t_hi[md] + 16 * t * Geo<D>::kRowBytes);
+    const bf16x4 hi = read_tr(tile + (t_lo[md] ^ kHiX) + (16 * t + 8) * Geo<D>::kRowBytes);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // A operand: tile rows 32 mb + lane%32 (tile row swap of it), k = d 16 ks + 8 half + 0..7
+  // A operand: tile rows 32 mb + lane%32 (tile row swap of it), k = d 16 ks + 8 half + 0..7.
+  // Unit 2 ks + half: the swizzle XOR leaves the low unit bit to `half`, so the
+  // offset is n_rd0 with the unit's upper bits XORed by ks.
   __device__ bf16x8 frag(const char* tile, int mb, int ks) const {
-    return *reinterpret_cast<const bf16x8*>(tile + n_rd[ks] + mb * 32 * Geo<D>::kRowBytes);
+    return *reinterpret_cast<const bf16x8*>(tile + (n_rd0 ^ (ks << 5)) +
+                                            mb * 32 * Geo<D>::kRowBytes);
   }
 };
 
@@ -328,15 +339,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // -------------------------------------------------------------- dK/dV kernel
+// A block is 8 waves over 128 keys: wave w of group g holds keys 32 (w%4) ..
+// +31 and takes rows 32 g .. 32 g + 31 of every 64-row Q/dO tile, so the two
+// groups split each tile and the block's dK, dV are the sum of the groups'
+// partial accumulators (merged through LDS at the end, in a fixed order).
+// The block's K and V rows sit in LDS for the whole kernel and are read as B
+// operands, which keeps a wave within 256 registers (two waves per SIMD).
+constexpr int kKvThreads = 512;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int TB = Geo<D>::kTileBytes;
-  // stage s: Q tile at 2s*TB, dO tile at (2s+1)*TB; LSE and Delta rows of
-  // stage s at 4*TB + 512 s (64 floats each)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 1024];
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int TB = Geo<D>::kTileBytes;  // one 64-row tile
+  constexpr int RB = Geo<D>::kRowBytes;
+  // [K: 2 tiles][V: 2 tiles][stage 0: Q, dO][stage 1: Q, dO][stats: 2 x 512 B]
+  constexpr int KV_BYTES = 4 * TB, ST_OFF = 8 * TB;
+  __shared__ __attribute__((aligned(1024))) char smem[8 * TB + 1024];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave in block, 0..7
+  const int grp = w8 >> 2, wave = w8 & 3;                    // row half, key group
   const int col = lane & 31, half = lane >> 5;
   const int BH = a.B * a.H;
   const int nkt = (a.Skv + kBlk - 1) / kBlk;
@@ -352,44 +373,73 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const int b = bh / a.H, h = bh - b * a.H;
   const int jk = kt * kBlk + wave * 32 + col;  // this lane's key
-  const bool valid = jk < a.Skv;
-  const int jc = valid ? jk : a.Skv - 1;
   const int k_first = kt * kBlk, k_last = min(k_first + kBlk - 1, a.Skv - 1);
   const int rs = a.H * D;
+  // exp2 factor with the scale's sign (no row maximum is needed here)
+  const float sl2 = a.scale * kLog2e;
 
-  // resident B operands: K^T (sign of the scale folded in) and V^T
-  bf16x8 kf[D / 16], vf[D / 16];
-  const int64_t krow = (static_cast<int64_t>(b) * a.Skv + jc) * a.H + h;
-  load_row_frags<D>(a.k + krow * D, valid, a.scale < 0.f ? 0x80008000u : 0u, half, kf);
-  load_row_frags<D>(a.v + krow * D, valid, 0u, half, vf);
-  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
-
-  // query tiles that can see this block's keys
-  int qt0 = 0;
+  int qt0 = 0;  // first query tile that can see this block's keys
   if (CAUSAL) {
-    const int qmin = k_first - a.diag;  // first query that sees key k_first
+    const int qmin = k_first - a.diag;
     qt0 = qmin <= 0 ? 0 : qmin / kTile;
   }
   const int nqt = (a.Sq + kTile - 1) / kTile;
   const int ntiles = max(0, nqt - qt0);
 
-  TileGeo<D> g;
-  g.init(wave, lane, rs);
-  const char* qbase = reinterpret_cast<const char*>(a.q + (static_cast<int64_t>(b) * a.Sq * a.H + h) * D);
-  const char* dbase = reinterpret_cast<const char*>(a.dout + (static_cast<int64_t>(b) * a.Sq * a.H + h) * D);
+  TileGeo<D, kKvThreads> g;
+  g.init(w8, lane, rs);
+  const int64_t head = (static_cast<int64_t>(b) * a.Sq * a.H + h) * D;
+  const char* qbase = reinterpret_cast<const char*>(a.q + head);
+  const char* dbase = reinterpret_cast<const char*>(a.dout + head);
   const int64_t lbase = (static_cast<int64_t>(b) * a.H + h) * a.Sq;
-  auto issue = [&](int st, int q0) {
-    char* dst = smem + 2 * st * TB;
-    g.issue(qbase, q0, a.Sq, rs, dst, wave);
-    g.issue(dbase, q0, a.Sq, rs, dst + TB, wave);
-    if (wave == 0) {  // 64 LSE and 64 Delta values, one per lane (clamped to the last row)
-      const int64_t r = lbase + min(q0 + lane, a.Sq - 1);
-      float* ls = reinterpret_cast<float*>(smem + 4 * TB + 512 * st);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.lse + r),
-                                       reinterpret_cast<void*>(ls), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.delta + r),
-                                       reinterpret_cast<void*>(ls + 64), 4, 0, 0);
+
+  // the block's K and V: two 64-row tiles each, same row-swapped layout
+  {
+    const int64_t kvh = (static_cast<int64_t>(b) * a.Skv * a.H + h) * D;
+    const char* kb = reinterpret_cast<const char*>(a.k + kvh);
+    const char* vb = reinterpret_cast<const char*>(a.v + kvh);
+    g.issue(kb, k_first, a.Skv, rs, smem, w8);
+    g.issue(vb, k_first, a.Skv, rs, smem + 2 * TB, w8);
+    if (k_first + kTile < a.Skv) {
+      g.issue(kb, k_first + kTile, a.Skv, rs, smem + TB, w8);
+      g.issue(vb, k_first + kTile, a.Skv, rs, smem + 3 * TB, w8);
     }
+  }
+  // B-operand reads of this wave's keys: block row 32 wave + col sits in tile
+  // wave/2 at LDS row swap(32 (wave%2) + col)
+  uint32_t kv_rd0;
+  {
+    const int local = 32 * (wave & 1) + col;
+    kv_rd0 = (wave >> 1) * TB + unit_off<D>(swap_bits23(local), half);
+  }
+  // unit 2 ks + half of the same row: the swizzle XOR leaves the low unit bit
+  // to `half`, so the offset of k-step ks is kv_rd0 ^ (ks << 5)
+  auto kv_frag = [&](const char* base, int ks) {
+    return *reinterpret_cast<const bf16x8*>(base + (kv_rd0 ^ (ks << 5)));
+  };
+
+  // Row statistics of a tile, staged by wave 0 through registers (see the
+  // forward-statistics note in the file header): rows past Sq and rows whose
+  // LSE is -inf get -inf, so their weights are exactly 0 with no masking.
+  float st_l = -INFINITY, st_d = 0.f;
+  auto fetch_stats = [&](int q0) {
+    const int r = q0 + lane;
+    st_l = -INFINITY;
+    st_d = 0.f;
+    if (r < a.Sq) {
+      st_l = a.lse[lbase + r];
+      st_d = a.delta[lbase + r];
+    }
+  };
+  auto commit_stats = [&](int st) {
+    float* ls = reinterpret_cast<float*>(smem + ST_OFF + 512 * st);
+    ls[lane] = neg_lse2(st_l);
+    ls[64 + lane] = st_d;
+  };
+  auto issue = [&](int st, int q0) {
+    char* dst = smem + KV_BYTES + 2 * st * TB;
+    g.issue(qbase, q0, a.Sq, rs, dst, w8);
+    g.issue(dbase, q0, a.Sq, rs, dst + TB, w8);
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -399,68 +449,103 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[md] = f32x16{};
   }
 
-  if (ntiles > 0) issue(0, qt0 * kTile);
+  if (ntiles > 0) {
+    issue(0, qt0 * kTile);
+    if (w8 == 0) {
+      fetch_stats(qt0 * kTile);
+      commit_stats(0);
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const char* kl = smem;
+  const char* vl = smem + 2 * TB;
   for (int j = 0; j < ntiles; ++j) {
     const int st = j & 1;
-    const char* ql = smem + 2 * st * TB;
+    const char* ql = smem + KV_BYTES + 2 * st * TB;
     const char* dl = ql + TB;
-    const float* ls = reinterpret_cast<const float*>(smem + 4 * TB + 512 * st);
+    const float* ls = reinterpret_cast<const float*>(smem + ST_OFF + 512 * st);
     const float* dt = ls + 64;
-    if (j + 1 < ntiles) issue(st ^ 1, (qt0 + j + 1) * kTile);
-    const int q0 = (qt0 + j) * kTile;
-    const bool masked = q0 + kTile > a.Sq || (CAUSAL && q0 + a.diag < k_last);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      // S and dP for 32 query rows; register r is tile row 32 mb + 16 (r/8) + 8 half + r%8
-      f32x16 s = mfma(g.frag(ql, mb, 0), kf[0], f32x16{});
-      f32x16 dp = mfma(g.frag(dl, mb, 0), vf[0], f32x16{});
-#pragma unroll
-      for (int ks = 1; ks < D / 16; ++ks) {
-        s = mfma(g.frag(ql, mb, ks), kf[ks], s);
-        dp = mfma(g.frag(dl, mb, ks), vf[ks], dp);
-      }
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = q0 + 32 * mb + 16 * (r >> 3) + 8 * half + (r & 7);
-          if (qi >= a.Sq || (CAUSAL && jk > qi + a.diag)) s[r] = -INFINITY;
-        }
-      }
-      bf16x8 pf[2], sf[2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int row = 32 * mb + 16 * t2 + 8 * half;
-        const float4 l0 = *reinterpret_cast<const float4*>(ls + row);
-        const float4 l1 = *reinterpret_cast<const float4*>(ls + row + 4);
-        const float4 d0 = *reinterpret_cast<const float4*>(dt + row);
-        const float4 d1 = *reinterpret_cast<const float4*>(dt + row + 4);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * t2 + e;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, neg_lse2(lv[e])));
-          pf[t2][e] = static_cast<__bf16>(p);
-          sf[t2][e] = static_cast<__bf16>(p * (dp[r] - dv8[e]));
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (k-steps 2 mb, 2 mb + 1)
-#pragma unroll
-      for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          dv[md] = mfma(g.tr_frag(dl, md, 2 * mb + t2), pf[t2], dv[md]);
-          dk[md] = mfma(g.tr_frag(ql, md, 2 * mb + t2), sf[t2], dk[md]);
-        }
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      issue(st ^ 1, (qt0 + j + 1) * kTile);
+      if (w8 == 0) fetch_stats((qt0 + j + 1) * kTile);
     }
+    const int q0 = (qt0 + j) * kTile;
+    // S and dP for this group's 32 rows; register r is tile row
+    // 32 grp + 16 (r/8) + 8 half + r%8
+    f32x16 s = mfma(g.frag(ql, grp, 0), kv_frag(kl, 0), f32x16{});
+    f32x16 dp = mfma(g.frag(dl, grp, 0), kv_frag(vl, 0), f32x16{});
+#pragma unroll
+    for (int ks = 1; ks < D / 16; ++ks) {
+      s = mfma(g.frag(ql, grp, ks), kv_frag(kl, ks), s);
+      dp = mfma(g.frag(dl, grp, ks), kv_frag(vl, ks), dp);
+    }
+    if (CAUSAL && q0 + a.diag < k_last) {  // some (row, key) pairs of the tile are masked
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + 32 * grp + 16 * (r >> 3) + 8 * half + (r & 7);
+        if (jk > qi + a.diag) s[r] = -INFINITY;
+      }
+    }
+    // P and dS (bf16): B operands of k-steps t = 2 grp + t2 (rows 16 t + 8 half + e)
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int row = 32 * grp + 16 * t2 + 8 * half;
+      const float4 l0 = *reinterpret_cast<const float4*>(ls + row);
+      const float4 l1 = *reinterpret_cast<const float4*>(ls + row + 4);
+      const float4 d0 = *reinterpret_cast<const float4*>(dt + row);
+      const float4 d1 = *reinterpret_cast<const float4*>(dt + row + 4);
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t2 + e;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, lv[e]));
+        pf[t2][e] = static_cast<__bf16>(p);
+        sf[t2][e] = static_cast<__bf16>(p * (dp[r] - dv8[e]));
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the group's 32 rows
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md) {
+        dv[md] = mfma(g.tr_frag(dl, md, 2 * grp + t2), pf[t2], dv[md]);
+        dk[md] = mfma(g.tr_frag(ql, md, 2 * grp + t2), sf[t2], dk[md]);
+      }
+    if (more && w8 == 0) commit_stats(st ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  (void)RB;
 
-  if (!valid) return;
+  // group 1 hands its partial dK, dV to group 0 through LDS (every wave is
+  // past its last tile read: the loop ends with a barrier)
+  float* xk = reinterpret_cast<float*>(smem);  // [wave][md][r][lane], dK then dV
+  constexpr int PER_WAVE = 2 * (D / 32) * 16 * 64;
+  if (grp == 1) {
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        xk[wave * PER_WAVE + (md * 16 + r) * 64 + lane] = dk[md][r];
+        xk[wave * PER_WAVE + ((D / 32 + md) * 16 + r) * 64 + lane] = dv[md][r];
+      }
+  }
+  __syncthreads();
+  if (grp == 1 || jk >= a.Skv) return;
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[md][r] += xk[wave * PER_WAVE + (md * 16 + r) * 64 + lane];
+      dv[md][r] += xk[wave * PER_WAVE + ((D / 32 + md) * 16 + r) * 64 + lane];
+    }
   // register r of block md is element d = 32 md + 8 (r/4) + 4 half + r%4 of key jk
+  const int64_t krow = (static_cast<int64_t>(b) * a.Skv + jk) * a.H + h;
   float* ok = a.dk + krow * D;
   float* ov = a.dv + krow * D;
   const bool acc = a.accum_dkv != 0;
@@ -527,7 +612,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t kv_blocks = CAUSAL ? nkt * BH : (nkt * BH + 7) / 8 * 8;
   if (kv_blocks > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(static_cast<uint32_t>(kv_blocks)),
-                       dim3(kThreads), 0, stream, a);
+                       dim3(kKvThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
