@@ -262,8 +262,8 @@ def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
 
 def backward_workloads(torch, cp, synthetic, dev, q0, vis, wf):
     """Attention backward: the FLUX ring rank's share (Delta, then one
-    cp_attn_chunk_backward per chunk in ring order: dQ accumulated over the
-    chunks, each chunk's dK/dV share written for its owner) and the Wan and
+    cp_ring_attention_backward call: dQ over the 4 chunks, each chunk's dK/dV
+    share written for its owner) and the Wan and
     128K-causal Ulysses ranks (one chunk over the whole sequence). The saved
     O and LSE come from this library's own forward. FLOP convention: 2.5x the
     forward's (five D-long products per visible pair: S, dP, dV, dK, dQ); the
@@ -281,16 +281,14 @@ def backward_workloads(torch, cp, synthetic, dev, q0, vis, wf):
 
     def ring_step():
         cp.attn_backward_delta(o, do, delta)
-        for c, (k, v, p) in enumerate(vis):
-            cp.attn_chunk_backward(q0, k, v, do, lse, delta, dq, grads[c][0], grads[c][1],
-                                   q_pos0=0, kv_pos0=p, accumulate_dq=c > 0)
+        cp.ring_attention_backward(q0, vis, do, lse, delta, dq, grads)
 
     flops = 2.5 * attn_flops(n, wf.S, H, D, False)
     d = time_launches(torch, ring_step, 3, 20)
     out["flux_ring_rank0_backward"] = {
         "us": median(d) * 1e3, "tflops": flops / (median(d) * 1e-3) / 1e12,
         "mfma_frac": flops / (median(d) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "gflop": flops / 1e9,
-        "launches": 1 + 2 * len(vis)}
+        "launches": 3}
     log(f"flux ring rank0 backward: {median(d) * 1e3:.0f} us, "
         f"{out['flux_ring_rank0_backward']['tflops']:.0f} TFLOP/s")
     del o, lse, do, delta, dq, grads

@@ -16,6 +16,9 @@ Entry points (same names as the C ABI, without the ``cp_`` prefix):
   kv_gather            the K/V all-gather's unpack (sequence shards joined)
   attn_backward_delta  Delta_i = <dO_i, O_i>, the backward's per-row statistic
   attn_chunk_backward  one K/V chunk's share of dQ, dK, dV from the saved LSE
+  ring_attention_backward
+                       one ring rank's backward: dQ over all its chunks, each
+                       chunk's dK/dV share
 """
 from __future__ import annotations
 
@@ -49,6 +52,10 @@ class KVChunk(ctypes.Structure):
     _fields_ = [("k", _vp), ("v", _vp), ("len", _i64), ("pos0", _i64)]
 
 
+class KVGrad(ctypes.Structure):
+    _fields_ = [("dk", _vp), ("dv", _vp)]
+
+
 def _sig(name, args, res=ctypes.c_int):
     f = getattr(_lib, name)
     f.argtypes = args
@@ -72,6 +79,9 @@ _kv_gather = _sig("cp_kv_gather", [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, 
 _bwd_delta = _sig("cp_attn_backward_delta", [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp])
 _chunk_bwd = _sig("cp_attn_chunk_backward", [_vp] * 9 + [_i64] * 5 +
                   [_int, _f32, _int, _i64, _i64, _int, _vp])
+_ring_bwd = _sig("cp_ring_attention_backward",
+                 [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(KVGrad),
+                  _i64, _i64, _i64, _i64, _int, _f32, _int, _i64, _int, _vp])
 _last_error = _sig("cp_last_error", [], ctypes.c_char_p)
 _abi_version = _sig("cp_abi_version", [])
 
@@ -336,8 +346,56 @@ def attn_chunk_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout:
     return dq, dk, dv
 
 
+def ring_attention_backward(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
+                            dout: torch.Tensor, lse: torch.Tensor, delta: torch.Tensor,
+                            dq: Optional[torch.Tensor] = None,
+                            grads: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor]]] = None,
+                            *, scale: Optional[float] = None, causal: bool = False,
+                            q_pos0: int = 0, accumulate_dq: bool = False,
+                            accumulate_dkv: bool = False, stream=None):
+    """One ring rank's backward over ``chunks = [(k_c, v_c, pos0_c), ...]``; see
+    cp_ring_attention_backward. Returns ``(dq, [(dk_c, dv_c), ...])`` in fp32."""
+    B, Sq, H, D = _bshd(q, "q")
+    if tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout must have q's shape")
+    if tuple(lse.shape) != (B, H, Sq) or tuple(delta.shape) != (B, H, Sq):
+        raise ValueError("lse and delta must be [B][H][Sq]")
+    if (accumulate_dq and dq is None) or (accumulate_dkv and grads is None):
+        raise ValueError("accumulating needs the running-sum buffers")
+    f32 = torch.float32
+    if dq is None:
+        dq = torch.empty((B, Sq, H, D), dtype=f32, device=q.device)
+    if grads is None:
+        grads = [(torch.empty(k.shape, dtype=f32, device=q.device),
+                  torch.empty(k.shape, dtype=f32, device=q.device)) for k, _, _ in chunks]
+    if len(grads) != len(chunks):
+        raise ValueError("one (dk, dv) pair per chunk")
+    n = max(1, len(chunks))
+    arr, garr = (KVChunk * n)(), (KVGrad * n)()
+    for c, ((k, v, pos0), (dk, dv)) in enumerate(zip(chunks, grads)):
+        Bk, L, Hk, Dk = _bshd(k, "k")
+        if (Bk, Hk, Dk) != (B, H, D) or tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"chunk {c} shape disagrees with q")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise TypeError(f"chunk {c} dtype disagrees with q")
+        for name, t in (("dk", dk), ("dv", dv)):
+            if t.dtype != f32 or tuple(t.shape) != tuple(k.shape):
+                raise ValueError(f"chunk {c} {name} must be float32 of shape {tuple(k.shape)}")
+        arr[c] = KVChunk(_ptr(k), _ptr(v), L, int(pos0))
+        garr[c] = KVGrad(_ptr(dk), _ptr(dv))
+    if dq.dtype != f32 or tuple(dq.shape) != (B, Sq, H, D):
+        raise ValueError("dq must be float32 of q's shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    flags = (BWD_ACCUMULATE_DQ if accumulate_dq else 0) | \
+        (BWD_ACCUMULATE_DKV if accumulate_dkv else 0)
+    _check("cp_ring_attention_backward", _ring_bwd(
+        _ptr(q), arr, len(chunks), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), garr, B, H, Sq,
+        D, _dtype_code(q.dtype), scale, int(causal), q_pos0, flags, _stream(stream)))
+    return dq, list(grads)
+
+
 __all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
            "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
            "ulysses_anything_head2seq", "kv_gather", "attn_backward_delta",
-           "attn_chunk_backward", "BWD_ACCUMULATE_DQ", "BWD_ACCUMULATE_DKV", "last_error", "abi_version", "CpAttnError",
+           "attn_chunk_backward", "ring_attention_backward", "KVGrad", "BWD_ACCUMULATE_DQ", "BWD_ACCUMULATE_DKV", "last_error", "abi_version", "CpAttnError",
            "KVChunk", "LIB_PATH"]

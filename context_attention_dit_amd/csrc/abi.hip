@@ -448,22 +448,133 @@ cp_status cp_attn_chunk_backward(const void* q, const void* k, const void* v, co
   }
   cpattn::BwdArgs a{};
   a.q = static_cast<const __bf16*>(q);
-  a.k = static_cast<const __bf16*>(k);
-  a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
   a.lse = lse;
   a.delta = delta;
   a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
   a.B = static_cast<int32_t>(B);
   a.H = static_cast<int32_t>(H);
   a.Sq = static_cast<int32_t>(Sq);
-  a.Skv = static_cast<int32_t>(Skv);
   a.scale = scale;
-  a.diag = clamp_delta(q_pos0, kv_pos0, Sq, Skv);
   a.accum_dq = (flags & CP_BWD_ACCUMULATE_DQ) ? 1 : 0;
   a.accum_dkv = (flags & CP_BWD_ACCUMULATE_DKV) ? 1 : 0;
+  a.nchunks = 1;
+  cpattn::BwdChunk& c = a.chunks[0];
+  c.k = static_cast<const __bf16*>(k);
+  c.v = static_cast<const __bf16*>(v);
+  c.dk = dk;
+  c.dv = dv;
+  c.len = static_cast<int32_t>(Skv);
+  c.diag = clamp_delta(q_pos0, kv_pos0, Sq, Skv);
+  c.tile0 = 0;
+  a.total_kt = static_cast<int32_t>((Skv + 127) / 128);
+  a.groups = cpattn::bwd_dq_groups(B, H, Sq, (Skv + 63) / 64);
+  return hip_status(cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+cp_status cp_ring_attention_backward(const void* q, const cp_kv_chunk* chunks, int64_t P,
+                                     const void* dout, const float* lse, const float* delta,
+                                     float* dq, const cp_kv_grad* grads, int64_t B, int64_t H,
+                                     int64_t Sq, int64_t D, cp_dtype in_dtype, float scale,
+                                     int causal, int64_t q_pos0, int flags, void* stream) {
+  const char* fn = "cp_ring_attention_backward";
+  cp_status s = check_attn_common(fn, B, H, Sq, D, in_dtype, causal, scale);
+  if (s != CP_OK) return s;
+  if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
+  if (P > CP_MAX_RING_CHUNKS)
+    return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d chunks", fn, (long long)P,
+                CP_MAX_RING_CHUNKS);
+  if (!chunks || !grads) return fail(CP_E_INVALID, "%s: null chunk or gradient array", fn);
+  if (flags & ~(CP_BWD_ACCUMULATE_DQ | CP_BWD_ACCUMULATE_DKV))
+    return fail(CP_E_INVALID, "%s: unknown flag bits 0x%x", fn, flags);
+  if (in_dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "%s: only bf16 inputs are built", fn);
+  int64_t total_kt = 0, total_keys = 0;
+  for (int64_t c = 0; c < P; ++c) {
+    const int64_t len = chunks[c].len;
+    if (len < 0) return fail(CP_E_INVALID, "%s: chunk %lld has negative length", fn, (long long)c);
+    if (len >= kMaxSeq)
+      return fail(CP_E_UNSUPPORTED, "%s: chunk %lld length exceeds 2^30", fn, (long long)c);
+    total_kt += (len + 127) / 128;
+    total_keys += len;
+  }
+  if (sat_mul({total_kt, B, H}) > kMaxGrid / 8)
+    return fail(CP_E_UNSUPPORTED, "%s: B*H*keys too large for one launch", fn);
+  if (B == 0 || H == 0 || (Sq == 0 && total_keys == 0)) return ok();
+  const int64_t q_bytes = sat_mul({B, Sq, H, D, 2}), dq_bytes = sat_mul({B, Sq, H, D, 4});
+  const int64_t l_bytes = sat_mul({B, H, Sq, 4});
+  const bool has_q = Sq > 0;
+  if (has_q && (!q || !dout || !lse || !delta || !dq))
+    return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if (has_q && (!aligned(q, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4) ||
+                !aligned(delta, 4)))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse/delta 4 B)", fn);
+  // every output against every input and every other output
+  struct Range {
+    const void* p;
+    int64_t n;
+  };
+  Range ins[4 + 2 * CP_MAX_RING_CHUNKS], outs[1 + 2 * CP_MAX_RING_CHUNKS];
+  int n_in = 0, n_out = 0;
+  if (has_q) {
+    ins[n_in++] = {q, q_bytes};
+    ins[n_in++] = {dout, q_bytes};
+    ins[n_in++] = {lse, l_bytes};
+    ins[n_in++] = {delta, l_bytes};
+    outs[n_out++] = {dq, dq_bytes};
+  }
+  for (int64_t c = 0; c < P; ++c) {
+    const int64_t len = chunks[c].len;
+    if (len == 0) continue;
+    const int64_t kv_bytes = sat_mul({B, len, H, D, 2}), g_bytes = sat_mul({B, len, H, D, 4});
+    if (!chunks[c].k || !chunks[c].v || !grads[c].dk || !grads[c].dv)
+      return fail(CP_E_INVALID, "%s: chunk %lld has a null pointer", fn, (long long)c);
+    if (!aligned(chunks[c].k, 16) || !aligned(chunks[c].v, 16) || !aligned(grads[c].dk, 16) ||
+        !aligned(grads[c].dv, 16))
+      return fail(CP_E_INVALID, "%s: chunk %lld pointer misaligned (16 B)", fn, (long long)c);
+    ins[n_in++] = {chunks[c].k, kv_bytes};
+    ins[n_in++] = {chunks[c].v, kv_bytes};
+    outs[n_out++] = {grads[c].dk, g_bytes};
+    outs[n_out++] = {grads[c].dv, g_bytes};
+  }
+  for (int x = 0; x < n_out; ++x) {
+    for (int y = 0; y < n_in; ++y)
+      if (overlap(outs[x].p, outs[x].n, ins[y].p, ins[y].n))
+        return fail(CP_E_INVALID, "%s: an output overlaps an input", fn);
+    for (int y = x + 1; y < n_out; ++y)
+      if (overlap(outs[x].p, outs[x].n, outs[y].p, outs[y].n))
+        return fail(CP_E_INVALID, "%s: output buffers overlap each other", fn);
+  }
+  cpattn::BwdArgs a{};
+  a.q = static_cast<const __bf16*>(q);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.B = static_cast<int32_t>(B);
+  a.H = static_cast<int32_t>(H);
+  a.Sq = static_cast<int32_t>(Sq);
+  a.scale = scale;
+  a.accum_dq = (flags & CP_BWD_ACCUMULATE_DQ) ? 1 : 0;
+  a.accum_dkv = (flags & CP_BWD_ACCUMULATE_DKV) ? 1 : 0;
+  a.nchunks = static_cast<int32_t>(P);
+  int32_t tile0 = 0;
+  int64_t key_tiles = 0;
+  for (int64_t c = 0; c < P; ++c) {
+    cpattn::BwdChunk& d = a.chunks[c];
+    d.k = static_cast<const __bf16*>(chunks[c].k);
+    d.v = static_cast<const __bf16*>(chunks[c].v);
+    d.dk = grads[c].dk;
+    d.dv = grads[c].dv;
+    d.len = static_cast<int32_t>(chunks[c].len);
+    d.diag = clamp_delta(q_pos0, chunks[c].pos0, Sq, chunks[c].len);
+    d.tile0 = tile0;
+    tile0 += static_cast<int32_t>((chunks[c].len + 127) / 128);
+    key_tiles += (chunks[c].len + 63) / 64;
+  }
+  a.total_kt = tile0;
+  a.groups = cpattn::bwd_dq_groups(B, H, Sq, key_tiles);
   return hip_status(cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0,
                                                  static_cast<hipStream_t>(stream)),
                     fn);

@@ -515,6 +515,17 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
                        : launch_g<D, CAUSAL, OUT_BF16, 1>(a, stream);
 }
 
+
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream) {
+  if (causal)
+    return out_bf16 ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
+  return out_bf16 ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
+}
+
+}  // namespace
+
 int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -528,15 +539,6 @@ int device_cus() {
   }
   return cached[dev];
 }
-
-template <int D>
-hipError_t launch_d(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream) {
-  if (causal)
-    return out_bf16 ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
-  return out_bf16 ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
-}
-
-}  // namespace
 
 // Blocks of 128 query rows, two resident per CU. A grid of at most one query
 // tile per CU runs two-group blocks: eight waves per tile, its keys split

@@ -192,6 +192,17 @@ __device__ __forceinline__ float neg_lse2(float lse) {
   return lse == -INFINITY ? -INFINITY : -lse * kLog2e;
 }
 
+// exp2 factor scale * log2(e), kept away from 0 so that a masked score times
+// it is never inf * 0.
+__device__ __forceinline__ float signed_sl2(float scale) {
+  return copysignf(fmaxf(fabsf(scale) * kLog2e, 1e-30f), scale);
+}
+// The score a masked (row, key) pair is given: its product with signed_sl2 is
+// -inf, so its weight exp2(...) is exactly 0.
+__device__ __forceinline__ float masked_score(float scale) {
+  return scale < 0.f ? INFINITY : -INFINITY;
+}
+
 // Store 4 consecutive fp32 values scaled by `s`, adding the old values if `acc`.
 __device__ __forceinline__ void store4(float* p, float s, float x0, float x1, float x2, float x3,
                                       bool acc) {
@@ -216,15 +227,22 @@ __device__ __forceinline__ int xcd_item(int nitems) {
 }
 
 // ---------------------------------------------------------------- dQ kernel
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+// G = 1: a block is 4 waves over 128 query rows, visiting every key tile of
+// every chunk in order. G = 2: two such groups of 4 waves share the query
+// rows, group g taking half g of the key tiles with its own LDS stages; their
+// dQ accumulators are added through LDS at the end (grids with no more query
+// tiles than compute units).
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(kThreads * G, G == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int TB = Geo<D>::kTileBytes;
-  constexpr int RB = Geo<D>::kRowBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // stage s: K at 2s, V at 2s+1
+  // per group: stage s holds K at 2s, V at 2s + 1
+  __shared__ __attribute__((aligned(1024))) char smem[G * 4 * TB];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = G == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
   const int col = lane & 31, half = lane >> 5;
+  char* const gsm = smem + (G == 1 ? 0 : grp * 4 * TB);
   const int BH = a.B * a.H;
   const int nqt = (a.Sq + kBlk - 1) / kBlk;
   int bh, qt;
@@ -244,89 +262,150 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q_first = qt * kBlk, q_last = min(q_first + kBlk - 1, a.Sq - 1);
   const int rs = a.H * D;
 
-  // resident B operands: Q^T (sign of the scale folded in) and dO^T
+  // resident B operands: Q^T and dO^T
   bf16x8 qf[D / 16], df[D / 16];
   const int64_t qrow = (static_cast<int64_t>(b) * a.Sq + ic) * a.H + h;
-  load_row_frags<D>(a.q + qrow * D, valid, a.scale < 0.f ? 0x80008000u : 0u, half, qf);
+  load_row_frags<D>(a.q + qrow * D, valid, 0u, half, qf);
   load_row_frags<D>(a.dout + qrow * D, valid, 0u, half, df);
   const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + ic;
   const float nl = valid ? neg_lse2(a.lse[lrow]) : -INFINITY;
   const float dlt = valid ? a.delta[lrow] : 0.f;
-  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  const float sl2 = signed_sl2(a.scale);  // no row maximum is needed here
+  const float s_mask = masked_score(a.scale);
 
-  int nkeys = a.Skv;
-  if (CAUSAL) nkeys = max(0, min(nkeys, q_last + a.diag + 1));
-  const int ntiles = (nkeys + kTile - 1) / kTile;
+  // Chunk descriptors are read with a provably uniform index (scalar loads).
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto keys_of = [&](int c) {  // keys of chunk c this query tile can see
+    c = uni(c);
+    int n = a.chunks[c].len;
+    if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].diag + 1));
+    return n;
+  };
+  struct Cur {
+    int c, kt;
+  };
+  auto next_of = [&](Cur x) {
+    x.c = uni(x.c);
+    x.kt = uni(x.kt) + 1;
+    if (x.kt * kTile >= keys_of(x.c)) {
+      x.kt = 0;
+      ++x.c;
+      while (x.c < a.nchunks && keys_of(x.c) == 0) ++x.c;
+    }
+    return x;
+  };
 
   TileGeo<D> g;
   g.init(wave, lane, rs);
-  const char* kbase = reinterpret_cast<const char*>(a.k + (static_cast<int64_t>(b) * a.Skv * a.H + h) * D);
-  const char* vbase = reinterpret_cast<const char*>(a.v + (static_cast<int64_t>(b) * a.Skv * a.H + h) * D);
+  auto issue = [&](char* dst, Cur x) {
+    const int c = uni(x.c), key0 = uni(x.kt) * kTile;
+    const BwdChunk& ch = a.chunks[c];
+    const int64_t off = (static_cast<int64_t>(b) * ch.len * a.H + h) * D;
+    g.issue(reinterpret_cast<const char*>(ch.k + off), key0, ch.len, rs, dst, wave);
+    g.issue(reinterpret_cast<const char*>(ch.v + off), key0, ch.len, rs, dst + TB, wave);
+  };
+
+  // this group's share of the tiles, in chunk order
+  Cur cur{0, 0};
+  int left, steps;
+  {
+    int total = 0;
+    for (int c = 0; c < a.nchunks; ++c) total += (keys_of(c) + kTile - 1) / kTile;
+    const int t_begin = G == 2 ? (grp == 0 ? 0 : total / 2) : 0;
+    const int t_end = G == 2 ? (grp == 0 ? total / 2 : total) : total;
+    left = uni(t_end - t_begin);
+    steps = uni(G == 2 ? total - total / 2 : total);  // both groups join every barrier
+    int skip = t_begin;
+    while (cur.c < a.nchunks) {
+      const int nt = (keys_of(cur.c) + kTile - 1) / kTile;
+      if (skip < nt) break;
+      skip -= nt;
+      ++cur.c;
+    }
+    cur.kt = skip;
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int md = 0; md < D / 32; ++md) acc[md] = f32x16{};
 
-  if (ntiles > 0) {
-    g.issue(kbase, 0, a.Skv, rs, smem, wave);
-    g.issue(vbase, 0, a.Skv, rs, smem + TB, wave);
-  }
+  if (left > 0) issue(gsm, cur);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int st = j & 1;
-    const char* kl = smem + 2 * st * TB;
-    const char* vl = kl + TB;
-    if (j + 1 < ntiles) {
-      char* nk = smem + 2 * (st ^ 1) * TB;
-      g.issue(kbase, (j + 1) * kTile, a.Skv, rs, nk, wave);
-      g.issue(vbase, (j + 1) * kTile, a.Skv, rs, nk + TB, wave);
-    }
-    const int key0 = j * kTile;
-    // S^T and dP^T for the tile's 64 keys (two 32-key blocks); register r of
-    // block mb is key key0 + 32 mb + 16 (r/8) + 8 half + r%8
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = mfma(g.frag(kl, mb, 0), qf[0], f32x16{});
-      dp[mb] = mfma(g.frag(vl, mb, 0), df[0], f32x16{});
-#pragma unroll
-      for (int ks = 1; ks < D / 16; ++ks) {
-        s[mb] = mfma(g.frag(kl, mb, ks), qf[ks], s[mb]);
-        dp[mb] = mfma(g.frag(vl, mb, ks), df[ks], dp[mb]);
+  for (int j = 0; j < steps; ++j) {
+    if (G == 1 || j < left) {  // (a group out of tiles still joins the barrier below)
+      const int st = j & 1;
+      const char* kl = gsm + 2 * st * TB;
+      const char* vl = kl + TB;
+      Cur nx = cur;
+      if (j + 1 < left) {
+        nx = next_of(cur);
+        issue(gsm + 2 * (st ^ 1) * TB, nx);
       }
-    }
-    const bool masked = key0 + kTile > a.Skv || (CAUSAL && key0 + kTile - 1 > q_first + a.diag);
-    if (masked) {
-      int lim = a.Skv - key0;
-      if (CAUSAL) lim = min(lim, i + a.diag - key0 + 1);
-      lim -= 8 * half;
+      const int c = uni(cur.c);
+      const int len = a.chunks[c].len, diag = a.chunks[c].diag;
+      const int key0 = uni(cur.kt) * kTile;
+      // S^T and dP^T for the tile's 64 keys (two 32-key blocks); register r
+      // of block mb is key key0 + 32 mb + 16 (r/8) + 8 half + r%8
+      f32x16 s[2], dp[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = mfma(g.frag(kl, mb, 0), qf[0], f32x16{});
+        dp[mb] = mfma(g.frag(vl, mb, 0), df[0], f32x16{});
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s[mb][r] = -INFINITY;
-    }
-    // dS^T, rounded to bf16: B operand of k-step t (keys 16 t + 8 half + e)
-    bf16x8 dsf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int mb = t >> 1, r = (t & 1) * 8 + e;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, nl));
-        dsf[t][e] = static_cast<__bf16>(p * (dp[mb][r] - dlt));
+        for (int ks = 1; ks < D / 16; ++ks) {
+          s[mb] = mfma(g.frag(kl, mb, ks), qf[ks], s[mb]);
+          dp[mb] = mfma(g.frag(vl, mb, ks), df[ks], dp[mb]);
+        }
       }
-    // dQ^T += K^T dS^T
+      const bool masked = key0 + kTile > len || (CAUSAL && key0 + kTile - 1 > q_first + diag);
+      if (masked) {
+        asm volatile("" ::: "memory");
+        int lim = len - key0;
+        if (CAUSAL) lim = min(lim, i + diag - key0 + 1);
+        lim -= 8 * half;
 #pragma unroll
-    for (int md = 0; md < D / 32; ++md)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[md] = mfma(g.tr_frag(kl, md, t), dsf[t], acc[md]);
+          for (int r = 0; r < 16; ++r)
+            if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s[mb][r] = s_mask;
+      }
+      // dS^T, rounded to bf16: B operand of k-step t (keys 16 t + 8 half + e)
+      bf16x8 dsf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int mb = t >> 1, r = (t & 1) * 8 + e;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, nl));
+          dsf[t][e] = static_cast<__bf16>(p * (dp[mb][r] - dlt));
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[md] = mfma(g.tr_frag(kl, md, t), dsf[t], acc[md]);
+      cur = nx;
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  (void)RB;
 
+  if (G == 2) {  // group 1 hands its dQ^T to group 0 (the loop ended with a barrier)
+    float* x = reinterpret_cast<float*>(smem);  // [wave][md][r][lane]
+    if (grp == 1) {
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[((wave * (D / 32) + md) * 16 + r) * 64 + lane] = acc[md][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[md][r] += x[((wave * (D / 32) + md) * 16 + r) * 64 + lane];
+  }
   if (!valid) return;
   // dQ^T register r of block md is element d = 32 md + 8 (r/4) + 4 half + r%4
   float* out = a.dq + qrow * D;
@@ -360,27 +439,35 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int grp = w8 >> 2, wave = w8 & 3;                    // row half, key group
   const int col = lane & 31, half = lane >> 5;
   const int BH = a.B * a.H;
-  const int nkt = (a.Skv + kBlk - 1) / kBlk;
-  int bh, kt;
-  if (CAUSAL) {  // the first key tiles are seen by the most queries: launch them first
-    kt = static_cast<int>(blockIdx.x) / BH;
+  const int nkt = a.total_kt;  // key tiles over all chunks
+  int bh, t;
+  if (CAUSAL) {  // in chunk order, the first key tiles are seen by the most queries
+    t = static_cast<int>(blockIdx.x) / BH;
     bh = static_cast<int>(blockIdx.x) % BH;
-  } else {
+  } else {  // the key tiles of one head (every chunk) stay on one XCD
     const int L = xcd_item(nkt * BH);
     if (L < 0) return;
     bh = L / nkt;
-    kt = L % nkt;
+    t = L % nkt;
   }
+  // chunk of key tile t (uniform scalar scan over at most 64 descriptors)
+  int c = 0;
+  while (c + 1 < a.nchunks && a.chunks[c + 1].tile0 <= t) ++c;
+  c = __builtin_amdgcn_readfirstlane(c);
+  const BwdChunk& ch = a.chunks[c];
+  const int len = ch.len, diag = ch.diag;
+  const int kt = t - ch.tile0;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int jk = kt * kBlk + wave * 32 + col;  // this lane's key
-  const int k_first = kt * kBlk, k_last = min(k_first + kBlk - 1, a.Skv - 1);
+  const int jk = kt * kBlk + wave * 32 + col;  // this lane's key within the chunk
+  const int k_first = kt * kBlk, k_last = min(k_first + kBlk - 1, len - 1);
   const int rs = a.H * D;
   // exp2 factor with the scale's sign (no row maximum is needed here)
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = signed_sl2(a.scale);
+  const float s_mask = masked_score(a.scale);
 
   int qt0 = 0;  // first query tile that can see this block's keys
   if (CAUSAL) {
-    const int qmin = k_first - a.diag;
+    const int qmin = k_first - diag;
     qt0 = qmin <= 0 ? 0 : qmin / kTile;
   }
   const int nqt = (a.Sq + kTile - 1) / kTile;
@@ -395,14 +482,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   // the block's K and V: two 64-row tiles each, same row-swapped layout
   {
-    const int64_t kvh = (static_cast<int64_t>(b) * a.Skv * a.H + h) * D;
-    const char* kb = reinterpret_cast<const char*>(a.k + kvh);
-    const char* vb = reinterpret_cast<const char*>(a.v + kvh);
-    g.issue(kb, k_first, a.Skv, rs, smem, w8);
-    g.issue(vb, k_first, a.Skv, rs, smem + 2 * TB, w8);
-    if (k_first + kTile < a.Skv) {
-      g.issue(kb, k_first + kTile, a.Skv, rs, smem + TB, w8);
-      g.issue(vb, k_first + kTile, a.Skv, rs, smem + 3 * TB, w8);
+    const int64_t kvh = (static_cast<int64_t>(b) * len * a.H + h) * D;
+    const char* kb = reinterpret_cast<const char*>(ch.k + kvh);
+    const char* vb = reinterpret_cast<const char*>(ch.v + kvh);
+    g.issue(kb, k_first, len, rs, smem, w8);
+    g.issue(vb, k_first, len, rs, smem + 2 * TB, w8);
+    if (k_first + kTile < len) {
+      g.issue(kb, k_first + kTile, len, rs, smem + TB, w8);
+      g.issue(vb, k_first + kTile, len, rs, smem + 3 * TB, w8);
     }
   }
   // B-operand reads of this wave's keys: block row 32 wave + col sits in tile
@@ -481,12 +568,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       s = mfma(g.frag(ql, grp, ks), kv_frag(kl, ks), s);
       dp = mfma(g.frag(dl, grp, ks), kv_frag(vl, ks), dp);
     }
-    if (CAUSAL && q0 + a.diag < k_last) {  // some (row, key) pairs of the tile are masked
+    if (CAUSAL && q0 + diag < k_last) {  // some (row, key) pairs of the tile are masked
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + 32 * grp + 16 * (r >> 3) + 8 * half + (r & 7);
-        if (jk > qi + a.diag) s[r] = -INFINITY;
+        if (jk > qi + diag) s[r] = s_mask;
       }
     }
     // P and dS (bf16): B operands of k-steps t = 2 grp + t2 (rows 16 t + 8 half + e)
@@ -536,7 +623,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
   }
   __syncthreads();
-  if (grp == 1 || jk >= a.Skv) return;
+  if (grp == 1 || jk >= len) return;
 #pragma unroll
   for (int md = 0; md < D / 32; ++md)
 #pragma unroll
@@ -545,9 +632,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dv[md][r] += xk[wave * PER_WAVE + ((D / 32 + md) * 16 + r) * 64 + lane];
     }
   // register r of block md is element d = 32 md + 8 (r/4) + 4 half + r%4 of key jk
-  const int64_t krow = (static_cast<int64_t>(b) * a.Skv + jk) * a.H + h;
-  float* ok = a.dk + krow * D;
-  float* ov = a.dv + krow * D;
+  const int64_t krow = (static_cast<int64_t>(b) * len + jk) * a.H + h;
+  float* ok = ch.dk + krow * D;
+  float* ov = ch.dv + krow * D;
   const bool acc = a.accum_dkv != 0;
 #pragma unroll
   for (int md = 0; md < D / 32; ++md)
@@ -604,27 +691,38 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* o, const T* dou
   }
 }
 
+template <int D, bool CAUSAL, int G>
+hipError_t launch_dq(const BwdArgs& a, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, G>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(kThreads * G), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t BH = static_cast<int64_t>(a.B) * a.H;
-  const int64_t nqt = (a.Sq + kBlk - 1) / kBlk, nkt = (a.Skv + kBlk - 1) / kBlk;
+  const int64_t nqt = (a.Sq + kBlk - 1) / kBlk;
   const int64_t dq_blocks = CAUSAL ? nqt * BH : (nqt * BH + 7) / 8 * 8;
-  const int64_t kv_blocks = CAUSAL ? nkt * BH : (nkt * BH + 7) / 8 * 8;
+  const int64_t kv_blocks = CAUSAL ? a.total_kt * BH : (a.total_kt * BH + 7) / 8 * 8;
   if (kv_blocks > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(static_cast<uint32_t>(kv_blocks)),
                        dim3(kKvThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (dq_blocks > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<uint32_t>(dq_blocks)),
-                       dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  if (dq_blocks == 0) return hipSuccess;
+  return a.groups == 2 ? launch_dq<D, CAUSAL, 2>(a, dq_blocks, stream)
+                       : launch_dq<D, CAUSAL, 1>(a, dq_blocks, stream);
 }
 
 }  // namespace
+
+// Two-group dQ blocks when the query tiles do not fill the compute units and
+// each has at least 4 key tiles to split.
+int bwd_dq_groups(int64_t B, int64_t H, int64_t Sq, int64_t key_tiles) {
+  const int64_t units = (Sq + kBlk - 1) / kBlk * B * H;
+  return units <= device_cus() && key_tiles >= 4 ? 2 : 1;
+}
 
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream) {
   if (D == 64) return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);

@@ -100,24 +100,39 @@ int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles);
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D);
 
 // ----- backward (attn_bwd.hip)
+struct BwdChunk {
+  const __bf16* k;  // [B][len][H][D]
+  const __bf16* v;
+  float* dk;        // [B][len][H][D]: this Q shard's share of the chunk's gradients
+  float* dv;
+  int32_t len;
+  int32_t diag;   // causal: key j visible to query i iff j <= i + diag (clamped like ChunkDesc)
+  int32_t tile0;  // 128-key tiles of the chunks before this one
+  int32_t pad;
+};
+
 struct BwdArgs {
   const __bf16* q;
-  const __bf16* k;
-  const __bf16* v;
   const __bf16* dout;
   const float* lse;    // [B][H][Sq], the full rows' LSE
   const float* delta;  // [B][H][Sq], <dO_i, O_i>
   float* dq;           // [B][Sq][H][D]
-  float* dk;           // [B][Skv][H][D]
-  float* dv;           // [B][Skv][H][D]
-  int32_t B, H, Sq, Skv;
+  int32_t B, H, Sq;
   float scale;
-  int32_t diag;  // causal: key j visible to query i iff j <= i + diag (clamped like ChunkDesc)
   int32_t accum_dq, accum_dkv;  // add into dq / dk, dv instead of overwriting
+  int32_t nchunks;
+  int32_t total_kt;  // 128-key tiles over all chunks
+  int32_t groups;    // dQ kernel: 1, or 2 (two groups of 4 waves split the key tiles)
+  BwdChunk chunks[CP_MAX_RING_CHUNKS];
 };
+// Groups per block (1 or 2) of the dQ kernel for these sizes.
+int bwd_dq_groups(int64_t B, int64_t H, int64_t Sq, int64_t key_tiles);
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t B, int64_t H,
                             int64_t Sq, int64_t D, bool bf16, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cus();
 
 // out_bf16: write O as bf16 (else fp32). causal: position-based masking.
 hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream);

@@ -302,13 +302,48 @@ cp_status cp_attn_backward_delta(const void* o, const void* dout, float* delta, 
  * written once by one block (no atomics), so results are byte-identical on
  * repeat. Sq == 0 gives dk = dv = 0 (unchanged when accumulating); Skv == 0
  * gives dq = 0 (unchanged when accumulating). D in {64, 128}; Sq, Skv < 2^30.
- * Two kernel launches; no workspace.
+ * Two kernel launches; no workspace. This is cp_ring_attention_backward with
+ * one chunk.
  */
 cp_status cp_attn_chunk_backward(const void* q, const void* k, const void* v, const void* dout,
                                  const float* lse, const float* delta, float* dq, float* dk,
                                  float* dv, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                  int64_t D, cp_dtype in_dtype, float scale, int causal,
                                  int64_t q_pos0, int64_t kv_pos0, int flags, void* stream);
+
+/* Gradient outputs of one K/V chunk: fp32 [B][len][H][D] each. */
+typedef struct {
+  float* dk;
+  float* dv;
+} cp_kv_grad;
+
+/*
+ * cp_ring_attention_backward — one ring rank's whole backward share: its Q
+ * shard against P K/V chunks.
+ *
+ * Defined by: the derivative of the ring's attention (see
+ * cp_attn_chunk_backward; Context parallelism guide (diffusers), sections Ring
+ * Attention and Ring Anything Attention for the chunks and their uneven
+ * lengths). Equal to P cp_attn_chunk_backward calls with dQ accumulated over
+ * the chunks, in one pair of launches: every chunk's key tiles form one grid
+ * for dK/dV, and the dQ kernel walks all chunks' keys per query tile.
+ *
+ *   q, dout [B][Sq][H][D] bf16; chunks: HOST array of P descriptors (as for
+ *   cp_ring_attention; pos0 drives causal masking, q_pos0 is the shard's first
+ *   position); lse, delta [B][H][Sq] fp32 of the full rows.
+ *   dq [B][Sq][H][D] fp32 = sum over the chunks of their dQ shares
+ *   (+= with CP_BWD_ACCUMULATE_DQ).
+ *   grads: HOST array of P cp_kv_grad; grads[c].dk / .dv receive chunk c's
+ *   dK, dV share from this Q shard (+= with CP_BWD_ACCUMULATE_DKV).
+ *   Zero-length chunks are skipped (their pointers may be null). P in 1..64.
+ *   No output may overlap an input or another output. No workspace.
+ * Arithmetic, determinism and limits as cp_attn_chunk_backward.
+ */
+cp_status cp_ring_attention_backward(const void* q, const cp_kv_chunk* chunks, int64_t P,
+                                     const void* dout, const float* lse, const float* delta,
+                                     float* dq, const cp_kv_grad* grads, int64_t B, int64_t H,
+                                     int64_t Sq, int64_t D, cp_dtype in_dtype, float scale,
+                                     int causal, int64_t q_pos0, int flags, void* stream);
 
 /* Text describing the last failed call on this thread ("" after a successful
  * call). Valid until the next cp_* call on the same thread. */

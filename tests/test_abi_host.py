@@ -263,3 +263,40 @@ def test_backward_delta_rejects(kw, status):
 
 def test_backward_delta_zero_size_is_noop():
     assert _delta(Sq=0, o=None, do=None, delta=None) == OK
+
+
+def _ring_bwd(P=2, lens=(8, 8), q=FAKE, do=FAKE4, lse=FAKE5, delta=FAKE6, dq=FAKE7,
+              kv=None, gr=None, B=1, H=2, Sq=8, D=128, dt=BF16, scale=0.1, causal=0, qp=0,
+              flags=0, null_arrays=False):
+    kv = kv or [(FAKE2 + 0x100000 * c, FAKE3 + 0x100000 * c) for c in range(P)]
+    gr = gr or [(FAKE8 + 0x100000 * c, FAKE9 + 0x100000 * c) for c in range(P)]
+    n = max(1, P)
+    arr, garr = (cp.KVChunk * n)(), (cp.KVGrad * n)()
+    for c in range(min(P, len(lens))):
+        arr[c] = cp.KVChunk(kv[c][0], kv[c][1], lens[c], 8 * c)
+        garr[c] = cp.KVGrad(gr[c][0], gr[c][1])
+    if null_arrays:
+        arr, garr = None, None
+    return cp._ring_bwd(q, arr, P, do, lse, delta, dq, garr, B, H, Sq, D, dt, scale, causal, qp,
+                        flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), INVALID), (dict(P=65), UNSUPPORTED), (dict(null_arrays=True), INVALID),
+    (dict(dt=F32), UNSUPPORTED), (dict(D=80), UNSUPPORTED), (dict(flags=8), INVALID),
+    (dict(lens=(8, -1)), INVALID), (dict(lens=(8, 1 << 30)), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(dq=FAKE7 + 8), INVALID),
+    (dict(kv=[(FAKE2, FAKE3), (None, FAKE3)]), INVALID),
+    (dict(gr=[(FAKE8, FAKE9), (FAKE8 + 0x100000, None)]), INVALID),
+    (dict(gr=[(FAKE8, FAKE9), (FAKE8, FAKE9 + 0x100000)]), INVALID),   # dk of both chunks alias
+    (dict(gr=[(FAKE2, FAKE9), (FAKE8 + 0x100000, FAKE9 + 0x100000)]), INVALID),  # dk on K
+    (dict(dq=FAKE8), INVALID),                                          # dq on a chunk's dk
+])
+def test_ring_backward_rejects(kw, status):
+    assert _ring_bwd(**kw) == status
+    assert cp.last_error().startswith("cp_ring_attention_backward")
+
+
+def test_ring_backward_zero_size_is_noop():
+    assert _ring_bwd(B=0) == OK
+    assert _ring_bwd(Sq=0, lens=(0, 0)) == OK and cp.last_error() == ""

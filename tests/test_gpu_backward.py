@@ -109,15 +109,16 @@ def test_chunk_backward_matches_oracle(B, Sq, Skv, H, D, causal, q_pos0, kv_pos0
     check_grad(dv, wv, "dV")
 
 
-def test_negative_scale():
-    say("backward negative scale")
+@pytest.mark.parametrize("scale,causal", [(-0.1, False), (-0.1, True), (0.0, True)])
+def test_negative_and_zero_scale(scale, causal):
+    say(f"backward scale={scale} causal={causal}")
     B, Sq, Skv, H, D = 1, 96, 160, 2, 128
     q, k, v, do = _inputs(B, Sq, Skv, H, D, seed=900)
     q64, k64, v64, do64 = (to_f64(x) for x in (q, k, v, do))
-    scale = -0.1
-    o, lse, delta, o_bf, lse_f = _saved_stats(q64, k64, v64, do64, scale, False, None, None)
-    _, dq, dk, dv = _run(q, k, v, do, o_bf, lse_f, scale, False, 0, 0)
-    wq, wk, wv = oracle.chunk_grad(q64, k64, v64, do64, lse, delta, scale)
+    q_pos, k_pos = np.arange(64, 64 + Sq), np.arange(Skv)
+    o, lse, delta, o_bf, lse_f = _saved_stats(q64, k64, v64, do64, scale, causal, q_pos, k_pos)
+    _, dq, dk, dv = _run(q, k, v, do, o_bf, lse_f, scale, causal, 64, 0)
+    wq, wk, wv = oracle.chunk_grad(q64, k64, v64, do64, lse, delta, scale, causal, q_pos, k_pos)
     check_grad(dq, wq, "dQ")
     check_grad(dk, wk, "dK")
     check_grad(dv, wv, "dV")
@@ -248,3 +249,79 @@ def test_delta_dtypes(dtype):
     torch.cuda.synchronize()
     want = oracle.backward_delta(to_f64(o), to_f64(do))
     assert np.abs(to_f64(got) - want).max() <= F32_MAX
+
+
+@pytest.mark.parametrize("lens,causal,H", [
+    ((96, 96, 96, 96), False, 2),          # even ring of 4
+    ((130, 0, 257, 64), True, 2),          # uneven, an empty chunk, causal
+    ((1025, 1025, 1025, 1024), True, 1),   # the ring-anything split of 4099
+    ((300,), False, 3),                    # P = 1
+])
+def test_ring_backward_matches_oracle(lens, causal, H):
+    """cp_ring_attention_backward: dQ over every chunk, each chunk's dK/dV share,
+    in ring order (rank 1 of the ring: its own chunk first)."""
+    say(f"ring backward lens={lens} causal={causal} H={H}")
+    D = 128
+    S = sum(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    r = 1 if len(lens) > 1 else 0
+    q0, n = int(starts[r]), lens[r] if lens[r] > 0 else lens[0]
+    q, k, v, do = _inputs(1, n, S, H, D, seed=S + H)
+    q64, k64, v64, do64 = (to_f64(x) for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    q_pos = np.arange(q0, q0 + n)
+    o, lse, delta, o_bf, lse_f = _saved_stats(q64, k64, v64, do64, scale, causal, q_pos,
+                                              np.arange(S))
+    wq, wk, wv = oracle.chunk_grad(q64, k64, v64, do64, lse, delta, scale, causal, q_pos,
+                                   np.arange(S))
+    kd, vd = k.to(DEV), v.to(DEV)
+    order = synthetic.ring_order(r, len(lens))
+    chunks = [(kd[:, s:s + m].contiguous(), vd[:, s:s + m].contiguous(), int(s))
+              for s, m in zip(starts, lens)]
+    qd, dod = q.to(DEV), do.to(DEV)
+    delta_d = cp.attn_backward_delta(o_bf.to(DEV), dod)
+    dq, grads = cp.ring_attention_backward(qd, [chunks[c] for c in order], dod, lse_f.to(DEV),
+                                           delta_d, scale=scale, causal=causal, q_pos0=q0)
+    torch.cuda.synchronize()
+    check_grad(dq, wq, "dQ")
+    got_k = torch.cat([grads[order.index(c)][0] for c in range(len(lens))], dim=1)
+    got_v = torch.cat([grads[order.index(c)][1] for c in range(len(lens))], dim=1)
+    check_grad(got_k, wk, "dK")
+    check_grad(got_v, wv, "dV")
+    # the same through per-chunk calls with dQ accumulated: identical bytes for
+    # dK/dV (the same blocks do the same work), dQ within rounding of the
+    # summation order
+    dq2 = torch.empty_like(dq)
+    for step, c in enumerate(order):
+        kc, vc, s0 = chunks[c]
+        _, dk2, dv2 = cp.attn_chunk_backward(qd, kc, vc, dod, lse_f.to(DEV), delta_d, dq2,
+                                             scale=scale, causal=causal, q_pos0=q0, kv_pos0=s0,
+                                             accumulate_dq=step > 0)
+        gk, gv = grads[step]
+        assert torch.equal(dk2, gk) and torch.equal(dv2, gv)
+    torch.cuda.synchronize()
+    check_grad(dq2, wq, "dQ per chunk")
+
+
+def test_ring_backward_accumulates_into_existing_buffers():
+    say("ring backward accumulate flags")
+    B, Sq, H, D = 1, 100, 2, 128
+    lens = (70, 130)
+    q, do = (x.to(DEV) for x in _inputs(B, Sq, 1, H, D, seed=990)[::3])
+    kv = [(synthetic.make_tensor((B, m, H, D), torch.bfloat16, 991 + c).to(DEV),
+           synthetic.make_tensor((B, m, H, D), torch.bfloat16, 995 + c).to(DEV), 70 * c)
+          for c, m in enumerate(lens)]
+    lse = torch.randn((B, H, Sq), device=DEV) + 8.0
+    delta = torch.randn((B, H, Sq), device=DEV)
+    dq0, g0 = cp.ring_attention_backward(q, kv, do, lse, delta)
+    base_q = torch.randn_like(dq0)
+    base_g = [(torch.randn_like(a), torch.randn_like(b)) for a, b in g0]
+    dq1 = base_q.clone()
+    g1 = [(a.clone(), b.clone()) for a, b in base_g]
+    cp.ring_attention_backward(q, kv, do, lse, delta, dq1, g1, accumulate_dq=True,
+                               accumulate_dkv=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(dq1, base_q + dq0, rtol=0, atol=1e-6)
+    for (a, b), (a0, b0), (x, y) in zip(g1, base_g, g0):
+        assert torch.allclose(a, a0 + x, rtol=0, atol=1e-6)
+        assert torch.allclose(b, b0 + y, rtol=0, atol=1e-6)
