@@ -219,10 +219,11 @@ __device__ __forceinline__ void store4(float* p, float s, float x0, float x1, fl
 
 // Block index -> (work item) with consecutive ids spread over the 8 XCDs and
 // each XCD taking a contiguous run of items (the tiles of one head stay in
-// one L2). Returns -1 for the padding blocks of the last round.
-__device__ __forceinline__ int xcd_item(int nitems) {
+// one L2). Returns -1 for the padding blocks of the last round. `blk` counts
+// from a multiple of 8, so blk % 8 is still the XCD the block runs on.
+__device__ __forceinline__ int xcd_item(int blk, int nitems) {
   const int per_xcd = (nitems + 7) / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int L = (blk % 8) * per_xcd + blk / 8;
   return L < nitems ? L : -1;
 }
 
@@ -233,10 +234,9 @@ __device__ __forceinline__ int xcd_item(int nitems) {
 // dQ accumulators are added through LDS at the end (grids with no more query
 // tiles than compute units).
 template <int D, bool CAUSAL, int G>
-__global__ __launch_bounds__(kThreads * G, G == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
   constexpr int TB = Geo<D>::kTileBytes;
-  // per group: stage s holds K at 2s, V at 2s + 1
-  __shared__ __attribute__((aligned(1024))) char smem[G * 4 * TB];
+  // smem: G * 4 * TB bytes; per group, stage s holds K at 2s, V at 2s + 1
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int grp = G == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
@@ -247,10 +247,11 @@ __global__ __launch_bounds__(kThreads * G, G == 1 ? 2 : 1) void bwd_dq_kernel(Bw
   const int nqt = (a.Sq + kBlk - 1) / kBlk;
   int bh, qt;
   if (CAUSAL) {  // the last query tiles see the most keys: launch them first
-    qt = nqt - 1 - static_cast<int>(blockIdx.x) / BH;
-    bh = static_cast<int>(blockIdx.x) % BH;
+    if (blk >= nqt * BH) return;
+    qt = nqt - 1 - blk / BH;
+    bh = blk % BH;
   } else {
-    const int L = xcd_item(nqt * BH);
+    const int L = xcd_item(blk, nqt * BH);
     if (L < 0) return;
     bh = L / nqt;
     qt = L % nqt;
@@ -427,12 +428,12 @@ __global__ __launch_bounds__(kThreads * G, G == 1 ? 2 : 1) void bwd_dq_kernel(Bw
 constexpr int kKvThreads = 512;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* smem, int blk) {
   constexpr int TB = Geo<D>::kTileBytes;  // one 64-row tile
   constexpr int RB = Geo<D>::kRowBytes;
-  // [K: 2 tiles][V: 2 tiles][stage 0: Q, dO][stage 1: Q, dO][stats: 2 x 512 B]
+  // smem (8 TB + 1024 bytes): [K: 2 tiles][V: 2 tiles][stage 0: Q, dO]
+  // [stage 1: Q, dO][stats: 2 x 512 B]
   constexpr int KV_BYTES = 4 * TB, ST_OFF = 8 * TB;
-  __shared__ __attribute__((aligned(1024))) char smem[8 * TB + 1024];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave in block, 0..7
@@ -442,10 +443,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nkt = a.total_kt;  // key tiles over all chunks
   int bh, t;
   if (CAUSAL) {  // in chunk order, the first key tiles are seen by the most queries
-    t = static_cast<int>(blockIdx.x) / BH;
-    bh = static_cast<int>(blockIdx.x) % BH;
+    if (blk >= nkt * BH) return;
+    t = blk / BH;
+    bh = blk % BH;
   } else {  // the key tiles of one head (every chunk) stay on one XCD
-    const int L = xcd_item(nkt * BH);
+    const int L = xcd_item(blk, nkt * BH);
     if (L < 0) return;
     bh = L / nkt;
     t = L % nkt;
@@ -648,6 +650,32 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(kThreads * G, G == 1 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[G * 4 * Geo<D>::kTileBytes];
+  dq_body<D, CAUSAL, G>(a, smem, static_cast<int>(blockIdx.x));
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[8 * Geo<D>::kTileBytes + 1024];
+  dkdv_body<D, CAUSAL>(a, smem, static_cast<int>(blockIdx.x));
+}
+
+// Both backward kernels in one grid, for grids too small to fill the GPU
+// alone: the first a.dq_blocks blocks are two-group dQ blocks (the longest
+// work, dispatched first), the rest dK/dV blocks, all of 512 threads. The
+// tail of one kind then fills the compute units the other leaves idle.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_fused_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[8 * Geo<D>::kTileBytes + 1024];
+  const int blk = static_cast<int>(blockIdx.x);
+  if (blk < a.dq_blocks)
+    dq_body<D, CAUSAL, 2>(a, smem, blk);
+  else
+    dkdv_body<D, CAUSAL>(a, smem, blk - a.dq_blocks);
+}
+
 // ------------------------------------------------------------- Delta kernel
 // Delta[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d] in fp32; 16 lanes per
 // row, each reading D/16 consecutive elements.
@@ -699,11 +727,20 @@ hipError_t launch_dq(const BwdArgs& a, int64_t blocks, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
   const int64_t BH = static_cast<int64_t>(a.B) * a.H;
   const int64_t nqt = (a.Sq + kBlk - 1) / kBlk;
-  const int64_t dq_blocks = CAUSAL ? nqt * BH : (nqt * BH + 7) / 8 * 8;
-  const int64_t kv_blocks = CAUSAL ? a.total_kt * BH : (a.total_kt * BH + 7) / 8 * 8;
+  // grids padded to whole rounds of the 8 XCDs (padding blocks exit at once)
+  const int64_t dq_blocks = (nqt * BH + 7) / 8 * 8;
+  const int64_t kv_blocks = (a.total_kt * BH + 7) / 8 * 8;
+  if (a.groups == 2 && kv_blocks > 0 && dq_blocks > 0) {
+    a.dq_blocks = static_cast<int32_t>(dq_blocks);
+    hipLaunchKernelGGL((bwd_fused_kernel<D, CAUSAL>),
+                       dim3(static_cast<uint32_t>(dq_blocks + kv_blocks)), dim3(kKvThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   if (kv_blocks > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(static_cast<uint32_t>(kv_blocks)),
                        dim3(kKvThreads), 0, stream, a);

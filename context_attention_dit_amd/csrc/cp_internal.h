@@ -123,6 +123,7 @@ struct BwdArgs {
   int32_t nchunks;
   int32_t total_kt;  // 128-key tiles over all chunks
   int32_t groups;    // dQ kernel: 1, or 2 (two groups of 4 waves split the key tiles)
+  int32_t dq_blocks;  // set by the launcher: dQ blocks at the front of a fused grid
   BwdChunk chunks[CP_MAX_RING_CHUNKS];
 };
 // Groups per block (1 or 2) of the dQ kernel for these sizes.
