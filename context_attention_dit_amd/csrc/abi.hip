@@ -415,12 +415,11 @@ cp_status cp_attn_chunk_backward(const void* q, const void* k, const void* v, co
   if (Skv >= kMaxSeq) return fail(CP_E_UNSUPPORTED, "%s: Skv exceeds 2^30", fn);
   if (flags & ~(CP_BWD_ACCUMULATE_DQ | CP_BWD_ACCUMULATE_DKV))
     return fail(CP_E_INVALID, "%s: unknown flag bits 0x%x", fn, flags);
-  if (in_dtype != CP_BF16)
-    return fail(CP_E_UNSUPPORTED, "%s: only bf16 inputs are built", fn);
   if (sat_mul({(Skv + 63) / 64, B, H}) > kMaxGrid / 8)
     return fail(CP_E_UNSUPPORTED, "%s: B*H*Skv too large for one launch", fn);
   if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ok();
-  const int64_t q_bytes = sat_mul({B, Sq, H, D, 2}), kv_bytes = sat_mul({B, Skv, H, D, 2});
+  const int64_t es = elem_size(in_dtype);
+  const int64_t q_bytes = sat_mul({B, Sq, H, D, es}), kv_bytes = sat_mul({B, Skv, H, D, es});
   const int64_t dq_bytes = sat_mul({B, Sq, H, D, 4}), dkv_bytes = sat_mul({B, Skv, H, D, 4});
   const int64_t l_bytes = sat_mul({B, H, Sq, 4});
   const bool has_q = Sq > 0, has_kv = Skv > 0;
@@ -469,8 +468,10 @@ cp_status cp_attn_chunk_backward(const void* q, const void* k, const void* v, co
   c.tile0 = 0;
   a.total_kt = static_cast<int32_t>((Skv + 127) / 128);
   a.groups = cpattn::bwd_dq_groups(B, H, Sq, (Skv + 63) / 64);
-  return hip_status(cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0,
-                                                 static_cast<hipStream_t>(stream)),
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(in_dtype == CP_BF16
+                        ? cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0, st)
+                        : cpattn::launch_attn_bwd_f32(a, static_cast<int>(D), causal != 0, st),
                     fn);
 }
 
@@ -489,7 +490,6 @@ cp_status cp_ring_attention_backward(const void* q, const cp_kv_chunk* chunks, i
   if (!chunks || !grads) return fail(CP_E_INVALID, "%s: null chunk or gradient array", fn);
   if (flags & ~(CP_BWD_ACCUMULATE_DQ | CP_BWD_ACCUMULATE_DKV))
     return fail(CP_E_INVALID, "%s: unknown flag bits 0x%x", fn, flags);
-  if (in_dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "%s: only bf16 inputs are built", fn);
   int64_t total_kt = 0, total_keys = 0;
   for (int64_t c = 0; c < P; ++c) {
     const int64_t len = chunks[c].len;
@@ -502,7 +502,8 @@ cp_status cp_ring_attention_backward(const void* q, const cp_kv_chunk* chunks, i
   if (sat_mul({total_kt, B, H}) > kMaxGrid / 8)
     return fail(CP_E_UNSUPPORTED, "%s: B*H*keys too large for one launch", fn);
   if (B == 0 || H == 0 || (Sq == 0 && total_keys == 0)) return ok();
-  const int64_t q_bytes = sat_mul({B, Sq, H, D, 2}), dq_bytes = sat_mul({B, Sq, H, D, 4});
+  const int64_t es = elem_size(in_dtype);
+  const int64_t q_bytes = sat_mul({B, Sq, H, D, es}), dq_bytes = sat_mul({B, Sq, H, D, 4});
   const int64_t l_bytes = sat_mul({B, H, Sq, 4});
   const bool has_q = Sq > 0;
   if (has_q && (!q || !dout || !lse || !delta || !dq))
@@ -527,7 +528,7 @@ cp_status cp_ring_attention_backward(const void* q, const cp_kv_chunk* chunks, i
   for (int64_t c = 0; c < P; ++c) {
     const int64_t len = chunks[c].len;
     if (len == 0) continue;
-    const int64_t kv_bytes = sat_mul({B, len, H, D, 2}), g_bytes = sat_mul({B, len, H, D, 4});
+    const int64_t kv_bytes = sat_mul({B, len, H, D, es}), g_bytes = sat_mul({B, len, H, D, 4});
     if (!chunks[c].k || !chunks[c].v || !grads[c].dk || !grads[c].dv)
       return fail(CP_E_INVALID, "%s: chunk %lld has a null pointer", fn, (long long)c);
     if (!aligned(chunks[c].k, 16) || !aligned(chunks[c].v, 16) || !aligned(grads[c].dk, 16) ||
@@ -575,8 +576,10 @@ cp_status cp_ring_attention_backward(const void* q, const cp_kv_chunk* chunks, i
   }
   a.total_kt = tile0;
   a.groups = cpattn::bwd_dq_groups(B, H, Sq, key_tiles);
-  return hip_status(cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0,
-                                                 static_cast<hipStream_t>(stream)),
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(in_dtype == CP_BF16
+                        ? cpattn::launch_attn_bwd_bf16(a, static_cast<int>(D), causal != 0, st)
+                        : cpattn::launch_attn_bwd_f32(a, static_cast<int>(D), causal != 0, st),
                     fn);
 }
 

@@ -129,6 +129,8 @@ struct BwdArgs {
 // Groups per block (1 or 2) of the dQ kernel for these sizes.
 int bwd_dq_groups(int64_t B, int64_t H, int64_t Sq, int64_t key_tiles);
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
+// fp32 inputs (the __bf16 pointers of BwdArgs then hold fp32 tensors).
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t B, int64_t H,
                             int64_t Sq, int64_t D, bool bf16, hipStream_t stream);
 

@@ -290,15 +290,16 @@ cp_status cp_attn_backward_delta(const void* o, const void* dout, float* delta, 
  * (CP_BWD_ACCUMULATE_DKV). One chunk over the whole sequence is a Ulysses
  * rank's local backward.
  *
- *   q, dout [B][Sq][H][D] and k, v [B][Skv][H][D] in in_dtype (CP_BF16 only);
+ *   q, dout [B][Sq][H][D] and k, v [B][Skv][H][D] in in_dtype (CP_BF16 or CP_F32);
  *   lse, delta [B][H][Sq] fp32 (lse in the cp_attn_chunk_partial convention);
  *   dq [B][Sq][H][D] and dk, dv [B][Skv][H][D] fp32, caller-allocated; with an
  *   ACCUMULATE flag the buffer must hold the running sum, else it is
  *   overwritten. causal, q_pos0, kv_pos0 and scale as in cp_attn_chunk_partial
  *   and equal to the forward's.
  *
- * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are rounded
- * to bf16 for their products (as P is in the forward). Each output element is
+ * Arithmetic: for bf16 inputs, bf16 MFMA products with fp32 accumulation; P
+ * and dS are rounded to bf16 for their products (as P is in the forward). For
+ * fp32 inputs every step is fp32 (the fp32 forward's companion). Each output element is
  * written once by one block (no atomics), so results are byte-identical on
  * repeat. Sq == 0 gives dk = dv = 0 (unchanged when accumulating); Skv == 0
  * gives dq = 0 (unchanged when accumulating). D in {64, 128}; Sq, Skv < 2^30.
@@ -328,7 +329,8 @@ typedef struct {
  * the chunks, in one pair of launches: every chunk's key tiles form one grid
  * for dK/dV, and the dQ kernel walks all chunks' keys per query tile.
  *
- *   q, dout [B][Sq][H][D] bf16; chunks: HOST array of P descriptors (as for
+ *   q, dout [B][Sq][H][D] in in_dtype (CP_BF16 or CP_F32); chunks: HOST
+ *   array of P descriptors (K/V in in_dtype, as for
  *   cp_ring_attention; pos0 drives causal masking, q_pos0 is the shard's first
  *   position); lse, delta [B][H][Sq] fp32 of the full rows.
  *   dq [B][Sq][H][D] fp32 = sum over the chunks of their dQ shares

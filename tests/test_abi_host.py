@@ -225,7 +225,7 @@ def _chunk_bwd(q=FAKE, k=FAKE2, v=FAKE3, do=FAKE4, lse=FAKE5, delta=FAKE6, dq=FA
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=96), UNSUPPORTED), (dict(dt=F32), UNSUPPORTED), (dict(dt=7), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(dt=7), INVALID),
     (dict(B=-1), INVALID), (dict(Skv=-1), INVALID), (dict(Skv=1 << 30), UNSUPPORTED),
     (dict(Sq=1 << 30), UNSUPPORTED), (dict(causal=2), INVALID),
     (dict(scale=float("inf")), INVALID), (dict(flags=4), INVALID),
@@ -283,7 +283,7 @@ def _ring_bwd(P=2, lens=(8, 8), q=FAKE, do=FAKE4, lse=FAKE5, delta=FAKE6, dq=FAK
 
 @pytest.mark.parametrize("kw,status", [
     (dict(P=0), INVALID), (dict(P=65), UNSUPPORTED), (dict(null_arrays=True), INVALID),
-    (dict(dt=F32), UNSUPPORTED), (dict(D=80), UNSUPPORTED), (dict(flags=8), INVALID),
+    (dict(dt=5), INVALID), (dict(D=80), UNSUPPORTED), (dict(flags=8), INVALID),
     (dict(lens=(8, -1)), INVALID), (dict(lens=(8, 1 << 30)), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(dq=FAKE7 + 8), INVALID),
     (dict(kv=[(FAKE2, FAKE3), (None, FAKE3)]), INVALID),

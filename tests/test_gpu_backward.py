@@ -325,3 +325,83 @@ def test_ring_backward_accumulates_into_existing_buffers():
     for (a, b), (a0, b0), (x, y) in zip(g1, base_g, g0):
         assert torch.allclose(a, a0 + x, rtol=0, atol=1e-6)
         assert torch.allclose(b, b0 + y, rtol=0, atol=1e-6)
+
+
+F32_GRAD_MAX = 1e-5
+
+
+@pytest.mark.parametrize("Sq,Skv,H,D,causal,q_pos0", [
+    (64, 256, 2, 64, False, 0),     # the tiny fp32 workload's ring rank against all keys
+    (64, 256, 2, 64, True, 64),     # the same rank, causal
+    (70, 133, 3, 128, True, 40),    # ragged, D = 128
+    (0, 40, 2, 64, False, 0),       # no queries: dK = dV = 0
+])
+def test_f32_backward_matches_oracle(Sq, Skv, H, D, causal, q_pos0):
+    """fp32 inputs: every step in fp32; max-abs 1e-5 (relative to max(1, max|ref|))."""
+    say(f"fp32 backward Sq={Sq} Skv={Skv} H={H} D={D} causal={causal}")
+    q, k, v, do = (synthetic.make_tensor(shape, torch.float32, 1300 + n)
+                   for n, shape in enumerate([(1, Sq, H, D), (1, Skv, H, D), (1, Skv, H, D),
+                                              (1, Sq, H, D)]))
+    q64, k64, v64, do64 = (to_f64(x) for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    q_pos, k_pos = np.arange(q_pos0, q_pos0 + Sq), np.arange(Skv)
+    o, lse = oracle.attention(q64, k64, v64, scale, causal, q_pos, k_pos)
+    delta = oracle.backward_delta(o, do64)
+    dd = [x.to(DEV) for x in (q, k, v, do)]
+    if Sq > 0:
+        delta_d = cp.attn_backward_delta(torch.tensor(o, dtype=torch.float32).to(DEV), dd[3])
+    else:
+        delta_d = torch.empty((1, H, 0), device=DEV)
+    dq, dk, dv = cp.attn_chunk_backward(*dd, torch.tensor(lse, dtype=torch.float32).to(DEV),
+                                        delta_d, scale=scale, causal=causal, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    want = oracle.chunk_grad(q64, k64, v64, do64, lse, delta, scale, causal, q_pos, k_pos)
+    for got, w, name in zip((dq, dk, dv), want, ("dQ", "dK", "dV")):
+        g = to_f64(got)
+        assert np.all(np.isfinite(g))
+        if w.size == 0:
+            continue
+        err = np.abs(g - w).max()
+        print(f"  {name}: max-abs {err:.2e} (max|ref| {np.abs(w).max():.2e})", flush=True)
+        assert err <= F32_GRAD_MAX * max(1.0, np.abs(w).max()), f"{name}: max-abs {err:.3e}"
+
+
+def test_f32_ring_backward_tiny_workload():
+    """The tiny fp32 workload (S 256, H 2, D 64, ring of 4): every rank's
+    backward through cp_ring_attention_backward; dK/dV summed over the ranks."""
+    w = synthetic.TINY
+    say(f"{w.name}: fp32 ring backward, all ranks")
+    q, k, v = synthetic.make_qkv(w)
+    do = synthetic.make_tensor(tuple(q.shape), torch.float32, 1400)
+    q64, k64, v64, do64 = (to_f64(x) for x in (q, k, v, do))
+    scale = 1 / math.sqrt(w.D)
+    o, lse = oracle.attention(q64, k64, v64, scale)
+    delta = oracle.backward_delta(o, do64)
+    wq, wk, wv = oracle.attention_grad(q64, k64, v64, do64, scale)
+    starts = w.chunk_starts()
+    kd, vd = k.to(DEV), v.to(DEV)
+    chunks = [(kd[:, s:s + m].contiguous(), vd[:, s:s + m].contiguous(), s)
+              for s, m in zip(starts, w.chunk_lens)]
+    dq = torch.empty(q.shape, device=DEV)
+    dk = torch.zeros(k.shape, device=DEV)
+    dv = torch.zeros(v.shape, device=DEV)
+    o_d = torch.tensor(o, dtype=torch.float32).to(DEV)
+    lse_d = torch.tensor(lse, dtype=torch.float32).to(DEV)
+    for r in range(w.P):
+        s0, n = starts[r], w.chunk_lens[r]
+        rows = slice(s0, s0 + n)
+        order = synthetic.ring_order(r, w.P)
+        qr, dor = q[:, rows].contiguous().to(DEV), do[:, rows].contiguous().to(DEV)
+        dl = cp.attn_backward_delta(o_d[:, rows].contiguous(), dor)
+        dq_r, grads = cp.ring_attention_backward(qr, [chunks[c] for c in order], dor,
+                                                 lse_d[:, :, rows].contiguous(), dl, scale=scale,
+                                                 q_pos0=s0)
+        dq[:, rows] = dq_r
+        for c, (gk, gv) in zip(order, grads):
+            dk[:, starts[c]:starts[c] + w.chunk_lens[c]] += gk
+            dv[:, starts[c]:starts[c] + w.chunk_lens[c]] += gv
+    torch.cuda.synchronize()
+    for got, want, name in ((dq, wq, "dQ"), (dk, wk, "dK"), (dv, wv, "dV")):
+        err = np.abs(to_f64(got) - want).max()
+        print(f"  {name}: max-abs {err:.2e}", flush=True)
+        assert err <= F32_GRAD_MAX * max(1.0, np.abs(want).max()), f"{name}: max-abs {err:.3e}"
