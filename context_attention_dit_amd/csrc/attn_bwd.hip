@@ -1,34 +1,41 @@
-// Backward of bf16 attention over one K/V chunk on CDNA4 matrix cores (gfx950).
+// Backward of bf16 attention over a list of K/V chunks on CDNA4 matrix cores
+// (gfx950).
 //
 // What it computes: the gradients of O = softmax(scale * Q K^T) V against an
-// upstream gradient dO, restricted to one K/V chunk, from the row statistics
-// the forward saved (the row log-sum-exp LSE, and Delta_i = <dO_i, O_i>):
+// upstream gradient dO, over the K/V chunks it is given, from the row
+// statistics the forward saved (the row log-sum-exp LSE, and
+// Delta_i = <dO_i, O_i>):
 //   P_ij  = exp(scale <q_i, k_j> - LSE_i)         (0 for masked pairs)
 //   dS_ij = P_ij (<dO_i, v_j> - Delta_i)
 //   dQ_i  = scale * sum_j dS_ij k_j,  dK_j = scale * sum_i dS_ij q_i,
 //   dV_j  = sum_i P_ij dO_i.
-// With the full rows' LSE and Delta this is one chunk's exact share, so a ring
-// rank sums dQ over the chunks it visits and adds its dK, dV share into the
-// chunk's travelling accumulators (Context parallelism guide (diffusers),
-// section Ring Attention, run backwards); one chunk over the whole sequence is
-// a Ulysses rank's local backward (Ulysses Sequence Parallelism article:
-// training with long contexts; detailed notes 2: the score matrix is never
-// stored, so the weights are recomputed from the saved LSE).
+// With the full rows' LSE and Delta every chunk's share is exact, so a ring
+// rank sums dQ over the chunks it visits and adds each chunk's dK, dV share
+// into that chunk's travelling accumulators (Context parallelism guide
+// (diffusers), section Ring Attention, run backwards); one chunk over the
+// whole sequence is a Ulysses rank's local backward (Ulysses Sequence
+// Parallelism article: training with long contexts; detailed notes 2: the
+// score matrix is never stored, so the weights are recomputed from the LSE).
 //
-// How it maps to the hardware. Two kernels, each owning one output and
-// writing it exactly once (no atomics: deterministic, and dQ / dK / dV can be
-// accumulated into the caller's fp32 buffers with a plain read-add-write):
-//  * dq kernel: a block keeps 128 query rows resident (4 waves x 32) and
-//    streams 64-key K/V tiles through double-buffered LDS. Per tile a wave
-//    computes S^T = K Q^T and dP^T = V dO^T (Q^T and dO^T are B operands held
-//    in registers), forms dS^T in the accumulator layout (lane = query), and
-//    adds dQ^T += K^T dS^T with K^T fragments read transposed from the same
-//    K tile (ds_read_b64_tr_b16).
-//  * dkdv kernel: a block keeps 128 keys resident and streams 64-row Q / dO
-//    tiles (plus those rows' LSE and Delta). Per 32-row half-tile a wave
-//    computes S = Q K^T and dP = dO V^T (K^T and V^T are register B
-//    operands), so the accumulators hold P and dS with lane = key, then adds
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+// How it maps to the hardware. Two block bodies, each owning one kind of
+// output and writing every element of it exactly once (no atomics: results
+// are deterministic, and dQ / dK / dV can be accumulated into the caller's
+// fp32 buffers with a plain read-add-write):
+//  * dQ (query-stationary): 4 waves keep 128 query rows, with Q^T and dO^T
+//    held in registers as B operands, and walk every chunk's 64-key K/V tiles
+//    through double-buffered LDS. Per tile a wave computes S^T = K Q^T and
+//    dP^T = V dO^T, forms dS^T in the accumulator layout (lane = query) and
+//    adds dQ^T += K^T dS^T, the K^T fragments read transposed from the same K
+//    tile (ds_read_b64_tr_b16). On grids with no more query tiles than compute
+//    units a block is two such groups splitting the key tiles, their dQ
+//    added through LDS at the end.
+//  * dK/dV (key-stationary): 8 waves over 128 keys of one chunk. The keys' K
+//    and V stay in LDS for the whole block and are read as B operands; the
+//    two 4-wave groups take the two 32-row halves of every 64-row Q/dO tile.
+//    Per half-tile a wave computes S = Q K^T and dP = dO V^T, forms P and dS
+//    in the accumulator layout (lane = key) and adds dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T and Q^T read transposed. The groups' partial
+//    sums are added through LDS at the end, in a fixed order.
 //  * Every streamed tile sits in LDS with row bits 2 and 3 swapped and its
 //    16-byte units XOR-swizzled by the row. With the swap, the 32x32
 //    accumulator registers of lane l hold 8 consecutive tile rows per
@@ -37,9 +44,12 @@
 //    reads of the same tile find those rows as two groups of four.
 //  * Direct global->LDS loads (global_load_lds_dwordx4) fill the tiles with
 //    no staging registers; one barrier per tile.
-//  * The softmax weights use exp2 with scale*log2(e) folded into one FMA per
-//    score and the LSE pre-multiplied by log2(e).
-//  * A row whose LSE is -inf saw no key anywhere: its weights are 0.
+//  * Weights are exp2 of one FMA per score, with the signed scale*log2(e) and
+//    -log2(e)*LSE (no row maximum is needed, so no sign trick either). A row
+//    whose LSE is -inf saw no key anywhere and gets weight 0; a masked pair
+//    gets a score whose product with the signed factor is -inf.
+//  * Grids too small to fill the GPU run both bodies in one launch: the
+//    two-group dQ blocks first, the dK/dV blocks behind them.
 #include "cp_internal.h"
 
 namespace cpattn {
@@ -172,15 +182,12 @@ struct TileGeo {
 };
 
 // One row of a [.][H][D] bf16 tensor as B-operand fragments: lane holds
-// elements 16 ks + 8 half .. +7 of row `row` (zeros if !valid); `flip` XORs
-// the sign bits.
+// elements 16 ks + 8 half .. +7 of the row at `p` (zeros if !valid).
 template <int D>
-__device__ __forceinline__ void load_row_frags(const __bf16* p, bool valid, uint32_t flip,
-                                               int half, bf16x8* f) {
+__device__ __forceinline__ void load_row_frags(const __bf16* p, bool valid, int half, bf16x8* f) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * ks + 8 * half);
-    w ^= flip;
     if (!valid) w = u32x4{0, 0, 0, 0};
     f[ks] = __builtin_bit_cast(bf16x8, w);
   }
@@ -266,8 +273,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
   // resident B operands: Q^T and dO^T
   bf16x8 qf[D / 16], df[D / 16];
   const int64_t qrow = (static_cast<int64_t>(b) * a.Sq + ic) * a.H + h;
-  load_row_frags<D>(a.q + qrow * D, valid, 0u, half, qf);
-  load_row_frags<D>(a.dout + qrow * D, valid, 0u, half, df);
+  load_row_frags<D>(a.q + qrow * D, valid, half, qf);
+  load_row_frags<D>(a.dout + qrow * D, valid, half, df);
   const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + ic;
   const float nl = valid ? neg_lse2(a.lse[lrow]) : -INFINITY;
   const float dlt = valid ? a.delta[lrow] : 0.f;
@@ -430,7 +437,6 @@ constexpr int kKvThreads = 512;
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* smem, int blk) {
   constexpr int TB = Geo<D>::kTileBytes;  // one 64-row tile
-  constexpr int RB = Geo<D>::kRowBytes;
   // smem (8 TB + 1024 bytes): [K: 2 tiles][V: 2 tiles][stage 0: Q, dO]
   // [stage 1: Q, dO][stats: 2 x 512 B]
   constexpr int KV_BYTES = 4 * TB, ST_OFF = 8 * TB;
@@ -507,8 +513,9 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* smem, int blk)
     return *reinterpret_cast<const bf16x8*>(base + (kv_rd0 ^ (ks << 5)));
   };
 
-  // Row statistics of a tile, staged by wave 0 through registers (see the
-  // forward-statistics note in the file header): rows past Sq and rows whose
+  // Row statistics of a tile, staged by wave 0 through registers: fetched when
+  // the tile's loads are issued, converted to -log2(e)*LSE and written to LDS
+  // before the barrier that publishes the tile. Rows past Sq and rows whose
   // LSE is -inf get -inf, so their weights are exactly 0 with no masking.
   float st_l = -INFINITY, st_d = 0.f;
   auto fetch_stats = [&](int q0) {
@@ -609,7 +616,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* smem, int blk)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  (void)RB;
 
   // group 1 hands its partial dK, dV to group 0 through LDS (every wave is
   // past its last tile read: the loop ends with a barrier)
