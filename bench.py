@@ -370,6 +370,11 @@ def ulysses_workload(torch, cp, synthetic, dev, flush, w):
         rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)
     back = torch.empty_like(qkv[0])
     d_h2s = time_launches(torch, lambda: cp.ulysses_head2seq(heads[1], P, back), 2, 10, flush)
+    # the rank's Q, K and V regrouped together in one launch (stacked tensors)
+    qkv3 = torch.stack(qkv)
+    heads3 = torch.empty((3,) + tuple(heads[0].shape), dtype=w.dtype, device=dev)
+    d_s2h3 = time_launches(torch, lambda: cp.ulysses_seq2head(qkv3, P, heads3), 2, 10, flush)
+    del qkv3, heads3
     res = {
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
@@ -380,10 +385,14 @@ def ulysses_workload(torch, cp, synthetic, dev, flush, w):
         "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
         "relayout_bytes_per_tensor": nbytes,
         "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "seq2head_qkv_us": median(d_s2h3) * 1e3,
+        "seq2head_qkv_gbs": 3 * nbytes / (median(d_s2h3) * 1e-3) / 1e9,
+        "seq2head_qkv_hbm_frac": 3 * nbytes / (median(d_s2h3) * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "causal": w.causal, "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
-        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
+        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
+        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}")
     del qkv, heads, rq, rk, rv, o, lse, back
     torch.cuda.empty_cache()
     return res
@@ -423,7 +432,8 @@ def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
         "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
-        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
+        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
+        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}")
     return res
 
 

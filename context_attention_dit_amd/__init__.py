@@ -11,6 +11,7 @@ Entry points (same names as the C ABI, without the ``cp_`` prefix):
   ring_attention       one ring rank: Q over P chunks in visit order, fused fp32 merge
   ulysses_seq2head     Ulysses regrouping before attention (all P ranks)
   ulysses_head2seq     Ulysses regrouping after attention (inverse)
+                       (both also take a stack of tensors, e.g. Q, K, V, in one launch)
   ulysses_anything_seq2head / ulysses_anything_head2seq
                        the same with uneven per-rank token and head counts
   kv_gather            the K/V all-gather's unpack (sequence shards joined)
@@ -71,6 +72,8 @@ _ring = _sig("cp_ring_attention", [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp,
                                    _i64, _int, _f32, _int, _i64, _vp, ctypes.c_size_t, _vp])
 _seq2head = _sig("cp_ulysses_seq2head", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _head2seq = _sig("cp_ulysses_head2seq", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
+_seq2head_n = _sig("cp_ulysses_seq2head_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
+_head2seq_n = _sig("cp_ulysses_head2seq_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
 _any_seq2head = _sig("cp_ulysses_anything_seq2head",
                      [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
 _any_head2seq = _sig("cp_ulysses_anything_head2seq",
@@ -217,27 +220,45 @@ def ring_attention(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.T
 
 def ulysses_seq2head(x: torch.Tensor, P: int, out: Optional[torch.Tensor] = None, *,
                      stream=None) -> torch.Tensor:
-    """``[P][B][S_l][H][D]`` -> ``[P][B][P*S_l][H/P][D]``; see cp_ulysses_seq2head."""
-    if x.dim() != 5 or x.shape[0] != P:
-        raise ValueError("x must be [P][B][S_local][H][D]")
-    _, B, S_l, H, D = x.shape
+    """``[P][B][S_l][H][D]`` -> ``[P][B][P*S_l][H/P][D]``; see cp_ulysses_seq2head.
+
+    A 6-D ``x`` of shape ``[n][P][B][S_l][H][D]`` (for example a rank's Q, K and
+    V stacked) is regrouped tensor by tensor in one launch (cp_ulysses_seq2head_n).
+    """
+    if x.dim() not in (5, 6) or x.shape[-5] != P:
+        raise ValueError("x must be [P][B][S_local][H][D] or [n][P][B][S_local][H][D]")
+    _, B, S_l, H, D = x.shape[-5:]
+    lead = tuple(x.shape[:-5])
     if out is None:
-        out = torch.empty((P, B, P * S_l, H // P, D), dtype=x.dtype, device=x.device)
-    _check("cp_ulysses_seq2head", _seq2head(_ptr(x), _ptr(out), P, B, S_l, H, D,
-                                            _dtype_code(x.dtype), _stream(stream)))
+        out = torch.empty(lead + (P, B, P * S_l, H // P, D), dtype=x.dtype, device=x.device)
+    if x.dim() == 6:
+        _check("cp_ulysses_seq2head_n", _seq2head_n(_ptr(x), _ptr(out), x.shape[0], P, B, S_l,
+                                                    H, D, _dtype_code(x.dtype), _stream(stream)))
+    else:
+        _check("cp_ulysses_seq2head", _seq2head(_ptr(x), _ptr(out), P, B, S_l, H, D,
+                                                _dtype_code(x.dtype), _stream(stream)))
     return out
 
 
 def ulysses_head2seq(y: torch.Tensor, P: int, out: Optional[torch.Tensor] = None, *,
                      stream=None) -> torch.Tensor:
-    """``[P][B][P*S_l][H_l][D]`` -> ``[P][B][S_l][P*H_l][D]``; see cp_ulysses_head2seq."""
-    if y.dim() != 5 or y.shape[0] != P or y.shape[2] % P != 0:
-        raise ValueError("y must be [P][B][P*S_local][H/P][D]")
-    _, B, S, H_l, D = y.shape
+    """``[P][B][P*S_l][H_l][D]`` -> ``[P][B][S_l][P*H_l][D]``; see cp_ulysses_head2seq.
+
+    A 6-D ``y`` (``[n][P][B][P*S_l][H_l][D]``) is regrouped tensor by tensor in
+    one launch (cp_ulysses_head2seq_n)."""
+    if y.dim() not in (5, 6) or y.shape[-5] != P or y.shape[-3] % P != 0:
+        raise ValueError("y must be [P][B][P*S_local][H/P][D] or [n][P][B][P*S_local][H/P][D]")
+    _, B, S, H_l, D = y.shape[-5:]
+    lead = tuple(y.shape[:-5])
     if out is None:
-        out = torch.empty((P, B, S // P, H_l * P, D), dtype=y.dtype, device=y.device)
-    _check("cp_ulysses_head2seq", _head2seq(_ptr(y), _ptr(out), P, B, S // P, H_l * P, D,
-                                            _dtype_code(y.dtype), _stream(stream)))
+        out = torch.empty(lead + (P, B, S // P, H_l * P, D), dtype=y.dtype, device=y.device)
+    if y.dim() == 6:
+        _check("cp_ulysses_head2seq_n", _head2seq_n(_ptr(y), _ptr(out), y.shape[0], P, B, S // P,
+                                                    H_l * P, D, _dtype_code(y.dtype),
+                                                    _stream(stream)))
+    else:
+        _check("cp_ulysses_head2seq", _head2seq(_ptr(y), _ptr(out), P, B, S // P, H_l * P, D,
+                                                _dtype_code(y.dtype), _stream(stream)))
     return out
 
 

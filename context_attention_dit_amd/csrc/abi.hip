@@ -279,9 +279,11 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
                           static_cast<hipStream_t>(stream));
 }
 
-static cp_status relayout(const char* fn, const void* in, void* out, int64_t P, int64_t B,
-                          int64_t S_local, int64_t H, int64_t D, cp_dtype dtype, void* stream,
-                          bool seq2head) {
+static cp_status relayout(const char* fn, const void* in, void* out, int64_t count, int64_t P,
+                          int64_t B, int64_t S_local, int64_t H, int64_t D, cp_dtype dtype,
+                          void* stream, bool seq2head) {
+  if (count < 1) return fail(CP_E_INVALID, "%s: count must be >= 1", fn);
+  if (count > 65535) return fail(CP_E_UNSUPPORTED, "%s: count exceeds 65535", fn);
   if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
   if (B < 0 || S_local < 0 || H < 0 || D < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
   if (!valid_dtype(dtype)) return fail(CP_E_INVALID, "%s: unknown dtype %d", fn, dtype);
@@ -294,8 +296,10 @@ static cp_status relayout(const char* fn, const void* in, void* out, int64_t P, 
   if (!aligned(in, es) || !aligned(out, es))
     return fail(CP_E_INVALID, "%s: pointer not aligned to the element size", fn);
   const int64_t bytes = sat_mul({P, B, S_local, H, D, es});
-  if (overlap(in, bytes, out, bytes)) return fail(CP_E_INVALID, "%s: out overlaps in", fn);
-  cpattn::RelayoutDesc d{P, B, S_local, H, D, es, seq2head};
+  const int64_t all_bytes = sat_mul({count, bytes});
+  if (overlap(in, all_bytes, out, all_bytes))
+    return fail(CP_E_INVALID, "%s: out overlaps in", fn);
+  cpattn::RelayoutDesc d{P, B, S_local, H, D, es, seq2head, count};
   const int w = cpattn::relayout_word_bytes(in, out, d);
   if (bytes / w >= (int64_t(1) << 31) || sat_mul({P, B, S_local, P}) >= (int64_t(1) << 31))
     return fail(CP_E_UNSUPPORTED, "%s: tensor of %lld bytes too large for one launch", fn,
@@ -305,12 +309,26 @@ static cp_status relayout(const char* fn, const void* in, void* out, int64_t P, 
 
 cp_status cp_ulysses_seq2head(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
                               int64_t H, int64_t D, cp_dtype dtype, void* stream) {
-  return relayout("cp_ulysses_seq2head", in, out, P, B, S_local, H, D, dtype, stream, true);
+  return relayout("cp_ulysses_seq2head", in, out, 1, P, B, S_local, H, D, dtype, stream, true);
 }
 
 cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
                               int64_t H, int64_t D, cp_dtype dtype, void* stream) {
-  return relayout("cp_ulysses_head2seq", in, out, P, B, S_local, H, D, dtype, stream, false);
+  return relayout("cp_ulysses_head2seq", in, out, 1, P, B, S_local, H, D, dtype, stream, false);
+}
+
+cp_status cp_ulysses_seq2head_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,
+                                int64_t S_local, int64_t H, int64_t D, cp_dtype dtype,
+                                void* stream) {
+  return relayout("cp_ulysses_seq2head_n", in, out, count, P, B, S_local, H, D, dtype, stream,
+                  true);
+}
+
+cp_status cp_ulysses_head2seq_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,
+                                int64_t S_local, int64_t H, int64_t D, cp_dtype dtype,
+                                void* stream) {
+  return relayout("cp_ulysses_head2seq_n", in, out, count, P, B, S_local, H, D, dtype, stream,
+                  false);
 }
 
 static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t P, int64_t B,

@@ -37,6 +37,7 @@ struct RelayoutDesc {
   int64_t P, B, S_local, H, D;
   int elem_bytes;
   bool seq2head;
+  int64_t count = 1;  // tensors stored back to back in `in` and in `out`
 };
 int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d);
 hipError_t launch_relayout(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream);

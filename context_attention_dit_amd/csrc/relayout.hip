@@ -7,7 +7,9 @@
 //   seq2head: out[p][b][q*S_l + s][h][d] = in[q][b][s][p*H_l + h][d]
 //   head2seq: out[q][b][s][p*H_l + h][d] = in[p][b][q*S_l + s][h][d]
 // Each run is H_l*D contiguous elements on both sides, so the kernel is a
-// streaming copy: every work-item moves whole UNIT-byte words (16 bytes when
+// streaming copy (one launch can move several tensors stored back to back,
+// such as a rank's Q, K and V, which makes the transfer long enough to keep
+// HBM busy): every work-item moves whole UNIT-byte words (16 bytes when
 // the run length and both pointers allow it), consecutive lanes touch
 // consecutive words of a run, and loads/stores are non-temporal because each
 // byte is read once and written once.
@@ -75,8 +77,9 @@ template <int UNIT, bool SEQ2HEAD>
 __global__ __launch_bounds__(kThreads) void relayout_kernel(const void* __restrict__ in_,
                                                             void* __restrict__ out_, Geometry g) {
   using T = typename Word<UNIT>::T;
-  const T* in = static_cast<const T*>(in_);
-  T* out = static_cast<T*>(out_);
+  // blockIdx.y: which of the back-to-back tensors
+  const T* in = static_cast<const T*>(in_) + static_cast<uint64_t>(blockIdx.y) * g.total;
+  T* out = static_cast<T*>(out_) + static_cast<uint64_t>(blockIdx.y) * g.total;
   const uint32_t base = blockIdx.x * (kThreads * kUnitsPerThread) + threadIdx.x;
   T v[kUnitsPerThread];
   uint32_t dst[kUnitsPerThread];
@@ -104,13 +107,13 @@ hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStre
   g.seqP.init(static_cast<uint32_t>(d.P * d.S_local));
   g.P.init(static_cast<uint32_t>(d.P));
   const uint32_t per_block = kThreads * kUnitsPerThread;
-  const uint32_t blocks = (g.total + per_block - 1) / per_block;
+  const dim3 grid((g.total + per_block - 1) / per_block, static_cast<uint32_t>(d.count));
   if (d.seq2head)
-    hipLaunchKernelGGL((relayout_kernel<UNIT, true>), dim3(blocks), dim3(kThreads), 0, stream, in,
-                       out, g);
+    hipLaunchKernelGGL((relayout_kernel<UNIT, true>), grid, dim3(kThreads), 0, stream, in, out,
+                       g);
   else
-    hipLaunchKernelGGL((relayout_kernel<UNIT, false>), dim3(blocks), dim3(kThreads), 0, stream,
-                       in, out, g);
+    hipLaunchKernelGGL((relayout_kernel<UNIT, false>), grid, dim3(kThreads), 0, stream, in, out,
+                       g);
   return hipGetLastError();
 }
 

@@ -188,6 +188,27 @@ cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, i
                               int64_t H, int64_t D, cp_dtype dtype, void* stream);
 
 /*
+ * cp_ulysses_seq2head_n / cp_ulysses_head2seq_n — the same regroupings for
+ * `count` tensors stored back to back, in one launch.
+ *
+ * Defined by: as cp_ulysses_seq2head / cp_ulysses_head2seq. A Ulysses rank
+ * regroups its Q, K and V together before attention (Context parallelism
+ * guide (diffusers), section Ulysses Attention; Ulysses Sequence Parallelism
+ * article, detailed notes 4), so one launch moves all three.
+ *   in:  count tensors, tensor t starting at element t*P*B*S_local*H*D, each in
+ *        the single-tensor call's input layout; out likewise in its output
+ *        layout. count in 1..65535; every other argument, limit and rule as in
+ *        the single-tensor calls (each tensor below 2^31 words). Tensor t of
+ *        out equals the single-tensor call on tensor t of in, bit for bit.
+ */
+cp_status cp_ulysses_seq2head_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,
+                                int64_t S_local, int64_t H, int64_t D, cp_dtype dtype,
+                                void* stream);
+cp_status cp_ulysses_head2seq_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,
+                                int64_t S_local, int64_t H, int64_t D, cp_dtype dtype,
+                                void* stream);
+
+/*
  * cp_ulysses_anything_seq2head — the Ulysses regrouping when neither the
  * sequence nor the heads divide by the degree.
  *

@@ -300,3 +300,17 @@ def test_ring_backward_rejects(kw, status):
 def test_ring_backward_zero_size_is_noop():
     assert _ring_bwd(B=0) == OK
     assert _ring_bwd(Sq=0, lens=(0, 0)) == OK and cp.last_error() == ""
+
+
+@pytest.mark.parametrize("name", ["_seq2head_n", "_head2seq_n"])
+@pytest.mark.parametrize("count,kw,status", [
+    (0, {}, INVALID), (65536, {}, UNSUPPORTED), (3, dict(H=6, P=4), DIVISIBILITY),
+    (3, dict(out=FAKE + 3 * 4 * 1 * 8 * 8 * 128 * 2 - 64), INVALID),   # out overlaps the 3rd tensor
+])
+def test_batched_relayout_rejects(name, count, kw, status):
+    args = dict(inp=FAKE, out=FAKE2, P=4, B=1, S=8, H=8, D=128, dt=BF16)
+    args.update(kw)
+    fn = getattr(cp, name)
+    assert fn(args["inp"], args["out"], count, args["P"], args["B"], args["S"], args["H"],
+              args["D"], args["dt"], None) == status
+    assert cp.last_error().startswith("cp_ulysses")

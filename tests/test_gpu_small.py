@@ -492,3 +492,24 @@ def test_rejected_call_leaves_outputs_untouched():
     assert e.value.status == 3
     torch.cuda.synchronize()
     assert torch.all(o == 5.0) and torch.all(lse == 5.0) and torch.all(y == 5.0)
+
+
+@pytest.mark.parametrize("n,P,B,S_l,H,D,dtype", [
+    (3, 4, 1, 37, 8, 128, torch.bfloat16),    # a rank's Q, K, V
+    (2, 8, 2, 5, 40, 128, torch.bfloat16),
+    (3, 2, 1, 9, 4, 5, torch.float32),        # 4-byte words
+    (3, 3, 2, 4, 6, 3, torch.bfloat16),       # 2-byte words
+])
+def test_relayout_stacked_tensors_bit_exact(n, P, B, S_l, H, D, dtype):
+    """One launch over n tensors back to back equals n single-tensor relayouts."""
+    say(f"stacked relayout n={n} P={P} B={B} S_l={S_l} H={H} D={D} {dtype}")
+    isz = 2 if dtype == torch.bfloat16 else 4
+    bits = synthetic.random_bits((n, P, B, S_l, H, D), isz, seed=n * 1000 + P * 10 + D)
+    x = bits.view(dtype).to(DEV)
+    y = cp.ulysses_seq2head(x, P)
+    z = cp.ulysses_head2seq(y, P)
+    torch.cuda.synchronize()
+    yb = y.cpu().view(bits.dtype).numpy()
+    for t in range(n):
+        assert np.array_equal(yb[t], oracle.seq2head(bits[t].numpy(), P)), f"tensor {t}"
+    assert np.array_equal(z.cpu().view(bits.dtype).numpy(), bits.numpy())
