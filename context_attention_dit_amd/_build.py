@@ -58,6 +58,29 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
+    build_c_abi_check(verbose)
+
+
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_check")
+
+
+def build_c_abi_check(verbose: bool = False) -> None:
+    """Compile the plain-C99 program that drives the ABI through include/cp_attn.h
+    (gcc, HIP runtime C API, linked against the library just built)."""
+    if not os.path.exists(C_CHECK_SRC):
+        return
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), C_CHECK_SRC,
+           "-o", C_CHECK_BIN, "-L", PKG, "-lcpattn", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../../context_attention_dit_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {C_CHECK_SRC}:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_CHECK_BIN}", file=sys.stderr)
     return LIB
 
 
