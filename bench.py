@@ -56,7 +56,9 @@ def causal_pairs_square(S: int) -> int:
 
 
 def time_launches(torch, fn, warmup: int, iters: int, flush=None):
-    """Per-launch durations (ms) from HIP events on the current stream."""
+    """Per-launch durations (ms) from HIP events on the current stream, each launch
+    bracketed on its own (used with `flush` for the HBM-bound kernels, so that each
+    launch starts from cold caches)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -347,9 +349,9 @@ def merge_workload(torch, cp, dev, flush, q0, vis, wf):
     out["flux_lse_merge"] = {"us": median(d) * 1e3, "gbs": mbytes / (median(d) * 1e-3) / 1e9,
                              "bytes": mbytes,
                              "hbm_frac": mbytes / (median(d) * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    d = time_launches(torch, lambda: [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis], 2,
-                      10)
-    out["flux_partials_x4"] = {"us": median(d) * 1e3}
+    ms = time_back_to_back(torch, lambda: [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis],
+                           3, 20)
+    out["flux_partials_x4"] = {"us": ms * 1e3}
     return out
 
 
@@ -368,8 +370,8 @@ def ulysses_workload(torch, cp, synthetic, dev, flush, w):
     lse = torch.empty((1, w.H_local, w.S), dtype=torch.float32, device=dev)
     flops = 4.0 * D * w.H_local * (causal_pairs_square(w.S) if w.causal else w.S * w.S)
     reps = 3 if w.causal else 10
-    d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
-        rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)
+    d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
+        rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)]
     back = torch.empty_like(qkv[0])
     d_h2s = time_launches(torch, lambda: cp.ulysses_head2seq(heads[1], P, back), 2, 10, flush)
     # the rank's Q, K and V regrouped together in one launch (stacked tensors)
@@ -417,8 +419,8 @@ def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
     o = torch.empty_like(rq)
     lse = torch.empty((1, h0, S), dtype=torch.float32, device=dev)
     flops = 4.0 * D * h0 * S * S
-    d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
-        rq, rk, rv, o, lse, out_dtype=torch.bfloat16), 2, 10)
+    d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
+        rq, rk, rv, o, lse, out_dtype=torch.bfloat16), 5, 50)]
     back = torch.empty_like(qkv[0])
     d_h2s = time_launches(torch, lambda: cp.ulysses_anything_head2seq(
         groups[1], s_lens, h_counts, 1, D, back), 2, 10, flush)
@@ -454,8 +456,8 @@ def kv_gather_workload(torch, cp, synthetic, dev, flush):
     o = torch.empty_like(q0)
     lse = torch.empty((1, H, n0), dtype=torch.float32, device=dev)
     flops = 4.0 * D * H * n0 * S
-    d_att = time_launches(torch, lambda: cp.attn_chunk_partial(
-        q0, kg, vg, o, lse, out_dtype=torch.bfloat16), 1, 5)
+    d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
+        q0, kg, vg, o, lse, out_dtype=torch.bfloat16), 1, 5)]
     res = {
         "rank_rows": n0, "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
@@ -533,8 +535,8 @@ def ring_anything_workload(torch, cp, synthetic, dev):
             s0, n = starts[r], w.chunk_lens[r]
             qr = q[:, s0:s0 + n].contiguous()
             vis = [chunks[c] for c in synthetic.ring_order(r, w.P)]
-            d = time_launches(torch, lambda: cp.ring_attention(qr, vis, causal=causal, q_pos0=s0),
-                              2, 10)
+            d = [time_back_to_back(
+                torch, lambda: cp.ring_attention(qr, vis, causal=causal, q_pos0=s0), 5, 50)]
             tot_us += median(d) * 1e3
             tot_flops += attn_flops(n, w.S, w.H, w.D, causal, s0, 0)
         res["causal" if causal else "noncausal"] = {
