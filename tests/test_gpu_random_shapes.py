@@ -1,0 +1,116 @@
+"""GPU parity on seeded random shapes: forward ring, per-hop partials + merge,
+and ring backward, against the fp64 oracle.
+
+Each case draws B, H, D in {64, 128}, ragged Sq and a key length split into a
+random number of chunks (empty chunks allowed), causal or not, with random
+query and key position offsets and a random ring visit order. The draws are
+seeded, so every run checks the same cases.
+
+Tolerances: LSE max-abs 1e-4, gradients as in the other backward tests. For
+bf16 outputs: max-abs <= 1e-2 * max(1, max|ref|) and
+mean-abs <= max(1e-3, 2^-7 * mean|ref|). With only a few visible keys O is
+close to single value rows (|O| up to ~4), and bf16 itself rounds such values
+by up to 2^-8 of their size (half a bf16 step is 0.0078 at |O| = 2; about a
+quarter step on average), before the 2^-8 rounding of P. The absolute bars
+(1e-2, 1e-3) hold for outputs well below 1, which is what averages over many
+keys give, as in every workload.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests._parity import BF16_MAX, BF16_MEAN, check_lse, say, to_f64
+from tests.test_gpu_backward import check_grad
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import context_attention_dit_amd as cp
+DEV = "cuda:0"
+
+N_CASES = 64
+
+
+def check_o_scaled(got, want, what):
+    g = to_f64(got)
+    assert g.shape == want.shape and not np.any(np.isnan(g)), what
+    err = np.abs(g - want)
+    big = max(1.0, float(np.abs(want).max()))
+    mean_bar = max(BF16_MEAN, 2.0 ** -7 * float(np.abs(want).mean()))
+    assert err.max() <= BF16_MAX * big, f"{what}: max-abs {err.max():.3e} > {BF16_MAX} * {big:.2f}"
+    assert err.mean() <= mean_bar, f"{what}: mean-abs {err.mean():.3e} > {mean_bar:.3e}"
+
+
+def _case(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    B = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 5))
+    D = int(rng.choice([64, 128]))
+    Sq = int(rng.integers(1, 300))
+    Skv = int(rng.integers(1, 400))
+    P = int(rng.integers(1, 6))
+    causal = bool(rng.integers(0, 2))
+    cuts = np.sort(rng.integers(0, Skv + 1, size=P - 1))
+    lens = tuple(int(x) for x in np.diff(np.concatenate([[0], cuts, [Skv]])))
+    q_pos0 = int(rng.integers(0, Skv + 64)) if causal else 0
+    kv_pos0 = int(rng.integers(0, 32)) if causal else 0
+    order = [int(x) for x in rng.permutation(P)]
+    return B, H, D, Sq, lens, causal, q_pos0, kv_pos0, order
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape_forward_and_backward(seed):
+    B, H, D, Sq, lens, causal, q_pos0, kv_pos0, order = _case(seed)
+    Skv = sum(lens)
+    say(f"random case {seed}: B={B} H={H} D={D} Sq={Sq} lens={lens} causal={causal} "
+        f"q_pos0={q_pos0} kv_pos0={kv_pos0} order={order}")
+    bf = torch.bfloat16
+    q = synthetic.make_tensor((B, Sq, H, D), bf, 20_000 + 4 * seed)
+    k = synthetic.make_tensor((B, Skv, H, D), bf, 20_001 + 4 * seed)
+    v = synthetic.make_tensor((B, Skv, H, D), bf, 20_002 + 4 * seed)
+    do = synthetic.make_tensor((B, Sq, H, D), bf, 20_003 + 4 * seed)
+    q64, k64, v64, do64 = (to_f64(x) for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    q_pos = np.arange(q_pos0, q_pos0 + Sq)
+    k_pos = np.arange(kv_pos0, kv_pos0 + Skv)
+    wo, wl = oracle.attention(q64, k64, v64, scale, causal, q_pos, k_pos)
+
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    kd, vd = k.to(DEV), v.to(DEV)
+    chunks = [(kd[:, s:s + m].contiguous(), vd[:, s:s + m].contiguous(), kv_pos0 + int(s))
+              for s, m in zip(starts, lens)]
+    visit = [chunks[c] for c in order]
+    qd, dod = q.to(DEV), do.to(DEV)
+    o, lse = cp.ring_attention(qd, visit, causal=causal, q_pos0=q_pos0)
+    parts = [cp.attn_chunk_partial(qd, kc, vc, causal=causal, q_pos0=q_pos0, kv_pos0=p0)
+             for kc, vc, p0 in visit]
+    mo, ml = cp.lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
+                          out_dtype=bf)
+    torch.cuda.synchronize()
+    check_o_scaled(o, wo, "ring O")
+    check_lse(lse, wl, "ring LSE")
+    check_o_scaled(mo, wo, "partials + merge O")
+    check_lse(ml, wl, "partials + merge LSE")
+
+    # backward of the same rank from the oracle's saved statistics
+    o_bf = torch.tensor(wo, dtype=torch.float32).to(bf).to(DEV)
+    delta = cp.attn_backward_delta(o_bf, dod)
+    dq, grads = cp.ring_attention_backward(qd, visit, dod,
+                                           torch.tensor(wl, dtype=torch.float32).to(DEV), delta,
+                                           causal=causal, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    # the kernel's contract: gradients for the Delta of the O it is given (the
+    # oracle's O rounded to bf16, as stored); with few keys O is not small and
+    # that rounding alone moves Delta by more than the kernel's own arithmetic
+    wq, wk, wv = oracle.chunk_grad(q64, k64, v64, do64, wl,
+                                   oracle.backward_delta(to_f64(o_bf), do64), scale, causal,
+                                   q_pos, k_pos)
+    check_grad(dq, wq, "dQ")
+    got_k = torch.cat([grads[order.index(c)][0] for c in range(len(lens))], dim=1)
+    got_v = torch.cat([grads[order.index(c)][1] for c in range(len(lens))], dim=1)
+    check_grad(got_k, wk, "dK")
+    check_grad(got_v, wv, "dV")
