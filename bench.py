@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-FLUSH_BYTES = 1 << 30         # written between timed launches of HBM-bound kernels
+ROTATE_BYTES = 1 << 30        # footprint of the buffer sets an HBM-bound kernel rotates over
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_flux_ring_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "context_attention_dit_amd", "csrc", "attn_bf16.hip")
 
@@ -55,26 +55,39 @@ def causal_pairs_square(S: int) -> int:
     return S * (S + 1) // 2
 
 
-def time_launches(torch, fn, warmup: int, iters: int, flush=None):
-    """Per-launch durations (ms) from HIP events on the current stream, each launch
-    bracketed on its own (used with `flush` for the HBM-bound kernels, so that each
-    launch starts from cold caches)."""
+def buffer_sets(bytes_per_launch: int) -> int:
+    """Buffer sets to rotate over so that a launch never finds its operands in
+    the caches: together they span ROTATE_BYTES (4x the 256 MB last-level cache
+    and the L2s), and there are at least two."""
+    return max(2, math.ceil(ROTATE_BYTES / max(1, bytes_per_launch)))
+
+
+def rotating_pairs(x, out_like, nbytes: int):
+    """(input, output) buffer sets for an HBM-bound transform of `x`: copies of
+    the input and fresh outputs shaped like `out_like`, enough of them that
+    they span ROTATE_BYTES together."""
+    return [(x.clone(), out_like.new_empty(out_like.shape)) for _ in range(buffer_sets(nbytes))]
+
+
+def time_rotating(torch, fns, warmup: int, rounds: int) -> float:
+    """Mean ms per launch of an HBM-bound kernel, issued back to back over
+    `rounds` passes through `fns` (one closure per buffer set) between one pair
+    of HIP events. Each launch reads operands last touched a full rotation
+    earlier, so they come from HBM, and there is no per-launch event or cache
+    flush in the timed region."""
     for _ in range(warmup):
-        fn()
+        for f in fns:
+            f()
     torch.cuda.synchronize()
-    durs = []
-    for _ in range(iters):
-        if flush is not None:
-            flush()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        b.synchronize()
-        durs.append(a.elapsed_time(b))
-    durs.sort()
-    return durs
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(rounds):
+        for f in fns:
+            f()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / (rounds * len(fns))
 
 
 def time_back_to_back(torch, fn, warmup: int, iters: int) -> float:
@@ -180,11 +193,6 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copied 256 MiB x 5 (read 268435456 B, write 268435456 B per launch)")
         return 0
-    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-
-    def flush():
-        flush_buf.fill_(1.0)
-
     # ---------------------------------------------------------------- headline
     w = synthetic.FLUX_RING
     log(f"{w.name}: inputs")
@@ -228,8 +236,7 @@ def main() -> int:
     detail = {"flux_ring_rank0": {"us_per_step": ms_step * 1e3, "kernel_us": launch_ms * 1e3,
                                   "tflops": achieved, "gflop": flops / 1e9}}
     if not args.quick:
-        detail.update(other_workloads(torch, cp, synthetic, dev, flush, q0, vis, w, args.only))
-    del flush_buf
+        detail.update(other_workloads(torch, cp, synthetic, dev, q0, vis, w, args.only))
 
     traffic = traffic_record()
     line = {
@@ -256,24 +263,23 @@ def main() -> int:
     return 0
 
 
-def other_workloads(torch, cp, synthetic, dev, flush, q0, vis, wf, only=None):
+def other_workloads(torch, cp, synthetic, dev, q0, vis, wf, only=None):
     out = {}
     want = (lambda tag: only is None or only == tag)
     # standalone merge of the FLUX ring's 4 fp32 partials (HBM-bound)
     if want("merge"):
-        out.update(merge_workload(torch, cp, dev, flush, q0, vis, wf))
+        out.update(merge_workload(torch, cp, dev, q0, vis, wf))
     tags = {synthetic.QWEN_ULYSSES.name: "qwen", synthetic.WAN_ULYSSES.name: "wan",
             synthetic.LLM_ULYSSES.name: "llm"}
     for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
         if want(tags[w.name]):
-            out[w.name] = ulysses_workload(torch, cp, synthetic, dev, flush, w)
+            out[w.name] = ulysses_workload(torch, cp, synthetic, dev, w)
     if want("ra"):
         out[synthetic.LLM_RING_ANYTHING.name] = ring_anything_workload(torch, cp, synthetic, dev)
     if want("anything"):
-        out[synthetic.FLUX_ANYTHING.name] = ulysses_anything_workload(torch, cp, synthetic, dev,
-                                                                      flush)
+        out[synthetic.FLUX_ANYTHING.name] = ulysses_anything_workload(torch, cp, synthetic, dev)
     if want("kvgather"):
-        out[synthetic.WAN_KV_GATHER.name] = kv_gather_workload(torch, cp, synthetic, dev, flush)
+        out[synthetic.WAN_KV_GATHER.name] = kv_gather_workload(torch, cp, synthetic, dev)
     if want("unified"):
         out[synthetic.FLUX_UNIFIED.name] = unified_workload(torch, cp, synthetic, dev)
     if want("bwd"):
@@ -335,7 +341,7 @@ def backward_workloads(torch, cp, synthetic, dev, q0, vis, wf):
     return out
 
 
-def merge_workload(torch, cp, dev, flush, q0, vis, wf):
+def merge_workload(torch, cp, dev, q0, vis, wf):
     out = {}
     parts = [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis]
     po = torch.stack([p[0] for p in parts])
@@ -345,24 +351,31 @@ def merge_workload(torch, cp, dev, flush, q0, vis, wf):
     ml = torch.empty((1, wf.H, q0.shape[1]), dtype=torch.float32, device=dev)
     P, B, Sq, H, D = po.shape
     mbytes = P * (Sq * H * D * 4 + Sq * H * 4) + Sq * H * D * 2 + Sq * H * 4
-    d = time_launches(torch, lambda: cp.lse_merge(po, pl, mo, ml), 3, 20, flush)
-    out["flux_lse_merge"] = {"us": median(d) * 1e3, "gbs": mbytes / (median(d) * 1e-3) / 1e9,
-                             "bytes": mbytes,
-                             "hbm_frac": mbytes / (median(d) * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    sets = [(po.clone(), pl.clone(), torch.empty_like(mo), torch.empty_like(ml))
+            for _ in range(buffer_sets(mbytes))]
+    d = time_rotating(torch, [lambda s=s: cp.lse_merge(*s) for s in sets], 1, 10)
+    del sets
+    out["flux_lse_merge"] = {"us": d * 1e3, "gbs": mbytes / (d * 1e-3) / 1e9, "bytes": mbytes,
+                             "hbm_frac": mbytes / (d * 1e-3) / 1e9 / PEAK_HBM_GBS}
     ms = time_back_to_back(torch, lambda: [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis],
                            3, 20)
     out["flux_partials_x4"] = {"us": ms * 1e3}
     return out
 
 
-def ulysses_workload(torch, cp, synthetic, dev, flush, w):
+def ulysses_workload(torch, cp, synthetic, dev, w):
     log(f"{w.name}: inputs")
     P, S_l, H, D = w.P, w.S_local, w.H, w.D
     qkv = [x.view(P, 1, S_l, H, D).to(dev) for x in synthetic.make_qkv(w)]
     heads = [torch.empty((P, 1, w.S, w.H_local, D), dtype=w.dtype, device=dev) for _ in qkv]
     nbytes = qkv[0].numel() * qkv[0].element_size() * 2    # read + write, one tensor
-    d_s2h = time_launches(torch, lambda: cp.ulysses_seq2head(qkv[0], P, heads[0]), 2, 10,
-                          flush)
+    pairs = rotating_pairs(qkv[0], heads[0], nbytes)
+    d_s2h = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_seq2head(x, P, y)
+                                  for x, y in pairs], 1, 5)
+    # head2seq over the same sets, from head layout back into the sequence copies
+    d_h2s = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_head2seq(y, P, x)
+                                  for x, y in pairs], 1, 5)
+    del pairs
     for x, y in zip(qkv, heads):
         cp.ulysses_seq2head(x, P, y)
     rq, rk, rv = (y[0] for y in heads)
@@ -372,37 +385,39 @@ def ulysses_workload(torch, cp, synthetic, dev, flush, w):
     reps = 3 if w.causal else 10
     d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
         rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)]
-    back = torch.empty_like(qkv[0])
-    d_h2s = time_launches(torch, lambda: cp.ulysses_head2seq(heads[1], P, back), 2, 10, flush)
+    del o, lse
     # the rank's Q, K and V regrouped together in one launch (stacked tensors)
     qkv3 = torch.stack(qkv)
     heads3 = torch.empty((3,) + tuple(heads[0].shape), dtype=w.dtype, device=dev)
-    d_s2h3 = time_launches(torch, lambda: cp.ulysses_seq2head(qkv3, P, heads3), 2, 10, flush)
+    pairs = rotating_pairs(qkv3, heads3, 3 * nbytes)
     del qkv3, heads3
+    d_s2h3 = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_seq2head(x, P, y)
+                                   for x, y in pairs], 1, 5)
+    del pairs
     res = {
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "seq2head_us": median(d_s2h) * 1e3,
-        "seq2head_gbs": nbytes / (median(d_s2h) * 1e-3) / 1e9,
-        "head2seq_us": median(d_h2s) * 1e3,
-        "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
+        "seq2head_us": d_s2h * 1e3,
+        "seq2head_gbs": nbytes / (d_s2h * 1e-3) / 1e9,
+        "head2seq_us": d_h2s * 1e3,
+        "head2seq_gbs": nbytes / (d_h2s * 1e-3) / 1e9,
         "relayout_bytes_per_tensor": nbytes,
-        "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "seq2head_qkv_us": median(d_s2h3) * 1e3,
-        "seq2head_qkv_gbs": 3 * nbytes / (median(d_s2h3) * 1e-3) / 1e9,
-        "seq2head_qkv_hbm_frac": 3 * nbytes / (median(d_s2h3) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "relayout_hbm_frac": nbytes / (d_s2h * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "seq2head_qkv_us": d_s2h3 * 1e3,
+        "seq2head_qkv_gbs": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9,
+        "seq2head_qkv_hbm_frac": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "causal": w.causal, "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
         f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}")
-    del qkv, heads, rq, rk, rv, o, lse, back
+    del qkv, heads, rq, rk, rv
     torch.cuda.empty_cache()
     return res
 
 
-def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
+def ulysses_anything_workload(torch, cp, synthetic, dev):
     """FLUX 1008x1008 over a Ulysses degree of 4 with uneven shards (Ulysses Anything)."""
     w = synthetic.FLUX_ANYTHING
     log(f"{w.name}: inputs")
@@ -410,8 +425,12 @@ def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
     qkv = [x.to(dev).reshape(-1) for x in synthetic.make_qkv(w)]
     groups = [torch.empty_like(x) for x in qkv]
     nbytes = qkv[0].numel() * qkv[0].element_size() * 2
-    d_s2h = time_launches(torch, lambda: cp.ulysses_anything_seq2head(
-        qkv[0], s_lens, h_counts, 1, D, groups[0]), 2, 10, flush)
+    pairs = rotating_pairs(qkv[0], groups[0], nbytes)
+    d_s2h = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_anything_seq2head(
+        x, s_lens, h_counts, 1, D, y) for x, y in pairs], 1, 5)
+    d_h2s = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_anything_head2seq(
+        y, s_lens, h_counts, 1, D, x) for x, y in pairs], 1, 5)
+    del pairs
     for x, y in zip(qkv, groups):
         cp.ulysses_anything_seq2head(x, s_lens, h_counts, 1, D, y)
     h0 = h_counts[0]
@@ -421,18 +440,17 @@ def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
     flops = 4.0 * D * h0 * S * S
     d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
         rq, rk, rv, o, lse, out_dtype=torch.bfloat16), 5, 50)]
-    back = torch.empty_like(qkv[0])
-    d_h2s = time_launches(torch, lambda: cp.ulysses_anything_head2seq(
-        groups[1], s_lens, h_counts, 1, D, back), 2, 10, flush)
     res = {
         "seq_split": s_lens, "head_split": h_counts,
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "seq2head_gbs": nbytes / (median(d_s2h) * 1e-3) / 1e9,
-        "head2seq_gbs": nbytes / (median(d_h2s) * 1e-3) / 1e9,
+        "seq2head_us": d_s2h * 1e3,
+        "seq2head_gbs": nbytes / (d_s2h * 1e-3) / 1e9,
+        "head2seq_us": d_h2s * 1e3,
+        "head2seq_gbs": nbytes / (d_h2s * 1e-3) / 1e9,
         "relayout_bytes_per_tensor": nbytes,
-        "relayout_hbm_frac": nbytes / (median(d_s2h) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "relayout_hbm_frac": nbytes / (d_s2h * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
@@ -440,7 +458,7 @@ def ulysses_anything_workload(torch, cp, synthetic, dev, flush):
     return res
 
 
-def kv_gather_workload(torch, cp, synthetic, dev, flush):
+def kv_gather_workload(torch, cp, synthetic, dev):
     """Wan over a K/V-gather degree of 4: rank 0's query shard over the gathered K/V."""
     w = synthetic.WAN_KV_GATHER
     log(f"{w.name}: inputs")
@@ -448,8 +466,10 @@ def kv_gather_workload(torch, cp, synthetic, dev, flush):
     q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
     kg = torch.empty_like(k)
     nbytes = k.numel() * k.element_size() * 2
-    d_g = time_launches(torch, lambda: cp.kv_gather(k.reshape(-1), lens, 1, H, D, kg), 2, 10,
-                        flush)
+    pairs = rotating_pairs(k.reshape(-1), kg, nbytes)
+    d_g = time_rotating(torch, [lambda x=x, y=y: cp.kv_gather(x, lens, 1, H, D, y)
+                                for x, y in pairs], 1, 5)
+    del pairs
     vg = cp.kv_gather(v.reshape(-1), lens, 1, H, D)
     n0 = lens[0]
     q0 = q[:, :n0].contiguous()
@@ -462,8 +482,9 @@ def kv_gather_workload(torch, cp, synthetic, dev, flush):
         "rank_rows": n0, "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "gather_gbs": nbytes / (median(d_g) * 1e-3) / 1e9,
-        "gather_hbm_frac": nbytes / (median(d_g) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "gather_us": d_g * 1e3,
+        "gather_gbs": nbytes / (d_g * 1e-3) / 1e9,
+        "gather_hbm_frac": nbytes / (d_g * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "gather_bytes_per_tensor": nbytes, "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, gather {res['gather_gbs']:.0f} GB/s")
