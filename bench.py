@@ -431,6 +431,13 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
     d_h2s = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_anything_head2seq(
         y, s_lens, h_counts, 1, D, x) for x, y in pairs], 1, 5)
     del pairs
+    # the rank's Q, K and V regrouped in one launch (stacked tensors)
+    qkv3 = torch.stack(qkv)
+    pairs = rotating_pairs(qkv3, qkv3, 3 * nbytes)
+    del qkv3
+    d_s2h3 = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_anything_seq2head(
+        x, s_lens, h_counts, 1, D, y) for x, y in pairs], 1, 5)
+    del pairs
     for x, y in zip(qkv, groups):
         cp.ulysses_anything_seq2head(x, s_lens, h_counts, 1, D, y)
     h0 = h_counts[0]
@@ -451,10 +458,14 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
         "head2seq_gbs": nbytes / (d_h2s * 1e-3) / 1e9,
         "relayout_bytes_per_tensor": nbytes,
         "relayout_hbm_frac": nbytes / (d_s2h * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "seq2head_qkv_us": d_s2h3 * 1e3,
+        "seq2head_qkv_gbs": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9,
+        "seq2head_qkv_hbm_frac": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
-        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}")
+        f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
+        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}")
     return res
 
 
@@ -469,7 +480,14 @@ def kv_gather_workload(torch, cp, synthetic, dev):
     pairs = rotating_pairs(k.reshape(-1), kg, nbytes)
     d_g = time_rotating(torch, [lambda x=x, y=y: cp.kv_gather(x, lens, 1, H, D, y)
                                 for x, y in pairs], 1, 5)
+    # K and V gathered in one launch (stacked)
+    kv2 = torch.stack([k.reshape(-1), v.reshape(-1)])
+    pairs = rotating_pairs(kv2, torch.stack([kg, kg]), 2 * nbytes)
+    del kv2
+    d_g2 = time_rotating(torch, [lambda x=x, y=y: cp.kv_gather(x, lens, 1, H, D, y)
+                                 for x, y in pairs], 1, 5)
     del pairs
+    cp.kv_gather(k.reshape(-1), lens, 1, H, D, kg)
     vg = cp.kv_gather(v.reshape(-1), lens, 1, H, D)
     n0 = lens[0]
     q0 = q[:, :n0].contiguous()
@@ -485,9 +503,13 @@ def kv_gather_workload(torch, cp, synthetic, dev):
         "gather_us": d_g * 1e3,
         "gather_gbs": nbytes / (d_g * 1e-3) / 1e9,
         "gather_hbm_frac": nbytes / (d_g * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "gather_kv_us": d_g2 * 1e3,
+        "gather_kv_gbs": 2 * nbytes / (d_g2 * 1e-3) / 1e9,
+        "gather_kv_hbm_frac": 2 * nbytes / (d_g2 * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "gather_bytes_per_tensor": nbytes, "gflop": flops / 1e9,
     }
-    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, gather {res['gather_gbs']:.0f} GB/s")
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, gather {res['gather_gbs']:.0f} GB/s, "
+        f"K+V in one launch {res['gather_kv_gbs']:.0f}")
     del q, k, v, kg, vg, q0, o, lse
     torch.cuda.empty_cache()
     return res

@@ -78,7 +78,12 @@ _any_seq2head = _sig("cp_ulysses_anything_seq2head",
                      [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
 _any_head2seq = _sig("cp_ulysses_anything_head2seq",
                      [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _vp])
+_any_seq2head_n = _sig("cp_ulysses_anything_seq2head_n",
+                       [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _int, _vp])
+_any_head2seq_n = _sig("cp_ulysses_anything_head2seq_n",
+                       [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _int, _vp])
 _kv_gather = _sig("cp_kv_gather", [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _vp])
+_kv_gather_n = _sig("cp_kv_gather_n", [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _int, _vp])
 _bwd_delta = _sig("cp_attn_backward_delta", [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp])
 _chunk_bwd = _sig("cp_attn_chunk_backward", [_vp] * 9 + [_i64] * 5 +
                   [_int, _f32, _int, _i64, _i64, _int, _vp])
@@ -132,6 +137,17 @@ def _stream(stream: Optional[torch.cuda.Stream]) -> int:
     return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
 
 
+def _want(t: torch.Tensor, name: str, shape, dtype, device) -> torch.Tensor:
+    """A buffer the library reads or writes as `shape` elements of `dtype`: the
+    C ABI sees only its address, so its size, type and device are checked here."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, "
+                         f"got {t.dtype} of shape {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
 def _bshd(x: torch.Tensor, name: str) -> Tuple[int, int, int, int]:
     if x.dim() != 4:
         raise ValueError(f"{name} must be [B][S][H][D], got shape {tuple(x.shape)}")
@@ -150,10 +166,14 @@ def attn_chunk_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("q, k, v shapes disagree")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
+    _want(k, "k", k.shape, q.dtype, q.device)
+    _want(v, "v", k.shape, q.dtype, q.device)
     if o is None:
         o = torch.empty((B, Sq, H, D), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _want(o, "o", (B, Sq, H, D), o.dtype, q.device)
+    _want(lse, "lse", (B, H, Sq), torch.float32, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check("cp_attn_chunk_partial", _chunk_partial(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Skv, D, _dtype_code(q.dtype),
@@ -172,10 +192,13 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: Optional[torch.
         raise ValueError("lse_parts shape disagrees with o_parts")
     if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
         raise TypeError("partials must be float32")
+    _want(lse_parts, "lse_parts", (P, B, H, Sq), torch.float32, o_parts.device)
     if o is None:
         o = torch.empty((B, Sq, H, D), dtype=out_dtype, device=o_parts.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=o_parts.device)
+    _want(o, "o", (B, Sq, H, D), o.dtype, o_parts.device)
+    _want(lse, "lse", (B, H, Sq), torch.float32, o_parts.device)
     _check("cp_lse_merge", _lse_merge(_ptr(o_parts), _ptr(lse_parts), P, _ptr(o), _ptr(lse), B, H,
                                       Sq, D, _dtype_code(o.dtype), _stream(stream)))
     return o, lse
@@ -202,14 +225,21 @@ def ring_attention(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.T
             raise ValueError(f"chunk {c} shape disagrees with q")
         if k.dtype != q.dtype or v.dtype != q.dtype:
             raise TypeError(f"chunk {c} dtype disagrees with q")
-        arr[c] = KVChunk(_ptr(k), _ptr(v), L, int(pos0))
+        _want(k, f"chunk {c} k", k.shape, q.dtype, q.device)
+        _want(v, f"chunk {c} v", k.shape, q.dtype, q.device)
     if o is None:
         o = torch.empty((B, Sq, H, D), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _want(o, "o", (B, Sq, H, D), q.dtype, q.device)
+    _want(lse, "lse", (B, H, Sq), torch.float32, q.device)
+    for c, (k, v, pos0) in enumerate(chunks):
+        arr[c] = KVChunk(_ptr(k), _ptr(v), k.shape[1], int(pos0))
     need = ring_attention_workspace_bytes(len(chunks), B, H, Sq, D)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError(f"workspace must be on {q.device}")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check("cp_ring_attention", _ring(
@@ -231,6 +261,7 @@ def ulysses_seq2head(x: torch.Tensor, P: int, out: Optional[torch.Tensor] = None
     lead = tuple(x.shape[:-5])
     if out is None:
         out = torch.empty(lead + (P, B, P * S_l, H // P, D), dtype=x.dtype, device=x.device)
+    _want(out, "out", lead + (P, B, P * S_l, H // P, D), x.dtype, x.device)
     if x.dim() == 6:
         _check("cp_ulysses_seq2head_n", _seq2head_n(_ptr(x), _ptr(out), x.shape[0], P, B, S_l,
                                                     H, D, _dtype_code(x.dtype), _stream(stream)))
@@ -252,6 +283,7 @@ def ulysses_head2seq(y: torch.Tensor, P: int, out: Optional[torch.Tensor] = None
     lead = tuple(y.shape[:-5])
     if out is None:
         out = torch.empty(lead + (P, B, S // P, H_l * P, D), dtype=y.dtype, device=y.device)
+    _want(out, "out", lead + (P, B, S // P, H_l * P, D), y.dtype, y.device)
     if y.dim() == 6:
         _check("cp_ulysses_head2seq_n", _head2seq_n(_ptr(y), _ptr(out), y.shape[0], P, B, S // P,
                                                     H_l * P, D, _dtype_code(y.dtype),
@@ -267,18 +299,32 @@ def _counts(xs):
     return arr, ctypes.cast(arr, ctypes.c_void_p)
 
 
-def _anything(name, fn, x, s_lens, h_counts, B, D, out, stream):
+def _packed(x: torch.Tensor, n: int) -> int:
+    """Tensor count of a packed input: 1 for a flat tensor of n elements, or
+    the leading size of a 2-D [count][n] stack."""
+    if not x.is_contiguous() or x.dim() not in (1, 2) or x.shape[-1] != n:
+        raise ValueError(f"expected a contiguous packed tensor of {n} elements, or a 2-D "
+                         f"[count][{n}] stack of them")
+    return 1 if x.dim() == 1 else x.shape[0]
+
+
+def _anything(names, fns, x, s_lens, h_counts, B, D, out, stream):
     P = len(s_lens)
     if len(h_counts) != P:
         raise ValueError("s_lens and h_counts need one entry per rank")
     n = B * sum(s_lens) * sum(h_counts) * D
-    if not x.is_contiguous() or x.numel() != n:
-        raise ValueError(f"expected a contiguous packed tensor of {n} elements")
+    count = _packed(x, n)
     if out is None:
-        out = torch.empty(n, dtype=x.dtype, device=x.device)
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    _want(out, "out", x.shape, x.dtype, x.device)
     sa, sp = _counts(s_lens)
     ha, hp = _counts(h_counts)
-    _check(name, fn(_ptr(x), _ptr(out), P, B, sp, hp, D, _dtype_code(x.dtype), _stream(stream)))
+    if x.dim() == 2:
+        _check(names[1], fns[1](_ptr(x), _ptr(out), count, P, B, sp, hp, D, _dtype_code(x.dtype),
+                                _stream(stream)))
+    else:
+        _check(names[0], fns[0](_ptr(x), _ptr(out), P, B, sp, hp, D, _dtype_code(x.dtype),
+                                _stream(stream)))
     return out
 
 
@@ -286,32 +332,41 @@ def ulysses_anything_seq2head(x: torch.Tensor, s_lens, h_counts, B: int, D: int,
                               out: Optional[torch.Tensor] = None, *, stream=None) -> torch.Tensor:
     """Packed sequence shards (shard q = [B][s_lens[q]][H][D]) -> packed head
     groups (group p = [B][S][h_counts[p]][D]); see cp_ulysses_anything_seq2head.
-    Returns a flat tensor of B*S*H*D elements."""
-    return _anything("cp_ulysses_anything_seq2head", _any_seq2head, x, s_lens, h_counts, B, D,
-                     out, stream)
+    Returns a flat tensor of B*S*H*D elements. A 2-D ``x`` of shape
+    ``[n][B*S*H*D]`` (a rank's Q, K and V, say) is regrouped tensor by tensor in
+    one launch (cp_ulysses_anything_seq2head_n)."""
+    return _anything(("cp_ulysses_anything_seq2head", "cp_ulysses_anything_seq2head_n"),
+                     (_any_seq2head, _any_seq2head_n), x, s_lens, h_counts, B, D, out, stream)
 
 
 def ulysses_anything_head2seq(y: torch.Tensor, s_lens, h_counts, B: int, D: int,
                               out: Optional[torch.Tensor] = None, *, stream=None) -> torch.Tensor:
     """Packed head groups -> packed sequence shards; the inverse of
-    ulysses_anything_seq2head (see cp_ulysses_anything_head2seq)."""
-    return _anything("cp_ulysses_anything_head2seq", _any_head2seq, y, s_lens, h_counts, B, D,
-                     out, stream)
+    ulysses_anything_seq2head (see cp_ulysses_anything_head2seq). A 2-D ``y``
+    is a stack of such inputs (cp_ulysses_anything_head2seq_n)."""
+    return _anything(("cp_ulysses_anything_head2seq", "cp_ulysses_anything_head2seq_n"),
+                     (_any_head2seq, _any_head2seq_n), y, s_lens, h_counts, B, D, out, stream)
 
 
 def kv_gather(x: torch.Tensor, s_lens, B: int, H: int, D: int,
               out: Optional[torch.Tensor] = None, *, stream=None) -> torch.Tensor:
     """Packed sequence shards (shard q = [B][s_lens[q]][H][D]) -> the gathered
-    [B][S][H][D] tensor; see cp_kv_gather."""
+    [B][S][H][D] tensor; see cp_kv_gather. A 2-D ``x`` of shape
+    ``[n][B*S*H*D]`` (K and V, say) gives ``[n][B][S][H][D]`` in one launch
+    (cp_kv_gather_n)."""
     S = sum(s_lens)
-    n = B * S * H * D
-    if not x.is_contiguous() or x.numel() != n:
-        raise ValueError(f"expected a contiguous packed tensor of {n} elements")
+    count = _packed(x, B * S * H * D)
+    lead = (count,) if x.dim() == 2 else ()
     if out is None:
-        out = torch.empty((B, S, H, D), dtype=x.dtype, device=x.device)
+        out = torch.empty(lead + (B, S, H, D), dtype=x.dtype, device=x.device)
+    _want(out, "out", lead + (B, S, H, D), x.dtype, x.device)
     sa, sp = _counts(s_lens)
-    _check("cp_kv_gather", _kv_gather(_ptr(x), _ptr(out), len(s_lens), B, sp, H, D,
-                                      _dtype_code(x.dtype), _stream(stream)))
+    if x.dim() == 2:
+        _check("cp_kv_gather_n", _kv_gather_n(_ptr(x), _ptr(out), count, len(s_lens), B, sp, H,
+                                              D, _dtype_code(x.dtype), _stream(stream)))
+    else:
+        _check("cp_kv_gather", _kv_gather(_ptr(x), _ptr(out), len(s_lens), B, sp, H, D,
+                                          _dtype_code(x.dtype), _stream(stream)))
     return out
 
 
@@ -321,8 +376,10 @@ def attn_backward_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[tor
     B, Sq, H, D = _bshd(o, "o")
     if tuple(dout.shape) != tuple(o.shape) or dout.dtype != o.dtype:
         raise ValueError("o and dout must share shape and dtype")
+    _want(dout, "dout", o.shape, o.dtype, o.device)
     if delta is None:
         delta = torch.empty((B, H, Sq), dtype=torch.float32, device=o.device)
+    _want(delta, "delta", (B, H, Sq), torch.float32, o.device)
     _check("cp_attn_backward_delta", _bwd_delta(_ptr(o), _ptr(dout), _ptr(delta), B, H, Sq, D,
                                                 _dtype_code(o.dtype), _stream(stream)))
     return delta
@@ -348,6 +405,13 @@ def attn_chunk_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout:
         raise ValueError("dout must have q's shape")
     if tuple(lse.shape) != (B, H, Sq) or tuple(delta.shape) != (B, H, Sq):
         raise ValueError("lse and delta must be [B][H][Sq]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for name, t, shape, dt in (("k", k, k.shape, q.dtype), ("v", v, k.shape, q.dtype),
+                               ("dout", dout, q.shape, q.dtype),
+                               ("lse", lse, (B, H, Sq), torch.float32),
+                               ("delta", delta, (B, H, Sq), torch.float32)):
+        _want(t, name, shape, dt, q.device)
     if (accumulate_dq and dq is None) or (accumulate_dkv and (dk is None or dv is None)):
         raise ValueError("accumulating needs the running-sum buffers")
     f32 = torch.float32
@@ -355,8 +419,7 @@ def attn_chunk_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout:
     dk = torch.empty((B, Skv, H, D), dtype=f32, device=q.device) if dk is None else dk
     dv = torch.empty((B, Skv, H, D), dtype=f32, device=q.device) if dv is None else dv
     for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
-        if t.dtype != f32 or tuple(t.shape) != tuple(shape):
-            raise ValueError(f"{name} must be float32 of shape {tuple(shape)}")
+        _want(t, name, shape, f32, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     flags = (BWD_ACCUMULATE_DQ if accumulate_dq else 0) | \
         (BWD_ACCUMULATE_DKV if accumulate_dkv else 0)
@@ -381,6 +444,10 @@ def ring_attention_backward(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor
         raise ValueError("dout must have q's shape")
     if tuple(lse.shape) != (B, H, Sq) or tuple(delta.shape) != (B, H, Sq):
         raise ValueError("lse and delta must be [B][H][Sq]")
+    for name, t, shape, dt in (("dout", dout, q.shape, q.dtype),
+                               ("lse", lse, (B, H, Sq), torch.float32),
+                               ("delta", delta, (B, H, Sq), torch.float32)):
+        _want(t, name, shape, dt, q.device)
     if (accumulate_dq and dq is None) or (accumulate_dkv and grads is None):
         raise ValueError("accumulating needs the running-sum buffers")
     f32 = torch.float32
@@ -399,13 +466,13 @@ def ring_attention_backward(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor
             raise ValueError(f"chunk {c} shape disagrees with q")
         if k.dtype != q.dtype or v.dtype != q.dtype:
             raise TypeError(f"chunk {c} dtype disagrees with q")
+        _want(k, f"chunk {c} k", k.shape, q.dtype, q.device)
+        _want(v, f"chunk {c} v", k.shape, q.dtype, q.device)
         for name, t in (("dk", dk), ("dv", dv)):
-            if t.dtype != f32 or tuple(t.shape) != tuple(k.shape):
-                raise ValueError(f"chunk {c} {name} must be float32 of shape {tuple(k.shape)}")
+            _want(t, f"chunk {c} {name}", k.shape, f32, q.device)
         arr[c] = KVChunk(_ptr(k), _ptr(v), L, int(pos0))
         garr[c] = KVGrad(_ptr(dk), _ptr(dv))
-    if dq.dtype != f32 or tuple(dq.shape) != (B, Sq, H, D):
-        raise ValueError("dq must be float32 of q's shape")
+    _want(dq, "dq", (B, Sq, H, D), f32, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     flags = (BWD_ACCUMULATE_DQ if accumulate_dq else 0) | \
         (BWD_ACCUMULATE_DKV if accumulate_dkv else 0)

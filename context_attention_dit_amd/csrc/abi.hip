@@ -331,9 +331,12 @@ cp_status cp_ulysses_head2seq_n(const void* in, void* out, int64_t count, int64_
                   false);
 }
 
-static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t P, int64_t B,
-                              const int64_t* s_lens, const int64_t* h_counts, int64_t D,
-                              cp_dtype dtype, void* stream, bool seq2head) {
+static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t count,
+                              int64_t P, int64_t B, const int64_t* s_lens,
+                              const int64_t* h_counts, int64_t D, cp_dtype dtype, void* stream,
+                              bool seq2head) {
+  if (count < 1) return fail(CP_E_INVALID, "%s: count must be >= 1", fn);
+  if (count > 65535) return fail(CP_E_UNSUPPORTED, "%s: count exceeds 65535", fn);
   if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
   if (P > CP_MAX_RING_CHUNKS)
     return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d ranks", fn, (long long)P,
@@ -356,6 +359,7 @@ static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t
   d.H = d.h_off[P];
   d.D = D;
   d.seq2head = seq2head;
+  d.count = count;
   if (B == 0 || d.S == 0 || d.H == 0 || D == 0) return ok();
   if (!in || !out) return fail(CP_E_INVALID, "%s: null pointer", fn);
   const int es = elem_size(dtype);
@@ -363,10 +367,12 @@ static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t
   if (!aligned(in, es) || !aligned(out, es))
     return fail(CP_E_INVALID, "%s: pointer not aligned to the element size", fn);
   const int64_t bytes = sat_mul({B, d.S, d.H, D, es});
-  if (overlap(in, bytes, out, bytes)) return fail(CP_E_INVALID, "%s: out overlaps in", fn);
-  // one launch: every (rank pair, batch) block of words, and all offsets, fit 32 bits
+  const int64_t all_bytes = sat_mul({count, bytes});
+  if (overlap(in, all_bytes, out, all_bytes))
+    return fail(CP_E_INVALID, "%s: out overlaps in", fn);
+  // one launch: every (rank pair, batch, tensor) block of words, and all offsets, fit 32 bits
   const int w = cpattn::any_relayout_word_bytes(in, out, d);
-  if (B >= 65536 || sat_mul({d.S, d.H, D, es}) / w >= (int64_t(1) << 32) ||
+  if (sat_mul({B, count}) >= 65536 || sat_mul({d.S, d.H, D, es}) / w >= (int64_t(1) << 32) ||
       sat_mul({B, d.S, d.H}) >= (int64_t(1) << 32))
     return fail(CP_E_UNSUPPORTED, "%s: tensor of %lld bytes too large for one launch", fn,
                 (long long)bytes);
@@ -376,20 +382,36 @@ static cp_status any_relayout(const char* fn, const void* in, void* out, int64_t
 cp_status cp_ulysses_anything_seq2head(const void* in, void* out, int64_t P, int64_t B,
                                        const int64_t* s_lens, const int64_t* h_counts, int64_t D,
                                        cp_dtype dtype, void* stream) {
-  return any_relayout("cp_ulysses_anything_seq2head", in, out, P, B, s_lens, h_counts, D, dtype,
-                      stream, true);
+  return any_relayout("cp_ulysses_anything_seq2head", in, out, 1, P, B, s_lens, h_counts, D,
+                      dtype, stream, true);
 }
 
 cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int64_t B,
                                        const int64_t* s_lens, const int64_t* h_counts, int64_t D,
                                        cp_dtype dtype, void* stream) {
-  return any_relayout("cp_ulysses_anything_head2seq", in, out, P, B, s_lens, h_counts, D, dtype,
-                      stream, false);
+  return any_relayout("cp_ulysses_anything_head2seq", in, out, 1, P, B, s_lens, h_counts, D,
+                      dtype, stream, false);
 }
 
-cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const int64_t* s_lens,
-                       int64_t H, int64_t D, cp_dtype dtype, void* stream) {
-  const char* fn = "cp_kv_gather";
+cp_status cp_ulysses_anything_seq2head_n(const void* in, void* out, int64_t count, int64_t P,
+                                         int64_t B, const int64_t* s_lens,
+                                         const int64_t* h_counts, int64_t D, cp_dtype dtype,
+                                         void* stream) {
+  return any_relayout("cp_ulysses_anything_seq2head_n", in, out, count, P, B, s_lens, h_counts,
+                      D, dtype, stream, true);
+}
+
+cp_status cp_ulysses_anything_head2seq_n(const void* in, void* out, int64_t count, int64_t P,
+                                         int64_t B, const int64_t* s_lens,
+                                         const int64_t* h_counts, int64_t D, cp_dtype dtype,
+                                         void* stream) {
+  return any_relayout("cp_ulysses_anything_head2seq_n", in, out, count, P, B, s_lens, h_counts,
+                      D, dtype, stream, false);
+}
+
+static cp_status kv_gather(const char* fn, const void* in, void* out, int64_t count, int64_t P,
+                           int64_t B, const int64_t* s_lens, int64_t H, int64_t D, cp_dtype dtype,
+                           void* stream) {
   if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
   if (P > CP_MAX_RING_CHUNKS)
     return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d ranks", fn, (long long)P,
@@ -398,7 +420,18 @@ cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const in
   // one destination group holding every head
   int64_t h_counts[CP_MAX_RING_CHUNKS] = {0};
   h_counts[0] = H;
-  return any_relayout(fn, in, out, P, B, s_lens, h_counts, D, dtype, stream, true);
+  return any_relayout(fn, in, out, count, P, B, s_lens, h_counts, D, dtype, stream, true);
+}
+
+cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const int64_t* s_lens,
+                       int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  return kv_gather("cp_kv_gather", in, out, 1, P, B, s_lens, H, D, dtype, stream);
+}
+
+cp_status cp_kv_gather_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,
+                         const int64_t* s_lens, int64_t H, int64_t D, cp_dtype dtype,
+                         void* stream) {
+  return kv_gather("cp_kv_gather_n", in, out, count, P, B, s_lens, H, D, dtype, stream);
 }
 
 cp_status cp_attn_backward_delta(const void* o, const void* dout, float* delta, int64_t B,

@@ -52,6 +52,7 @@ struct AnyRelayoutDesc {
   bool seq2head;
   int64_t s_off[CP_MAX_RING_CHUNKS + 1];  // token offsets: shard q = [s_off[q], s_off[q+1])
   int64_t h_off[CP_MAX_RING_CHUNKS + 1];  // head offsets: group p = [h_off[p], h_off[p+1])
+  int64_t count = 1;                      // tensors stored back to back
 };
 int any_relayout_word_bytes(const void* in, void* out, const AnyRelayoutDesc& d);
 hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc& d,

@@ -106,11 +106,13 @@ hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStre
 // S_q rows of H_p*D elements, contiguous on the head-group side and at a row
 // stride of H*D on the sequence-shard side. Only pairs with rows and heads are
 // launched: block (x, y, z) takes words [1024x, 1024x + 1024) of pair
-// (act_p[y / nq], act_q[y % nq]) for batch z.
+// (act_p[y / nq], act_q[y % nq]) for batch z % B of tensor z / B (one launch
+// can move several tensors stored back to back, such as a rank's Q, K and V).
 struct AnyGeometry {
   int32_t P, nq;                  // nq: shards with tokens
   uint8_t act_p[CP_MAX_RING_CHUNKS], act_q[CP_MAX_RING_CHUNKS];
   uint32_t B, S, H, wd;           // wd: words per head row (D elements)
+  uint64_t tensor_words;          // B*S*H*wd: distance between back-to-back tensors
   uint32_t s_off[CP_MAX_RING_CHUNKS + 1];
   uint32_t h_off[CP_MAX_RING_CHUNKS + 1];
   FastDiv row[CP_MAX_RING_CHUNKS];  // words per copied row of group p: H_p * wd
@@ -121,10 +123,11 @@ __global__ __launch_bounds__(kThreads) void any_relayout_kernel(const void* __re
                                                                 void* __restrict__ out_,
                                                                 AnyGeometry g) {
   using T = typename Word<UNIT>::T;
-  const T* in = static_cast<const T*>(in_);
-  T* out = static_cast<T*>(out_);
+  const uint32_t tensor = blockIdx.z / g.B;
+  const uint32_t b = blockIdx.z - tensor * g.B;
+  const T* in = static_cast<const T*>(in_) + tensor * g.tensor_words;
+  T* out = static_cast<T*>(out_) + tensor * g.tensor_words;
   const int p = g.act_p[blockIdx.y / g.nq], q = g.act_q[blockIdx.y % g.nq];
-  const uint32_t b = blockIdx.z;
   const uint32_t sq = g.s_off[q + 1] - g.s_off[q];
   const uint32_t hp = g.h_off[p + 1] - g.h_off[p];
   const uint32_t row_words = hp * g.wd;
@@ -169,6 +172,7 @@ hipError_t launch_any_unit(const void* in, void* out, const AnyRelayoutDesc& d,
   g.S = static_cast<uint32_t>(d.S);
   g.H = static_cast<uint32_t>(d.H);
   g.wd = static_cast<uint32_t>(d.D * d.elem_bytes / UNIT);
+  g.tensor_words = static_cast<uint64_t>(d.B) * d.S * d.H * g.wd;
   uint64_t max_s = 0, max_h = 0;
   int np = 0, nq = 0;
   for (int r = 0; r < d.P; ++r) {
@@ -190,7 +194,7 @@ hipError_t launch_any_unit(const void* in, void* out, const AnyRelayoutDesc& d,
   const uint32_t per_block = kThreads * kUnitsPerThread;
   // (the caller guarantees S > 0 and H > 0, so np, nq >= 1)
   const dim3 grid(static_cast<uint32_t>((max_words + per_block - 1) / per_block),
-                  static_cast<uint32_t>(np * nq), g.B);
+                  static_cast<uint32_t>(np * nq), static_cast<uint32_t>(g.B * d.count));
   if (d.seq2head)
     hipLaunchKernelGGL((any_relayout_kernel<UNIT, true>), grid, dim3(kThreads), 0, stream, in,
                        out, g);
@@ -212,7 +216,7 @@ int any_relayout_word_bytes(const void* in, void* out, const AnyRelayoutDesc& d)
 }
 
 // The caller has checked: 1 <= P <= CP_MAX_RING_CHUNKS, every pair's words
-// and the grid fit 32 bits, B < 65536.
+// and the grid fit 32 bits, B*count < 65536.
 hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc& d,
                                hipStream_t stream) {
   switch (any_relayout_word_bytes(in, out, d)) {

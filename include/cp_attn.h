@@ -251,6 +251,28 @@ cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int
                                        cp_dtype dtype, void* stream);
 
 /*
+ * cp_ulysses_anything_seq2head_n / cp_ulysses_anything_head2seq_n — the
+ * uneven regroupings for `count` tensors stored back to back, in one launch.
+ *
+ * Defined by: as cp_ulysses_anything_seq2head / _head2seq; the rank's Q, K
+ * and V are regrouped together before attention (Context parallelism guide
+ * (diffusers), sections Ulysses Attention and Ulysses Anything Attention).
+ *   in:  count packed inputs, input t starting at element t*B*S*H*D, each laid
+ *        out as the single-tensor call's input; out likewise as its output.
+ * count in 1..65535 and B*count < 65536; every other argument, limit and
+ * rule as in the single-tensor calls. Tensor t of out equals the
+ * single-tensor call on tensor t of in, bit for bit.
+ */
+cp_status cp_ulysses_anything_seq2head_n(const void* in, void* out, int64_t count, int64_t P,
+                                         int64_t B, const int64_t* s_lens,
+                                         const int64_t* h_counts, int64_t D, cp_dtype dtype,
+                                         void* stream);
+cp_status cp_ulysses_anything_head2seq_n(const void* in, void* out, int64_t count, int64_t P,
+                                         int64_t B, const int64_t* s_lens,
+                                         const int64_t* h_counts, int64_t D, cp_dtype dtype,
+                                         void* stream);
+
+/*
  * cp_kv_gather — the unpack of the K/V all-gather: P sequence shards joined
  * into one sequence, all heads kept.
  *
@@ -274,6 +296,21 @@ cp_status cp_ulysses_anything_head2seq(const void* in, void* out, int64_t P, int
  */
 cp_status cp_kv_gather(const void* in, void* out, int64_t P, int64_t B, const int64_t* s_lens,
                        int64_t H, int64_t D, cp_dtype dtype, void* stream);
+
+/*
+ * cp_kv_gather_n — cp_kv_gather for `count` tensors stored back to back (K
+ * and V: the all-gather moves both), in one launch.
+ *
+ * Defined by: as cp_kv_gather.
+ *   in:  count packed shard sets, set t starting at element t*B*S*H*D; out:
+ *        count gathered tensors [B][S][H][D] back to back.
+ * count in 1..65535 and B*count < 65536; every other argument, limit and
+ * rule as in cp_kv_gather. Tensor t of out equals cp_kv_gather on set t of
+ * in, bit for bit.
+ */
+cp_status cp_kv_gather_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,
+                         const int64_t* s_lens, int64_t H, int64_t D, cp_dtype dtype,
+                         void* stream);
 
 /*
  * cp_attn_backward_delta — the per-row statistic the backward needs besides LSE:

@@ -209,6 +209,100 @@ def test_kv_gather_rejects(kw, status):
     assert cp.last_error().startswith("cp_kv_gather")
 
 
+def _anything_n(fn, count, inp=FAKE, out=FAKE2, P=3, B=1, s_lens=(4, 3, 3), h_counts=(2, 2, 1),
+                D=128, dt=BF16):
+    sa, sp = cp._counts(s_lens)
+    ha, hp = cp._counts(h_counts)
+    return fn(inp, out, count, P, B, sp, hp, D, dt, None)
+
+
+# one tensor of the default shape: B*S*H*D*2 = 1*10*5*128*2 bytes
+ANY_BYTES = 10 * 5 * 128 * 2
+
+
+@pytest.mark.parametrize("name", ["_any_seq2head_n", "_any_head2seq_n"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(count=0), INVALID), (dict(count=-1), INVALID), (dict(count=65536), UNSUPPORTED),
+    (dict(count=256, B=256), UNSUPPORTED),                  # B*count must stay below 2^16
+    (dict(count=2, out=FAKE + ANY_BYTES), INVALID),         # the second input overlaps out
+    (dict(count=3, P=0), INVALID), (dict(count=3, inp=None), INVALID),
+])
+def test_anything_relayout_n_rejects(name, kw, status):
+    kw = dict(kw)
+    assert _anything_n(getattr(cp, name), kw.pop("count"), **kw) == status
+    assert cp.last_error().startswith("cp_ulysses_anything")
+
+
+def test_anything_relayout_n_zero_size_is_noop():
+    assert _anything_n(cp._any_seq2head_n, 3, B=0) == OK
+    assert _anything_n(cp._any_head2seq_n, 3, s_lens=(0, 0, 0), inp=None, out=None) == OK
+
+
+@pytest.mark.parametrize("count,kw,status", [
+    (0, {}, INVALID), (65536, {}, UNSUPPORTED), (2, dict(B=40000), UNSUPPORTED),
+    (2, dict(out=FAKE + 10 * 4 * 128 * 2), INVALID),        # overlap from the second tensor on
+    (2, dict(H=-1), INVALID),
+])
+def test_kv_gather_n_rejects(count, kw, status):
+    args = dict(inp=FAKE, out=FAKE2, P=3, B=1, H=4, D=128, dt=BF16)
+    args.update(kw)
+    arr, ptr = cp._counts((4, 3, 3))
+    assert cp._kv_gather_n(args["inp"], args["out"], count, args["P"], args["B"], ptr, args["H"],
+                           args["D"], args["dt"], None) == status
+    assert cp.last_error().startswith("cp_kv_gather_n")
+
+
+# ---- the Python binding checks the buffers the C ABI only sees as addresses
+# (these raise before any pointer is taken, so they run on CPU tensors)
+
+def test_binding_rejects_wrong_output_buffers():
+    import torch
+    bf = torch.bfloat16
+    x = torch.zeros((2, 1, 3, 4, 8), dtype=bf)
+    with pytest.raises(ValueError, match="out must be"):
+        cp.ulysses_seq2head(x, 2, torch.zeros((2, 1, 6, 2, 7), dtype=bf))     # short last dim
+    with pytest.raises(ValueError, match="out must be"):
+        cp.ulysses_seq2head(x, 2, torch.zeros((2, 1, 6, 2, 8), dtype=torch.float32))
+    y = torch.zeros((2, 1, 6, 2, 8), dtype=bf)
+    with pytest.raises(ValueError, match="out must be"):
+        cp.ulysses_head2seq(y, 2, torch.zeros((2, 1, 3, 4, 4), dtype=bf))
+    flat = torch.zeros(1 * 5 * 3 * 8, dtype=bf)
+    with pytest.raises(ValueError, match="out must be"):
+        cp.ulysses_anything_seq2head(flat, (2, 3), (1, 2), 1, 8, torch.zeros(119, dtype=bf))
+    with pytest.raises(ValueError, match="packed tensor"):
+        cp.ulysses_anything_seq2head(flat[:-1], (2, 3), (1, 2), 1, 8)
+    with pytest.raises(ValueError, match="out must be"):
+        cp.kv_gather(flat, (2, 3), 1, 3, 8, torch.zeros((1, 5, 3, 4), dtype=bf))
+    q = torch.zeros((1, 4, 2, 64), dtype=bf)
+    with pytest.raises(ValueError, match="o must be"):
+        cp.attn_chunk_partial(q, q, q, torch.zeros((1, 4, 2, 32)))
+    with pytest.raises(ValueError, match="lse must be"):
+        cp.attn_chunk_partial(q, q, q, None, torch.zeros((1, 2, 4), dtype=bf))
+    with pytest.raises(ValueError, match="o must be"):
+        cp.ring_attention(q, [(q, q, 0)], torch.zeros((1, 4, 2, 64)))        # not q's dtype
+    parts = torch.zeros((2, 1, 4, 2, 64))
+    with pytest.raises(ValueError, match="lse must be"):
+        cp.lse_merge(parts, torch.zeros((2, 1, 2, 4)), None, torch.zeros((1, 2, 3)))
+
+
+def test_binding_rejects_wrong_backward_inputs():
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros((1, 4, 2, 64), dtype=bf)
+    lse32 = torch.zeros((1, 2, 4))
+    with pytest.raises(ValueError, match="lse must be"):
+        cp.attn_chunk_backward(q, q, q, q, lse32.to(bf), lse32)
+    with pytest.raises(ValueError, match="dout must be"):
+        cp.attn_chunk_backward(q, q, q, q.float(), lse32, lse32)
+    with pytest.raises(ValueError, match="delta must be"):
+        cp.ring_attention_backward(q, [(q, q, 0)], q, lse32, lse32.to(bf))
+    with pytest.raises(ValueError, match="delta must be"):
+        cp.attn_backward_delta(q, q, torch.zeros((1, 2, 4), dtype=bf))
+    with pytest.raises(ValueError, match="chunk 0 dk must be"):
+        cp.ring_attention_backward(q, [(q, q, 0)], q, lse32, lse32,
+                                   grads=[(torch.zeros((1, 4, 2, 32)), torch.zeros((1, 4, 2, 64)))])
+
+
 def test_error_text_cleared_by_success():
     assert _partial(D=96) == UNSUPPORTED and cp.last_error() != ""
     assert _partial(Sq=0) == OK and cp.last_error() == ""

@@ -8,8 +8,8 @@ patterns, then checks against the oracle:
   and their round trip;
 * the uneven (Ulysses Anything) regroupings with a random split of the tokens
   and of the heads over the ranks (ranks with no tokens or no heads allowed),
-  and their round trip;
-* the K/V gather over the same random token split.
+  and their round trip, on one tensor and on the same stack of tensors;
+* the K/V gather over the same random token split, on one tensor and stacked.
 
 The transforms are pure copies, so every comparison is on raw bits.
 """
@@ -109,3 +109,20 @@ def test_random_relayouts_bit_exact(seed):
     kv = cp.kv_gather(flat.view(dt).to(DEV), s_lens, B, Ht, D)
     torch.cuda.synchronize()
     assert np.array_equal(kv.cpu().view(flat.dtype).numpy(), oracle.kv_gather(shards)), "gather"
+
+    # the same three on a stack of n tensors, one launch each
+    stack = synthetic.random_bits((n, B * S * Ht * D), isz, seed=44_000 + seed)
+    sd = stack.view(dt).to(DEV)
+    gs = cp.ulysses_anything_seq2head(sd, s_lens, h_counts, B, D)
+    hs = cp.ulysses_anything_head2seq(sd, s_lens, h_counts, B, D)
+    ks = cp.kv_gather(sd, s_lens, B, Ht, D)
+    torch.cuda.synchronize()
+    gsb, hsb, ksb = (t.cpu().view(stack.dtype).numpy() for t in (gs, hs, ks))
+    for t in range(n):
+        sh = _pieces(stack[t].numpy(), [(B, s, Ht, D) for s in s_lens])
+        want = np.concatenate([w.ravel() for w in oracle.anything_seq2head(sh, list(h_counts))])
+        assert np.array_equal(gsb[t], want), f"stacked anything seq2head tensor {t}"
+        gr = _pieces(stack[t].numpy(), [(B, S, h, D) for h in h_counts])
+        want = np.concatenate([w.ravel() for w in oracle.anything_head2seq(gr, list(s_lens))])
+        assert np.array_equal(hsb[t], want), f"stacked anything head2seq tensor {t}"
+        assert np.array_equal(ksb[t], oracle.kv_gather(sh)), f"stacked gather tensor {t}"
