@@ -13,6 +13,10 @@
  *  - seq2head then head2seq is the identity, and seq2head moves every element
  *    to out[p][b][q*S_l + s][h][d] from in[q][b][s][p*H_l + h][d]
  *    (Context parallelism guide (diffusers), section Ulysses Attention).
+ *  - The uneven regroupings and the K/V gather, on two stacked tensors, move
+ *    every element by their index formulas (Context parallelism guide
+ *    (diffusers), section Ulysses Anything Attention; Sequence Parallelism
+ *    page (SGLang Diffusion), K/V gather) and the uneven pair round-trips.
  *  - With Q = 0 and 128 keys the backward is: dV_j = (1/128) sum_i dO_i,
  *    dK_j = 0, dQ_i = scale sum_j (1/128)(<dO_i, v_j> - Delta_i) k_j with
  *    Delta_i = <dO_i, mean_j v_j> (derivative of the same softmax).
@@ -208,6 +212,70 @@ static void check_relayout(void) {
   hipFree(in), hipFree(mid), hipFree(back);
 }
 
+/* ------------------------------------------- uneven regroupings, stacked */
+static void check_uneven_relayout(void) {
+  enum { P = 3, B = 2, D = 24, COUNT = 2 };
+  const int64_t s_lens[P] = {5, 0, 4}, h_counts[P] = {2, 3, 0};
+  int64_t s_off[P + 1] = {0}, h_off[P + 1] = {0};
+  for (int r = 0; r < P; ++r) {
+    s_off[r + 1] = s_off[r] + s_lens[r];
+    h_off[r + 1] = h_off[r] + h_counts[r];
+  }
+  const int64_t S = s_off[P], H = h_off[P];
+  const size_t n = (size_t)B * S * H * D; /* elements of one tensor */
+  uint16_t* hin = malloc(COUNT * n * 2);
+  uint16_t* hout = malloc(COUNT * n * 2);
+  for (size_t x = 0; x < COUNT * n; ++x) hin[x] = (uint16_t)(x * 40503u + 7u);
+  void *in = dev_alloc(COUNT * n * 2), *mid = dev_alloc(COUNT * n * 2);
+  void *back = dev_alloc(COUNT * n * 2), *gath = dev_alloc(COUNT * n * 2);
+  CHECK_HIP(hipMemcpy(in, hin, COUNT * n * 2, hipMemcpyHostToDevice));
+  expect(cp_ulysses_anything_seq2head_n(in, mid, COUNT, P, B, s_lens, h_counts, D, CP_BF16,
+                                        NULL) == CP_OK, "anything seq2head_n");
+  expect(cp_ulysses_anything_head2seq_n(mid, back, COUNT, P, B, s_lens, h_counts, D, CP_BF16,
+                                        NULL) == CP_OK, "anything head2seq_n");
+  expect(cp_kv_gather_n(in, gath, COUNT, P, B, s_lens, H, D, CP_BF16, NULL) == CP_OK,
+         "kv_gather_n");
+  CHECK_HIP(hipDeviceSynchronize());
+  CHECK_HIP(hipMemcpy(hout, mid, COUNT * n * 2, hipMemcpyDeviceToHost));
+  int perm_ok = 1;
+  for (int t = 0; t < COUNT; ++t)
+    for (int p = 0; p < P; ++p)
+      for (int q = 0; q < P; ++q)
+        for (int b = 0; b < B; ++b)
+          for (int64_t s = 0; s < s_lens[q]; ++s)
+            for (int64_t h = 0; h < h_counts[p]; ++h)
+              for (int d = 0; d < D; ++d) {
+                /* group p = [B][S][h_counts[p]][D] at B*S*h_off[p]*D; shard q =
+                   [B][s_lens[q]][H][D] at B*s_off[q]*H*D */
+                const size_t o = t * n + (size_t)(B * S * h_off[p] * D) +
+                                 (size_t)(((b * S + s_off[q] + s) * h_counts[p] + h) * D + d);
+                const size_t i = t * n + (size_t)(B * s_off[q] * H * D) +
+                                 (size_t)(((b * s_lens[q] + s) * H + h_off[p] + h) * D + d);
+                if (hout[o] != hin[i]) perm_ok = 0;
+              }
+  expect(perm_ok, "anything seq2head_n moves in_q[b][s][h0_p+h][d] to out_p[b][off_q+s][h][d]");
+  CHECK_HIP(hipMemcpy(hout, back, COUNT * n * 2, hipMemcpyDeviceToHost));
+  expect(memcmp(hout, hin, COUNT * n * 2) == 0, "anything head2seq_n(seq2head_n(x)) == x");
+  CHECK_HIP(hipMemcpy(hout, gath, COUNT * n * 2, hipMemcpyDeviceToHost));
+  int gather_ok = 1;
+  for (int t = 0; t < COUNT; ++t)
+    for (int q = 0; q < P; ++q)
+      for (int b = 0; b < B; ++b)
+        for (int64_t s = 0; s < s_lens[q]; ++s)
+          for (int64_t h = 0; h < H; ++h)
+            for (int d = 0; d < D; ++d) {
+              const size_t o = t * n + (size_t)(((b * S + s_off[q] + s) * H + h) * D + d);
+              const size_t i = t * n + (size_t)(B * s_off[q] * H * D) +
+                               (size_t)(((b * s_lens[q] + s) * H + h) * D + d);
+              if (hout[o] != hin[i]) gather_ok = 0;
+            }
+  expect(gather_ok, "kv_gather_n moves in_q[b][s][h][d] to out[b][off_q+s][h][d]");
+  printf("ok: uneven regrouping and K/V gather of %d stacked tensors, s_lens {5,0,4}, "
+         "h_counts {2,3,0}, bit for bit\n", COUNT);
+  free(hin), free(hout);
+  hipFree(in), hipFree(mid), hipFree(back), hipFree(gath);
+}
+
 /* --------------------------------------------------------------- backward */
 static void check_backward(void) {
   enum { Sq = 70, Skv = 128, H = 2, D = 128 };
@@ -298,6 +366,7 @@ int main(void) {
   printf("libcpattn ABI version %d\n", cp_abi_version());
   check_forward();
   check_relayout();
+  check_uneven_relayout();
   check_backward();
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);
