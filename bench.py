@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROTATE_BYTES = 1 << 30        # footprint of the buffer sets an HBM-bound kernel rotates over
+WARM_MS = 30.0                # sustained GPU work before a detail entry's timed region
+MIN_TIMED_MS = 20.0           # shortest timed region of a detail entry
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_flux_ring_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "context_attention_dit_amd", "csrc", "attn_bf16.hip")
 
@@ -69,33 +71,57 @@ def rotating_pairs(x, out_like, nbytes: int):
     return [(x.clone(), out_like.new_empty(out_like.shape)) for _ in range(buffer_sets(nbytes))]
 
 
+def warm_up(torch, fn) -> float:
+    """Run `fn` back to back until WARM_MS of GPU work has passed, so the GPU is
+    at its steady clocks when the timed region starts (it takes about 20 ms of
+    sustained work from idle; the detail entries follow host-side input
+    generation, during which the GPU idles). Returns the mean ms per call."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0 or n < 4:
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) * 1e3
+            if el >= WARM_MS:
+                return el / n
+
+
 def time_rotating(torch, fns, warmup: int, rounds: int) -> float:
     """Mean ms per launch of an HBM-bound kernel, issued back to back over
-    `rounds` passes through `fns` (one closure per buffer set) between one pair
-    of HIP events. Each launch reads operands last touched a full rotation
-    earlier, so they come from HBM, and there is no per-launch event or cache
-    flush in the timed region."""
-    for _ in range(warmup):
+    `rounds` passes (at least MIN_TIMED_MS of work) through `fns` (one closure
+    per buffer set) between one pair of HIP events, after warm_up. Each launch
+    reads operands last touched a full rotation earlier, so they come from HBM,
+    and there is no per-launch event or cache flush in the timed region."""
+    def one_round():
         for f in fns:
             f()
+    for _ in range(warmup):
+        one_round()
+    est = warm_up(torch, one_round)
+    rounds = max(rounds, math.ceil(MIN_TIMED_MS / max(est, 1e-3)))
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(rounds):
-        for f in fns:
-            f()
+        one_round()
     b.record()
     b.synchronize()
     return a.elapsed_time(b) / (rounds * len(fns))
 
 
 def time_back_to_back(torch, fn, warmup: int, iters: int) -> float:
-    """Mean ms per call of `iters` calls issued back to back between one pair of
-    HIP events on the current stream (host-side argument marshalling overlaps
-    the GPU work of the previous call, as it does in a training loop)."""
+    """Mean ms per call of at least `iters` calls (and MIN_TIMED_MS of work)
+    issued back to back between one pair of HIP events on the current stream,
+    after warm_up (host-side argument marshalling overlaps the GPU work of the
+    previous call, as it does in a training loop)."""
     for _ in range(warmup):
         fn()
+    est = warm_up(torch, fn)
+    iters = max(iters, math.ceil(MIN_TIMED_MS / max(est, 1e-3)))
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)

@@ -632,28 +632,33 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* smem, int blk)
   }
   __syncthreads();
   if (grp == 1 || jk >= len) return;
-#pragma unroll
-  for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[md][r] += xk[wave * PER_WAVE + (md * 16 + r) * 64 + lane];
-      dv[md][r] += xk[wave * PER_WAVE + ((D / 32 + md) * 16 + r) * 64 + lane];
-    }
   // register r of block md is element d = 32 md + 8 (r/4) + 4 half + r%4 of key jk
   const int64_t krow = (static_cast<int64_t>(b) * len + jk) * a.H + h;
   float* ok = ch.dk + krow * D;
   float* ov = ch.dv + krow * D;
   const bool acc = a.accum_dkv != 0;
 #pragma unroll
-  for (int md = 0; md < D / 32; ++md)
+  for (int md = 0; md < D / 32; ++md) {
+    // group 1's share of block md, read right before the block is stored: the
+    // fence keeps the compiler from hoisting every block's reads, which would
+    // hold both groups' sums in registers at once and spill
+    asm volatile("" ::: "memory");
+    f32x16 xkm, xvm;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      xkm[r] = xk[wave * PER_WAVE + (md * 16 + r) * 64 + lane];
+      xvm[r] = xk[wave * PER_WAVE + ((D / 32 + md) * 16 + r) * 64 + lane];
+    }
+    const f32x16 k_sum = dk[md] + xkm, v_sum = dv[md] + xvm;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * md + 8 * q4 + 4 * half;
-      store4(ok + d0, a.scale, dk[md][4 * q4], dk[md][4 * q4 + 1], dk[md][4 * q4 + 2],
-             dk[md][4 * q4 + 3], acc);
-      store4(ov + d0, 1.f, dv[md][4 * q4], dv[md][4 * q4 + 1], dv[md][4 * q4 + 2],
-             dv[md][4 * q4 + 3], acc);
+      store4(ok + d0, a.scale, k_sum[4 * q4], k_sum[4 * q4 + 1], k_sum[4 * q4 + 2],
+             k_sum[4 * q4 + 3], acc);
+      store4(ov + d0, 1.f, v_sum[4 * q4], v_sum[4 * q4 + 1], v_sum[4 * q4 + 2],
+             v_sum[4 * q4 + 3], acc);
     }
+  }
 }
 
 template <int D, bool CAUSAL, int G>
