@@ -20,7 +20,10 @@
  *    Tensor pointers must be 16-byte aligned; LSE pointers 4-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued on it and no call synchronises: results are valid once
- *    the stream has reached that point.
+ *    the stream has reached that point. A call enqueues kernel launches only
+ *    (no memset, copy, allocation or synchronisation), so calls may be
+ *    captured into a HIP graph on a capturing stream and replayed; the
+ *    arguments (pointers, sizes, chunk lists) are fixed at capture.
  *  - Arguments are validated on the host before anything is enqueued. On any
  *    error the call returns a non-zero cp_status, enqueues nothing, leaves
  *    every output untouched, and cp_last_error() describes the problem. A
