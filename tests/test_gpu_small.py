@@ -346,19 +346,22 @@ def test_chunk_partial_small_grid_two_groups(causal, Sq, Skv, H, D):
     check_lse(lse, wl)
 
 
-def test_ring_key_splits_across_blocks():
-    """Between one and two query tiles per CU (300 tiles): each tile's keys are
-    split over two blocks whose fp32 partials go through the workspace."""
+@pytest.mark.parametrize("Sq", [
+    128 * 75,        # 300 query tiles
+    128 * 100 - 3,   # 400 query tiles, the last ragged
+])
+def test_ring_key_splits_across_blocks(Sq):
+    """Between one and two query tiles per CU: each tile's keys are split over
+    two blocks whose fp32 partials go through the workspace."""
     lens = (1024, 1040)
     S, H, D = sum(lens), 4, 128
-    Sq = 128 * 75
     q = synthetic.make_tensor((1, Sq, H, D), torch.bfloat16, 41)
     k = synthetic.make_tensor((1, S, H, D), torch.bfloat16, 42)
     v = synthetic.make_tensor((1, S, H, D), torch.bfloat16, 43)
     chunks = _chunk_tensors(k.to(DEV), v.to(DEV), lens)
     ws = cp.ring_attention_workspace_bytes(2, 1, H, Sq, D)
     assert ws > 0, "expected a split across blocks for this grid"
-    say(f"ring with key splits across blocks, workspace {ws} bytes")
+    say(f"ring with key splits across blocks, Sq={Sq}, workspace {ws} bytes")
     o, lse = cp.ring_attention(q.to(DEV), chunks)
     torch.cuda.synchronize()
     rows = np.arange(0, Sq, 37)
