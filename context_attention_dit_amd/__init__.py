@@ -35,7 +35,8 @@ LIB_PATH = os.path.join(_HERE, "libcpattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        f"{LIB_PATH} is missing: build it with "
+        "`python -c 'import __graft_entry__ as g; g.build()'` "
         "(or `python context_attention_dit_amd/_build.py`). There is no fallback path.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -430,7 +431,8 @@ def attn_chunk_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout:
     return dq, dk, dv
 
 
-def ring_attention_backward(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
+def ring_attention_backward(q: torch.Tensor,
+                            chunks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
                             dout: torch.Tensor, lse: torch.Tensor, delta: torch.Tensor,
                             dq: Optional[torch.Tensor] = None,
                             grads: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor]]] = None,
@@ -485,5 +487,6 @@ def ring_attention_backward(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor
 __all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
            "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
            "ulysses_anything_head2seq", "kv_gather", "attn_backward_delta",
-           "attn_chunk_backward", "ring_attention_backward", "KVGrad", "BWD_ACCUMULATE_DQ", "BWD_ACCUMULATE_DKV", "last_error", "abi_version", "CpAttnError",
-           "KVChunk", "LIB_PATH"]
+           "attn_chunk_backward", "ring_attention_backward", "KVGrad", "BWD_ACCUMULATE_DQ",
+           "BWD_ACCUMULATE_DKV", "last_error", "abi_version", "CpAttnError", "KVChunk",
+           "LIB_PATH"]
