@@ -6,6 +6,10 @@
   The tensors are zero except for seeded inputs on a few heads at both ends of
   the head range; the oracle computes those heads (heads are independent).
 * Most chunks: a ring of 64 chunks (CP_MAX_RING_CHUNKS), forward and backward.
+* Longest chunk: 2^21 keys of 8 heads in one chunk (4 GiB per K or V, so a
+  chunk's own offsets pass 2^31 bytes) and the same keys as a ring of two
+  chunks, causal and not; the running fp32 sums cover 2^21 keys per row. The
+  oracle computes two sampled heads (the others are zero).
 """
 import math
 
@@ -111,3 +115,43 @@ def test_ring_of_64_chunks_forward_and_backward():
     got_v = torch.cat([grads[order.index(c)][1] for c in range(P)], dim=1)
     check_grad(got_k, wk, "dK")
     check_grad(got_v, wv, "dV")
+
+
+def test_longest_chunk_forward_and_ring():
+    D, H, Sq, Skv = 128, 8, 200, 1 << 21
+    heads = [0, H - 1]
+    n = len(heads)
+    say(f"longest chunk: Skv={Skv} H={H} D={D} Sq={Sq}, sampled heads {heads}")
+    bf = torch.bfloat16
+    src = [synthetic.make_tensor(shape, bf, 1700 + t) for t, shape in
+           enumerate([(1, Sq, n, D), (1, Skv, n, D), (1, Skv, n, D)])]
+    hidx = torch.tensor(heads, device=DEV)
+    q = torch.zeros((1, Sq, H, D), dtype=bf, device=DEV)
+    k = torch.zeros((1, Skv, H, D), dtype=bf, device=DEV)
+    v = torch.zeros((1, Skv, H, D), dtype=bf, device=DEV)
+    for dst, x in zip((q, k, v), src):
+        dst[:, :, hidx] = x.to(DEV)
+    scale = 1 / math.sqrt(D)
+    q64, k64, v64 = (to_f64(x) for x in src)
+    # one chunk holding every key, non-causal
+    o, lse = cp.attn_chunk_partial(q, k, v, out_dtype=bf)
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(q64, k64, v64, scale)
+    check_o(o[:, :, hidx], wo, "bf16", "one chunk O, sampled heads")
+    check_lse(lse[:, hidx], wl, "one chunk LSE, sampled heads")
+    del o, lse
+    # the same keys as a ring of two chunks, queries at the end of the sequence
+    half = Skv // 2
+    chunks = [(k[:, half:].contiguous(), v[:, half:].contiguous(), half),
+              (k[:, :half].contiguous(), v[:, :half].contiguous(), 0)]
+    del k, v
+    q0 = Skv - Sq + 7          # row i sees keys 0 .. q0 + i; the last 7 rows see all of them
+    for causal in (False, True):
+        ro, rl = cp.ring_attention(q, chunks, causal=causal, q_pos0=q0)
+        torch.cuda.synchronize()
+        if causal:
+            wo, wl = oracle.attention(q64, k64, v64, scale, True, np.arange(q0, q0 + Sq),
+                                      np.arange(Skv))
+        check_o(ro[:, :, hidx], wo, "bf16", f"ring O (causal={causal}), sampled heads")
+        check_lse(rl[:, hidx], wl, f"ring LSE (causal={causal}), sampled heads")
+        del ro, rl
