@@ -182,6 +182,28 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"ring_attention (chunk partials + LSE merge) in {dt:.1f} s"}
 
 
+def cpu_oracle_relayout(budget_s: float = 2.0):
+    """The oracle's seq2head (a numpy transpose copy) on the Qwen rank's Q tensor,
+    repeated for ~budget_s on the host: host GB/s (read + write per element)."""
+    import torch
+
+    import oracle
+    import synthetic
+    w = synthetic.QWEN_ULYSSES
+    x = synthetic.make_qkv(w)[0].view(w.P, 1, w.S_local, w.H, w.D)
+    bits = x.contiguous().view(torch.int16).numpy()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.seq2head(bits, w.P)
+        n += 1
+    dt = time.perf_counter() - t0
+    nbytes = 2 * bits.nbytes
+    return {"gbs": n * nbytes / dt / 1e9, "unit": "GB/s", "kind": "oracle",
+            "sample": f"seq2head of the Qwen-Image rank's Q ({bits.nbytes / 1e6:.1f} MB, "
+                      f"[{w.P}][1][{w.S_local}][{w.H}][{w.D}] bf16 bits) {n} times in {dt:.1f} s "
+                      f"(numpy transpose copy)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +307,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline()
+        detail["cpu_oracle_relayout"] = cpu_oracle_relayout()
     print(json.dumps(line), flush=True)
     return 0
 
