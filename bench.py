@@ -406,9 +406,19 @@ def merge_workload(torch, cp, dev, q0, vis, wf):
     del sets
     out["flux_lse_merge"] = {"us": d * 1e3, "gbs": mbytes / (d * 1e-3) / 1e9, "bytes": mbytes,
                              "hbm_frac": mbytes / (d * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    ms = time_back_to_back(torch, lambda: [cp.attn_chunk_partial(q0, kc, vc) for kc, vc, _ in vis],
-                           3, 20)
-    out["flux_partials_x4"] = {"us": ms * 1e3}
+    # the per-hop form of the same rank: one partial per chunk into its slot of
+    # the stacked fp32 partials, then the merge (what a P2P ring does per hop)
+    flops = attn_flops(q0.shape[1], wf.S, wf.H, wf.D, False)
+
+    def hops():
+        for c, (kc, vc, _) in enumerate(vis):
+            cp.attn_chunk_partial(q0, kc, vc, po[c], pl[c])
+
+    ms = time_back_to_back(torch, hops, 3, 20)
+    ms_m = time_back_to_back(torch, lambda: (hops(), cp.lse_merge(po, pl, mo, ml)), 3, 20)
+    out["flux_partials_x4"] = {"us": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12,
+                               "with_merge_us": ms_m * 1e3,
+                               "with_merge_tflops": flops / (ms_m * 1e-3) / 1e12}
     return out
 
 
