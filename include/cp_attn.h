@@ -32,6 +32,10 @@
  *    sizes are CP_E_INVALID.
  *  - Repeating a call on identical inputs gives byte-identical outputs
  *    (fixed reduction order, no floating-point atomics).
+ *  - Attention inputs (Q, K, V, dO, partial O) must be finite. The kernels
+ *    do not propagate NaN or infinity the way the textbook formula would; a
+ *    non-finite input gives unspecified (possibly finite) outputs for the
+ *    rows it touches. The layout transforms move any bit pattern unchanged.
  */
 #ifndef CP_ATTN_H
 #define CP_ATTN_H
