@@ -213,8 +213,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
-                    help="run only this detail workload (qwen, wan, llm, ra, merge, anything, "
-                         "kvgather, unified, bwd) "
+                    help="run only this detail workload (qwen, wan, llm, overlap, ra, merge, "
+                         "anything, kvgather, unified, bwd) "
                          "after the "
                          "headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -323,6 +323,9 @@ def other_workloads(torch, cp, synthetic, dev, q0, vis, wf, only=None):
     for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
         if want(tags[w.name]):
             out[w.name] = ulysses_workload(torch, cp, synthetic, dev, w)
+    if want("overlap"):
+        out["qwen-image-1536-ulysses4-stream-overlap"] = stream_overlap_workload(
+            torch, cp, synthetic, dev)
     if want("ra"):
         out[synthetic.LLM_RING_ANYTHING.name] = ring_anything_workload(torch, cp, synthetic, dev)
     if want("anything"):
@@ -620,6 +623,58 @@ def unified_workload(torch, cp, synthetic, dev):
            "note": "step = one launch regrouping Q, K, V of both ring segments (stacked), "
                    "ring attention, inverse regrouping of O; back-to-back steps"}
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, whole step {res['step_tflops']:.0f}")
+    return res
+
+
+def stream_overlap_workload(torch, cp, synthetic, dev, layers: int = 4):
+    """Qwen-Image Ulysses layers, sequential against pipelined on two streams: the
+    stacked Q, K, V regrouping of layer l+1 (all P ranks' pack and unpack, on
+    stream B) runs beside layer l's rank-0 attention (stream A), ordered by
+    events. Both orders compute the same bytes."""
+    w = synthetic.QWEN_ULYSSES
+    log(f"{w.name}: stream overlap, {layers} layers")
+    P, S_l, H, D, Hl, S = w.P, w.S_local, w.H, w.D, w.H_local, w.S
+    base = torch.stack([x.view(P, 1, S_l, H, D) for x in synthetic.make_qkv(w)]).to(dev)
+    qkv = [base.clone() for _ in range(layers)]
+    del base
+    heads = [torch.empty((3, P, 1, S, Hl, D), dtype=w.dtype, device=dev) for _ in range(layers)]
+    o = torch.empty((1, S, Hl, D), dtype=w.dtype, device=dev)
+    lse = torch.empty((1, Hl, S), dtype=torch.float32, device=dev)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = [torch.cuda.Event() for _ in range(layers)]
+
+    def attend(l, stream):
+        cp.attn_chunk_partial(heads[l][0, 0], heads[l][1, 0], heads[l][2, 0], o, lse,
+                              out_dtype=w.dtype, stream=stream)
+
+    def sequential():
+        for l in range(layers):
+            cp.ulysses_seq2head(qkv[l], P, heads[l])
+            attend(l, None)
+
+    def pipelined():
+        sb.wait_stream(torch.cuda.current_stream())
+        cp.ulysses_seq2head(qkv[0], P, heads[0], stream=sb)
+        ready[0].record(sb)
+        for l in range(layers):
+            sa.wait_event(ready[l])
+            attend(l, sa)
+            if l + 1 < layers:
+                cp.ulysses_seq2head(qkv[l + 1], P, heads[l + 1], stream=sb)
+                ready[l + 1].record(sb)
+        torch.cuda.current_stream().wait_stream(sa)
+
+    seq_ms = time_back_to_back(torch, sequential, 2, 10) / layers
+    pipe_ms = time_back_to_back(torch, pipelined, 2, 10) / layers
+    res = {"layers": layers, "sequential_us_per_layer": seq_ms * 1e3,
+           "pipelined_us_per_layer": pipe_ms * 1e3,
+           "note": "per layer: stacked Q, K, V seq2head of all 4 ranks (349 MB moved) and "
+                   "rank-0 attention (6 heads x 9472); pipelined = next layer's regrouping on "
+                   "a second stream beside this layer's attention"}
+    log(f"{w.name}: sequential {res['sequential_us_per_layer']:.0f} us/layer, pipelined "
+        f"{res['pipelined_us_per_layer']:.0f} us/layer")
+    del qkv, heads
+    torch.cuda.empty_cache()
     return res
 
 
