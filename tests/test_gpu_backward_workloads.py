@@ -5,6 +5,11 @@ launch configuration the benchmark times.
   in ring order [0, 3, 2, 1] with dQ accumulated; every head, every output is
   compared with the fp64 oracle. The saved O (rounded to bf16) and LSE are the
   oracle's own forward.
+* The whole FLUX ring, all 4 ranks: each rank's forward (cp_ring_attention)
+  and backward (cp_ring_attention_backward, its chunks in its ring order), the
+  dK/dV shares accumulated across ranks into each chunk owner's buffers. The
+  summed gradients of two sampled heads are compared with the oracle's full
+  backward (attention_grad, from Q, K, V and dO alone), causal and not.
 * Wan and the 128K causal LLM Ulysses ranks: one call over the whole
   sequence. The oracle cannot afford every row's forward statistics there, so
   the kernel is fed the oracle's exact LSE and Delta for a sample of query rows
@@ -85,6 +90,44 @@ def test_flux_ring_rank0_backward_full():
         check_grad(grads[c][0], gk, f"dK chunk {c}")
         check_grad(grads[c][1], gv, f"dV chunk {c}")
     check_grad(dq, want_dq, "dQ")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_flux_ring_all_ranks_backward_accumulated(causal):
+    w = synthetic.FLUX_RING
+    say(f"{w.name}: every rank's forward and backward, causal={causal}")
+    q, k, v = synthetic.make_qkv(w)
+    H, D, P = w.H, w.D, w.P
+    do = synthetic.make_tensor((1, w.S, H, D), torch.bfloat16, 1078)
+    starts, lens = w.chunk_starts(), w.chunk_lens
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    chunks = [(kd[:, s:s + m].contiguous(), vd[:, s:s + m].contiguous(), s)
+              for s, m in zip(starts, lens)]
+    f32 = torch.float32
+    acc = [(torch.zeros((1, m, H, D), dtype=f32, device=DEV),
+            torch.zeros((1, m, H, D), dtype=f32, device=DEV)) for m in lens]
+    dq = torch.empty((1, w.S, H, D), dtype=f32, device=DEV)
+    for r in range(P):
+        s0, m = starts[r], lens[r]
+        order = synthetic.ring_order(r, P)
+        visit = [chunks[c] for c in order]
+        q_r, do_r = qd[:, s0:s0 + m].contiguous(), dod[:, s0:s0 + m].contiguous()
+        o_r, lse_r = cp.ring_attention(q_r, visit, causal=causal, q_pos0=s0)
+        delta_r = cp.attn_backward_delta(o_r, do_r)
+        dq_r, _ = cp.ring_attention_backward(q_r, visit, do_r, lse_r, delta_r,
+                                             grads=[acc[c] for c in order], causal=causal,
+                                             q_pos0=s0, accumulate_dkv=True)
+        dq[:, s0:s0 + m] = dq_r
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    say(f"{w.name}: oracle backward on heads {heads}")
+    hs = torch.tensor(heads)
+    q64, k64, v64, do64 = (_f64(x[:, :, hs]) for x in (q, k, v, do))
+    wq, wk, wv = oracle.attention_grad(q64, k64, v64, do64, 1 / math.sqrt(D), causal)
+    hd = hs.to(DEV)
+    check_grad(dq[:, :, hd], wq, "dQ, all ranks")
+    check_grad(torch.cat([a[0] for a in acc], dim=1)[:, :, hd], wk, "dK summed over ranks")
+    check_grad(torch.cat([a[1] for a in acc], dim=1)[:, :, hd], wv, "dV summed over ranks")
 
 
 @pytest.mark.parametrize("wname", [synthetic.WAN_ULYSSES.name, synthetic.LLM_ULYSSES.name])
