@@ -20,7 +20,8 @@
 namespace cpattn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;           // uneven regrouping
+constexpr int kRelayoutThreads = 512;   // standard regrouping (1% faster than 256 measured)
 constexpr int kUnitsPerThread = 4;  // words per work-item of the uneven regrouping
 
 template <int UNIT>
@@ -65,13 +66,14 @@ __device__ __forceinline__ uint32_t head_index(uint32_t u, const Geometry& g) {
 // on the Ulysses shapes this order, at one word per work-item, beats output
 // order and 2-8 words per work-item (71-83% of HBM peak against 67-79%).
 template <int UNIT, bool SEQ2HEAD>
-__global__ __launch_bounds__(kThreads) void relayout_kernel(const void* __restrict__ in_,
-                                                            void* __restrict__ out_, Geometry g) {
+__global__ __launch_bounds__(kRelayoutThreads) void relayout_kernel(const void* __restrict__ in_,
+                                                                    void* __restrict__ out_,
+                                                                    Geometry g) {
   using T = typename Word<UNIT>::T;
   // blockIdx.y: which of the back-to-back tensors
   const T* in = static_cast<const T*>(in_) + static_cast<uint64_t>(blockIdx.y) * g.total;
   T* out = static_cast<T*>(out_) + static_cast<uint64_t>(blockIdx.y) * g.total;
-  const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t u = blockIdx.x * kRelayoutThreads + threadIdx.x;
   if (u >= g.total) return;
   const uint32_t hu = head_index(u, g);
   if (SEQ2HEAD)
@@ -91,13 +93,14 @@ hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStre
   g.batch.init(static_cast<uint32_t>(d.B));
   g.seqP.init(static_cast<uint32_t>(d.P * d.S_local));
   g.P.init(static_cast<uint32_t>(d.P));
-  const dim3 grid((g.total + kThreads - 1) / kThreads, static_cast<uint32_t>(d.count));
+  const dim3 grid((g.total + kRelayoutThreads - 1) / kRelayoutThreads,
+                  static_cast<uint32_t>(d.count));
   if (d.seq2head)
-    hipLaunchKernelGGL((relayout_kernel<UNIT, true>), grid, dim3(kThreads), 0, stream, in, out,
-                       g);
+    hipLaunchKernelGGL((relayout_kernel<UNIT, true>), grid, dim3(kRelayoutThreads), 0, stream, in,
+                       out, g);
   else
-    hipLaunchKernelGGL((relayout_kernel<UNIT, false>), grid, dim3(kThreads), 0, stream, in, out,
-                       g);
+    hipLaunchKernelGGL((relayout_kernel<UNIT, false>), grid, dim3(kRelayoutThreads), 0, stream,
+                       in, out, g);
   return hipGetLastError();
 }
 
