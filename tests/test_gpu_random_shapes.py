@@ -3,8 +3,9 @@ and ring backward, against the fp64 oracle.
 
 Each case draws B, H, D in {64, 128}, ragged Sq and a key length split into a
 random number of chunks (empty chunks allowed), causal or not, with random
-query and key position offsets and a random ring visit order. The draws are
-seeded, so every run checks the same cases.
+query and key position offsets and a random ring visit order; about half the
+cases run the backward with both accumulate flags into pre-filled buffers. The
+draws are seeded, so every run checks the same cases.
 
 Tolerances: LSE max-abs 1e-4, gradients as in the other backward tests. For
 bf16 outputs: max-abs <= 1e-2 * max(1, max|ref|) and
@@ -59,15 +60,16 @@ def _case(seed):
     q_pos0 = int(rng.integers(0, Skv + 64)) if causal else 0
     kv_pos0 = int(rng.integers(0, 32)) if causal else 0
     order = [int(x) for x in rng.permutation(P)]
-    return B, H, D, Sq, lens, causal, q_pos0, kv_pos0, order
+    accumulate = bool(rng.integers(0, 2))   # backward adds into pre-filled buffers
+    return B, H, D, Sq, lens, causal, q_pos0, kv_pos0, order, accumulate
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_shape_forward_and_backward(seed):
-    B, H, D, Sq, lens, causal, q_pos0, kv_pos0, order = _case(seed)
+    B, H, D, Sq, lens, causal, q_pos0, kv_pos0, order, accumulate = _case(seed)
     Skv = sum(lens)
     say(f"random case {seed}: B={B} H={H} D={D} Sq={Sq} lens={lens} causal={causal} "
-        f"q_pos0={q_pos0} kv_pos0={kv_pos0} order={order}")
+        f"q_pos0={q_pos0} kv_pos0={kv_pos0} order={order} accumulate={accumulate}")
     bf = torch.bfloat16
     q = synthetic.make_tensor((B, Sq, H, D), bf, 20_000 + 4 * seed)
     k = synthetic.make_tensor((B, Skv, H, D), bf, 20_001 + 4 * seed)
@@ -99,10 +101,27 @@ def test_random_shape_forward_and_backward(seed):
     # backward of the same rank from the oracle's saved statistics
     o_bf = torch.tensor(wo, dtype=torch.float32).to(bf).to(DEV)
     delta = cp.attn_backward_delta(o_bf, dod)
+    f32 = torch.float32
+    if accumulate:
+        # running sums from earlier ranks or chunks, 0.1 N(0, 1): the call must add to
+        # them (a skipped addition would leave an error ~0.1, far above the bars), and
+        # the fp32 rounding of the sum stays ~1e-8, below the bars of small gradients
+        gen = torch.Generator().manual_seed(30_000 + seed)
+        pre_q = (0.1 * torch.randn((B, Sq, H, D), generator=gen)).to(DEV)
+        pre_kv = [((0.1 * torch.randn(kc.shape, generator=gen)).to(DEV),
+                   (0.1 * torch.randn(kc.shape, generator=gen)).to(DEV)) for kc, _, _ in visit]
+        dq_in, grads_in = pre_q.clone(), [(a.clone(), b.clone()) for a, b in pre_kv]
+    else:
+        dq_in, grads_in = None, None
     dq, grads = cp.ring_attention_backward(qd, visit, dod,
-                                           torch.tensor(wl, dtype=torch.float32).to(DEV), delta,
-                                           causal=causal, q_pos0=q_pos0)
+                                           torch.tensor(wl, dtype=f32).to(DEV), delta,
+                                           dq_in, grads_in, causal=causal, q_pos0=q_pos0,
+                                           accumulate_dq=accumulate, accumulate_dkv=accumulate)
     torch.cuda.synchronize()
+    if accumulate:   # the call's share, the prefill taken off exactly (in fp64)
+        dq = dq.double() - pre_q.double()
+        grads = [(a.double() - pa.double(), b.double() - pb.double())
+                 for (a, b), (pa, pb) in zip(grads, pre_kv)]
     # the kernel's contract: gradients for the Delta of the O it is given (the
     # oracle's O rounded to bf16, as stored); with few keys O is not small and
     # that rounding alone moves Delta by more than the kernel's own arithmetic
