@@ -237,7 +237,8 @@ def ring_attention(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.T
     for c, (k, v, pos0) in enumerate(chunks):
         arr[c] = KVChunk(_ptr(k), _ptr(v), k.shape[1], int(pos0))
     need = ring_attention_workspace_bytes(len(chunks), B, H, Sq, D)
-    if workspace is None and need > 0:
+    own_ws = workspace is None and need > 0 and q.dtype == torch.bfloat16
+    if own_ws:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None and workspace.device != q.device:
         raise ValueError(f"workspace must be on {q.device}")
@@ -246,6 +247,10 @@ def ring_attention(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.T
     _check("cp_ring_attention", _ring(
         _ptr(q), arr, len(chunks), _ptr(o), _ptr(lse), B, H, Sq, D, _dtype_code(q.dtype), scale,
         int(causal), q_pos0, _ptr(workspace), ws_bytes, _stream(stream)))
+    if own_ws and stream is not None:
+        # the workspace was allocated on the current stream but is used on `stream`:
+        # keep the caching allocator from reusing it before that work is done
+        workspace.record_stream(stream)
     return o, lse
 
 

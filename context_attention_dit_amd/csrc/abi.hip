@@ -210,7 +210,8 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
     return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d chunks", fn, (long long)P,
                 CP_MAX_RING_CHUNKS);
   if (P > 0 && !chunks) return fail(CP_E_INVALID, "%s: null chunk array", fn);
-  const size_t need = cp_ring_attention_workspace_bytes(P, B, H, Sq, D);
+  // the fp32 path never splits keys: only bf16 calls need the workspace
+  const size_t need = in_dtype == CP_BF16 ? cp_ring_attention_workspace_bytes(P, B, H, Sq, D) : 0;
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(CP_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace_bytes);

@@ -152,6 +152,7 @@ size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_
  *   cp_ring_attention_workspace_bytes(P, B, H, Sq, D) bytes (NULL if 0), owned
  *   by the caller, contents need no initialisation and are scratch afterwards;
  *   concurrent calls must not share one workspace. Too small: CP_E_WORKSPACE.
+ *   CP_F32 inputs never split keys and need no workspace (NULL, 0 accepted).
  *
  * 0 <= P <= CP_MAX_RING_CHUNKS; chunk lengths may differ and may be 0. Same D
  * and dtype support as cp_attn_chunk_partial (O in in_dtype).

@@ -143,6 +143,16 @@ def test_ring_zero_size_is_noop_and_workspace_query():
     assert _ring(H=300, ws_bytes=n - 16) == WORKSPACE
 
 
+def test_ring_fp32_needs_no_workspace():
+    # the fp32 path never splits keys: at a size where bf16 needs a workspace, an
+    # fp32 call without one passes the workspace check (and here fails on the
+    # misaligned LSE that follows it, so nothing is launched)
+    assert cp.ring_attention_workspace_bytes(4, 1, 300, 8, 128) > 0
+    assert _ring(H=300, dt=BF16, ws=None, ws_bytes=0, lse=FAKE5 + 2) == WORKSPACE
+    assert _ring(H=300, dt=F32, ws=None, ws_bytes=0, lse=FAKE5 + 2) == INVALID
+    assert "misaligned" in cp.last_error()
+
+
 def _relayout(fn, inp=FAKE, out=FAKE2, P=4, B=1, S=8, H=8, D=128, dt=BF16):
     return fn(inp, out, P, B, S, H, D, dt, None)
 
