@@ -42,7 +42,7 @@ hand-derived golden values (``tests/golden/``), identities, a library
 routine (torch's fp64 scaled_dot_product_attention, and its autograd for the
 backward), finite differences and explicit loops.
 """
-from .attention import (attention, bf16_bits_to_f64, chunk_partial, chunk_positions,
+from .attention import (attention, bf16_bits_to_f64, chunk_partial,
                         lse_merge, ring_attention, softmax_matrix)
 from .backward import attention_grad, backward_delta, chunk_grad
 from .relayout import (anything_head2seq, anything_head2seq_loop, anything_seq2head,
@@ -50,7 +50,7 @@ from .relayout import (anything_head2seq, anything_head2seq_loop, anything_seq2h
                        kv_gather_loop, seq2head, seq2head_loop)
 
 __all__ = ["attention", "chunk_partial", "lse_merge", "ring_attention", "softmax_matrix",
-           "bf16_bits_to_f64", "chunk_positions", "seq2head", "head2seq", "seq2head_loop",
+           "bf16_bits_to_f64", "seq2head", "head2seq", "seq2head_loop",
            "head2seq_loop", "anything_seq2head", "anything_head2seq", "anything_seq2head_loop",
            "anything_head2seq_loop", "even_split", "kv_gather", "kv_gather_loop",
            "attention_grad", "backward_delta", "chunk_grad"]

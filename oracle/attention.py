@@ -13,7 +13,7 @@ explicit integer arrays, one per query row and one per key row.
 """
 from __future__ import annotations
 
-from typing import List, Optional, Sequence, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -189,11 +189,3 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     u = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
     return u.view(np.float32).astype(np.float64)
 
-
-def chunk_positions(lens: Sequence[int], pos0: int = 0) -> List[np.ndarray]:
-    """Global key positions of each chunk of a sequence split into ``lens`` pieces."""
-    out, acc = [], pos0
-    for n in lens:
-        out.append(np.arange(acc, acc + n, dtype=np.int64))
-        acc += n
-    return out
