@@ -1,17 +1,22 @@
 """Benchmark of the context-parallel attention hot path on one MI355X.
 
-Default workload (the headline line): one ring rank of FLUX.1-dev at
-1024x1024 — B=1, H=24, D=128, S=4608 (4096 image + 512 text tokens), bf16,
-ring degree 4, rank 0's 1152 query rows against 4 K/V chunks of 1152 in ring
-order [0, 3, 2, 1], fp32 output+LSE merge fused. One step = one
-cp_ring_attention call. ``value`` is attention TFLOP/s (4*D FLOP per
-(query, key) pair) with inputs resident in HBM.
+Default workload (the headline line): one Ulysses rank of a 128K-token causal
+LLM at sequence-parallel degree 8 — S=131072, H=32 (4 heads per rank), D=128,
+bf16, causal from positions. One step is one pass of the rank's whole hot
+path: the Ulysses regrouping of Q, K and V ([8][1][16384][32][128] ->
+[8][1][131072][4][128], one stacked launch), rank 0's causal attention over
+the full sequence on its 4 heads (bf16 O, fp32 LSE), and the inverse
+regrouping of O. ``value`` is attention TFLOP/s over the whole step (4*D FLOP
+per visible (query, key) pair, 17.59 TFLOP per step) with inputs resident in
+HBM; ``roofline`` is the attention kernel alone, timed with HIP events on its
+launch stream.
 
 The same JSON line also carries, under ``detail``, every other workload:
-Ulysses seq2head/head2seq GB/s and rank-0 attention TFLOP/s for the
-Qwen-Image, Wan and 128K-causal shapes, the ring-anything S=4099 ranks, and
-the standalone LSE merge GB/s; plus the roofline of the dominant kernel and
-the fp64 CPU oracle timed on the host (``cpu_baseline``).
+the FLUX ring rank (with its own roofline), Ulysses seq2head/head2seq GB/s
+and rank-0 attention TFLOP/s for the Qwen-Image and Wan shapes, the
+ring-anything S=4099 ranks, the standalone LSE merge GB/s, the uneven
+regroupings, K/V gather, unified share and backward entries; plus the fp64
+CPU oracle timed on the host (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -33,7 +38,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROTATE_BYTES = 1 << 30        # footprint of the buffer sets an HBM-bound kernel rotates over
 WARM_MS = 30.0                # sustained GPU work before a detail entry's timed region
 MIN_TIMED_MS = 20.0           # shortest timed region of a detail entry
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_flux_ring_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llm_causal_traffic.json")
+FLUX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_flux_ring_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "context_attention_dit_amd", "csrc", "attn_bf16.hip")
 
 
@@ -137,10 +143,10 @@ def median(xs):
     return xs[len(xs) // 2]
 
 
-def traffic_record():
+def traffic_record(path=TRAFFIC_FILE):
     """HBM bytes per launch of the attention kernel, if taken on the current source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
         src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
         if rec.get("attn_bf16_sha256") == src_hash:
             return rec.get("bytes_per_launch")
@@ -149,37 +155,43 @@ def traffic_record():
     return None
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """fp64 oracle on a bounded sample of the FLUX ring rank: whole heads until ~budget_s."""
+def cpu_baseline(qkv_cpu, budget_s: float = 15.0):
+    """fp64 oracle on a bounded stratified sample of the headline's attention.
+
+    Rank 0 of the 128K causal Ulysses workload attends heads 0..3 over the whole
+    sequence. Per head the sample is the first 512 and the last 512 query rows
+    plus 4096 rows drawn at random (seeded), each against every key it may see;
+    heads are taken in turn until ~budget_s is spent. FLOP are counted as on
+    the GPU: 4*D per visible (query, key) pair of the sampled rows."""
     import numpy as np
     import torch
 
     import oracle
     import synthetic
-    w = synthetic.FLUX_RING
-    q, k, v = synthetic.make_qkv(w)
-    n = w.chunk_lens[0]
+    w = synthetic.LLM_ULYSSES
+    q, k, v = qkv_cpu
     f64 = lambda t: oracle.bf16_bits_to_f64(t.contiguous().view(torch.int16).numpy())
     ncores = len(os.sched_getaffinity(0))
     torch.set_num_threads(ncores)
-    chunks = []
-    for s0, ln in zip(w.chunk_starts(), w.chunk_lens):
-        chunks.append((f64(k[:, s0:s0 + ln]), f64(v[:, s0:s0 + ln]), np.arange(s0, s0 + ln)))
-    qf = f64(q[:, :n])
-    order = synthetic.ring_order(0, w.P)
-    # one head at a time, cycling over the 24 heads until the time budget is spent
-    done_heads, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        h = slice(done_heads % w.H, done_heads % w.H + 1)
-        oracle.ring_attention(qf[:, :, h], [(kc[:, :, h], vc[:, :, h], p) for kc, vc, p in chunks],
-                              order, 1 / math.sqrt(w.D))
-        done_heads += 1
+    rng = np.random.default_rng(1005)
+    S, D = w.S, w.D
+    mid = rng.choice(np.arange(512, S - 512), size=4096, replace=False)
+    rows = np.unique(np.concatenate([np.arange(512), mid, np.arange(S - 512, S)]))
+    kpos = np.arange(S)
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < w.H_local:
+        h = slice(done, done + 1)   # rank 0's heads are 0 .. H/P - 1
+        qh = f64(q[:, rows, h])
+        kh, vh = f64(k[:, :, h]), f64(v[:, :, h])
+        oracle.attention(qh, kh, vh, 1 / math.sqrt(D), causal=True, q_pos=rows, k_pos=kpos)
+        flops += 4.0 * D * float((rows + 1).sum())
+        done += 1
     dt = time.perf_counter() - t0
-    flops = attn_flops(n, w.S, done_heads, w.D, False)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
-            "sample": f"FLUX ring rank 0 (1152 rows x 4 chunks of 1152): {done_heads} single-head "
-                      f"passes ({done_heads / w.H:.2f} rank shares) of the fp64 numpy "
-                      f"ring_attention (chunk partials + LSE merge) in {dt:.1f} s"}
+            "sample": f"128K causal Ulysses rank 0: {done} of its {w.H_local} heads, "
+                      f"{len(rows)} query rows per head (first 512, last 512, 4096 seeded "
+                      f"random) against every visible key, fp64 numpy oracle.attention, "
+                      f"{flops / 1e9:.0f} GFLOP (visible pairs) in {dt:.1f} s"}
 
 
 def cpu_oracle_relayout(budget_s: float = 2.0):
@@ -204,19 +216,210 @@ def cpu_oracle_relayout(budget_s: float = 2.0):
                       f"(numpy transpose copy)"}
 
 
+def sample_sclk(torch, fn, seconds: float = 2.0):
+    """Graphics clock while `fn` runs back to back for ~`seconds`: amd-smi (else
+    rocm-smi) is queried from a side thread during the sustained run. Returns
+    (MHz or None, source/reason)."""
+    import re
+    import subprocess
+    import threading
+
+    readings, errors = [], []
+
+    def walk(x, path=""):
+        if isinstance(x, dict):
+            for key, val in x.items():
+                yield from walk(val, path + "/" + str(key).lower())
+        elif isinstance(x, list):
+            for val in x:
+                yield from walk(val, path)
+        else:
+            yield path, x
+
+    def query():
+        cmds = [["amd-smi", "metric", "-g", "0", "-c", "--json"],
+                ["rocm-smi", "-d", "0", "--showclocks", "--json"]]
+        for cmd in cmds:
+            try:
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+                data = json.loads(r.stdout)
+            except Exception as e:  # tool missing, no JSON, timeout
+                errors.append(f"{cmd[0]}: {type(e).__name__}")
+                continue
+            mhz = []
+            for path, val in walk(data):
+                # amd-smi: .../gfx_N/clk[/value]; rocm-smi: "sclk clock speed:" "(2100Mhz)"
+                if re.search(r"/gfx_\d+/clk(/value)?$", path) or "sclk clock speed" in path:
+                    m = re.search(r"(\d+(\.\d+)?)", str(val))
+                    if m and float(m.group(1)) > 100:
+                        mhz.append(float(m.group(1)))
+            if mhz:
+                readings.append((cmd[0], sum(mhz) / len(mhz)))
+                return
+            errors.append(f"{cmd[0]}: no clock field")
+
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set() and len(readings) < 3:
+            query()
+            if errors and not readings:
+                return
+
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds or (th.is_alive() and time.perf_counter() - t0 < 30):
+        fn()
+        n += 1
+        if n % 2 == 0:
+            torch.cuda.synchronize()
+        if not th.is_alive():
+            break
+    stop.set()
+    torch.cuda.synchronize()
+    th.join(timeout=30)
+    if readings:
+        vals = sorted(v for _, v in readings)
+        return vals[len(vals) // 2], f"{readings[0][0]} during back-to-back calls " \
+                                     f"({len(readings)} readings, median)"
+    return None, "; ".join(errors) or "no reading"
+
+
+def copy_ceiling(torch, cp, dev) -> float:
+    """GB/s (read + write) of a plain 16-byte streaming copy: the regrouping with
+    one rank is the identity permutation, so cp_ulysses_seq2head with P = 1 is
+    the library's own copy kernel. 512 MiB per launch, cold buffers."""
+    x = torch.empty((1, 1, 1 << 18, 8, 128), dtype=torch.bfloat16, device=dev).fill_(1.0)
+    nbytes = 2 * x.numel() * x.element_size()
+    pairs = rotating_pairs(x, x, nbytes)
+    d = time_rotating(torch, [lambda a=a, b=b: cp.ulysses_seq2head(a, 1, b) for a, b in pairs],
+                      1, 5)
+    del pairs, x
+    torch.cuda.empty_cache()
+    return nbytes / (d * 1e-3) / 1e9
+
+
+def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
+    """The 128K causal Ulysses rank's step: stacked seq2head of Q, K, V (all 8
+    ranks' regrouping), rank 0's causal attention on its 4 heads, head2seq of O
+    (rank 0's output in its slot; the other slots hold stand-in outputs)."""
+    w = synthetic.LLM_ULYSSES
+    P, S_l, H, D, Hl, S = w.P, w.S_local, w.H, w.D, w.H_local, w.S
+    log(f"{w.name}: inputs to the GPU")
+    qkv = torch.stack([x.view(P, 1, S_l, H, D) for x in qkv_cpu]).to(dev)  # [3][P][1][S_l][H][D]
+    heads = torch.empty((3, P, 1, S, Hl, D), dtype=w.dtype, device=dev)
+    o_all = torch.empty((P, 1, S, Hl, D), dtype=w.dtype, device=dev)
+    back = torch.empty((P, 1, S_l, H, D), dtype=w.dtype, device=dev)
+    lse = torch.empty((1, Hl, S), dtype=torch.float32, device=dev)
+    cp.ulysses_seq2head(qkv, P, heads)
+    o_all.copy_(heads[2])   # the other ranks' slots: their V head shards as stand-ins
+    rq, rk, rv, ro = heads[0, 0], heads[1, 0], heads[2, 0], o_all[0]
+    flops = 4.0 * D * Hl * causal_pairs_square(S)
+    relayout_bytes = 3 * 2 * qkv[0].numel() * qkv.element_size() + \
+        2 * o_all.numel() * o_all.element_size()
+
+    def attend():
+        cp.attn_chunk_partial(rq, rk, rv, ro, lse, causal=True, out_dtype=w.dtype)
+
+    def step(ev=None):
+        cp.ulysses_seq2head(qkv, P, heads)
+        if ev is not None:
+            ev[0].record()
+        attend()
+        if ev is not None:
+            ev[1].record()
+        cp.ulysses_head2seq(o_all, P, back)
+
+    log(f"{w.name}: warmup {warmup} steps, then >= {WARM_MS:.0f} ms of steps")
+    for _ in range(warmup):
+        step()
+    warm_ms_per_step = warm_up(torch, step)
+    # K steps back to back; an event pair around each attention launch (on the
+    # launch stream: torch's current stream, which the binding passes) gives
+    # the attention kernel's own duration inside the step
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        step(evs[i])
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    ms_step_ev = ev0.elapsed_time(ev1) / steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    relayout_ms = ms_step_ev - attn_ms
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms_step:.2f} ms/step ({value:.0f} TFLOP/s), attention kernel "
+        f"{attn_ms:.2f} ms ({achieved:.0f} TFLOP/s), regroupings {relayout_ms * 1e3:.0f} us")
+    # the regroupings alone, back to back over cold buffer sets, for their GB/s
+    s2h_qkv = time_rotating(torch, [lambda: cp.ulysses_seq2head(qkv, P, heads)], 1, 5)
+    h2s = time_rotating(torch, [lambda: cp.ulysses_head2seq(o_all, P, back)], 1, 5)
+    s2h_bytes = 3 * 2 * qkv[0].numel() * qkv.element_size()
+    h2s_bytes = 2 * o_all.numel() * o_all.element_size()
+    sclk, sclk_src = sample_sclk(torch, attend)
+    log(f"{w.name}: sclk {sclk} MHz ({sclk_src})")
+    res = {
+        "value": value, "ms_per_step": ms_step, "flops": flops,
+        "attn_ms": attn_ms, "achieved": achieved, "warm_ms_per_step": warm_ms_per_step,
+        "step_event_ms": ms_step_ev, "relayout_in_step_us": relayout_ms * 1e3,
+        "relayout_bytes_per_step": relayout_bytes,
+        "seq2head_qkv_us": s2h_qkv * 1e3,
+        "seq2head_qkv_gbs": s2h_bytes / (s2h_qkv * 1e-3) / 1e9,
+        "head2seq_us": h2s * 1e3, "head2seq_gbs": h2s_bytes / (h2s * 1e-3) / 1e9,
+        "sclk_mhz": sclk, "sclk_source": sclk_src,
+    }
+    del qkv, heads, o_all, back, lse, rq, rk, rv, ro
+    torch.cuda.empty_cache()
+    return res
+
+
+def flux_ring(torch, cp, synthetic, dev):
+    """FLUX ring rank 0 (detail entry with its own roofline): 1152 query rows over
+    4 chunks of 1152 in ring order, one cp_ring_attention call per step."""
+    w = synthetic.FLUX_RING
+    log(f"{w.name}: inputs")
+    q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
+    n = w.chunk_lens[0]
+    q0 = q[:, :n].contiguous()
+    starts = w.chunk_starts()
+    chunks = [(k[:, s:s + ln].contiguous(), v[:, s:s + ln].contiguous(), s)
+              for s, ln in zip(starts, w.chunk_lens)]
+    vis = [chunks[c] for c in synthetic.ring_order(0, w.P)]
+    o = torch.empty_like(q0)
+    lse = torch.empty((1, w.H, n), dtype=torch.float32, device=dev)
+    ws_bytes = cp.ring_attention_workspace_bytes(w.P, 1, w.H, n, w.D)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    flops = attn_flops(n, w.S, w.H, w.D, False)
+    ms = time_back_to_back(torch, lambda: cp.ring_attention(q0, vis, o, lse, workspace=ws), 5, 200)
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"{w.name}: kernel {ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s")
+    res = {"kernel_us": ms * 1e3, "tflops": achieved, "gflop": flops / 1e9,
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                        "traffic": traffic_record(FLUX_TRAFFIC_FILE),
+                        "kernel": "attn_bf16_kernel<128, causal=false, out_bf16=true>"}}
+    return res, q0, vis
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # defaults: 500 warmup steps (~40 ms) bring the GPU to its steady clocks before
-    # the timed region; 1000 timed steps take ~80 ms
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=500)
+    # one step is ~20 ms; each timed region is preceded by >= 30 ms of warm-up
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
-                    help="run only this detail workload (qwen, wan, llm, overlap, ra, merge, "
-                         "anything, kvgather, unified, bwd) "
-                         "after the "
-                         "headline; for profiling")
+                    help="run only this detail workload (flux, qwen, wan, overlap, ra, merge, "
+                         "anything, kvgather, unified, bwd) after the headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
@@ -224,6 +427,9 @@ def main() -> int:
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
         return 2
 
     import torch
@@ -242,71 +448,59 @@ def main() -> int:
         log("copied 256 MiB x 5 (read 268435456 B, write 268435456 B per launch)")
         return 0
     # ---------------------------------------------------------------- headline
-    w = synthetic.FLUX_RING
-    log(f"{w.name}: inputs")
-    q, k, v = (x.to(dev) for x in synthetic.make_qkv(w))
-    n = w.chunk_lens[0]
-    q0 = q[:, :n].contiguous()
-    starts = w.chunk_starts()
-    chunks = [(k[:, s:s + ln].contiguous(), v[:, s:s + ln].contiguous(), s)
-              for s, ln in zip(starts, w.chunk_lens)]
-    order = synthetic.ring_order(0, w.P)
-    vis = [chunks[c] for c in order]
-    o = torch.empty_like(q0)
-    lse = torch.empty((1, w.H, n), dtype=torch.float32, device=dev)
-    ws_bytes = cp.ring_attention_workspace_bytes(w.P, 1, w.H, n, w.D)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    step = lambda: cp.ring_attention(q0, vis, o, lse, workspace=ws)
-    flops = attn_flops(n, w.S, w.H, w.D, False)
-    log(f"{w.name}: warmup {args.warmup}, timed {args.steps}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # One event pair on the launch stream brackets the whole timed region: the
-    # steps run back to back, so the per-launch duration is the bracket / K
-    # (a pair of events around every launch would add its own overhead).
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    launch_ms = ev0.elapsed_time(ev1) / args.steps
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (launch_ms * 1e-3) / 1e12
-    log(f"{w.name}: {ms_step * 1e3:.1f} us/step, kernel {launch_ms * 1e3:.1f} us, "
-        f"{achieved:.1f} TFLOP/s")
+    w = synthetic.LLM_ULYSSES
+    log(f"{w.name}: drawing inputs on the host")
+    qkv_cpu = synthetic.make_qkv(w)
+    h = headline(torch, cp, synthetic, dev, args.steps, args.warmup, qkv_cpu)
+    copy_gbs = copy_ceiling(torch, cp, dev)
+    log(f"copy ceiling {copy_gbs:.0f} GB/s")
 
-    detail = {"flux_ring_rank0": {"us_per_step": ms_step * 1e3, "kernel_us": launch_ms * 1e3,
-                                  "tflops": achieved, "gflop": flops / 1e9}}
+    detail = {}
     if not args.quick:
-        detail.update(other_workloads(torch, cp, synthetic, dev, q0, vis, w, args.only))
+        if args.only in (None, "flux", "merge", "bwd"):
+            fl, q0, vis = flux_ring(torch, cp, synthetic, dev)
+            detail["flux_ring_rank0"] = fl
+        else:
+            q0 = vis = None
+        detail.update(other_workloads(torch, cp, synthetic, dev, q0, vis, synthetic.FLUX_RING,
+                                      args.only))
 
     traffic = traffic_record()
+    sclk = h["sclk_mhz"]
     line = {
         "metric": "attention TFLOP/s (bf16, 1 MI355X) + % MFMA peak; relayout GB/s",
-        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "value": h["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic N(0,1) inputs, seed 1002, rounded to bf16",
-        "config": {"workload": "flux-1024x1024 ring rank 0 of ring_degree=4: B=1 H=24 D=128 "
-                               "S=4608, Q 1152 rows x 4 K/V chunks of 1152 in order [0,3,2,1], "
-                               "fused fp32 LSE merge, non-causal",
-                   "global_batch": 1, "seq_len": w.S, "parallelism": "one ring rank (P=4)"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        "data": "synthetic N(0,1) inputs, seed 1005, rounded to bf16",
+        "config": {"workload": "128K-token causal LLM, Ulysses SP8 rank 0: S=131072 H=32 "
+                               "(4 heads per rank) D=128 bf16, causal from positions; step = "
+                               "seq2head of Q, K, V [8][1][16384][32][128] -> "
+                               "[8][1][131072][4][128] (one launch), rank-0 attention, "
+                               "head2seq of O",
+                   "global_batch": 1, "seq_len": w.S, "parallelism": "one Ulysses rank (P=8)"},
+        "roofline": {"bound": "mfma", "achieved": h["achieved"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": h["achieved"] / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "attn_bf16_kernel<128, causal=false, out_bf16=true>",
-                     "flop_per_launch": flops},
+                     "kernel": "attn_bf16_kernel<128, causal=true, out_bf16=true, groups=1>",
+                     "flop_per_launch": h["flops"], "kernel_ms": h["attn_ms"],
+                     "measured_sclk_mhz": sclk, "sclk_source": h["sclk_source"],
+                     "peak_at_measured_sclk": (PEAK_BF16_TFLOPS * sclk / 2400.0
+                                               if sclk else None)},
+        "relayout": {"seq2head_qkv_gbs": h["seq2head_qkv_gbs"],
+                     "seq2head_qkv_hbm_frac": h["seq2head_qkv_gbs"] / PEAK_HBM_GBS,
+                     "head2seq_gbs": h["head2seq_gbs"],
+                     "head2seq_hbm_frac": h["head2seq_gbs"] / PEAK_HBM_GBS,
+                     "seq2head_qkv_us": h["seq2head_qkv_us"], "head2seq_us": h["head2seq_us"],
+                     "in_step_us": h["relayout_in_step_us"],
+                     "copy_ceiling_gbs": copy_gbs,
+                     "copy_ceiling_hbm_frac": copy_gbs / PEAK_HBM_GBS},
+        "warm_ms_per_step": h["warm_ms_per_step"],
         "detail": detail,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
-        line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"] = cpu_baseline(qkv_cpu)
         detail["cpu_oracle_relayout"] = cpu_oracle_relayout()
     print(json.dumps(line), flush=True)
     return 0
@@ -318,12 +512,12 @@ def other_workloads(torch, cp, synthetic, dev, q0, vis, wf, only=None):
     # standalone merge of the FLUX ring's 4 fp32 partials (HBM-bound)
     if want("merge"):
         out.update(merge_workload(torch, cp, dev, q0, vis, wf))
-    tags = {synthetic.QWEN_ULYSSES.name: "qwen", synthetic.WAN_ULYSSES.name: "wan",
-            synthetic.LLM_ULYSSES.name: "llm"}
-    for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES, synthetic.LLM_ULYSSES):
+    # (the 128K causal Ulysses rank is the headline)
+    tags = {synthetic.QWEN_ULYSSES.name: "qwen", synthetic.WAN_ULYSSES.name: "wan"}
+    for w in (synthetic.QWEN_ULYSSES, synthetic.WAN_ULYSSES):
         if want(tags[w.name]):
             out[w.name] = ulysses_workload(torch, cp, synthetic, dev, w)
-    if want("overlap"):
+    if only == "overlap":   # two-stream layer pipelining: on request only
         out["qwen-image-1536-ulysses4-stream-overlap"] = stream_overlap_workload(
             torch, cp, synthetic, dev)
     if want("ra"):
