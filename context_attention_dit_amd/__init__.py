@@ -9,6 +9,8 @@ Entry points (same names as the C ABI, without the ``cp_`` prefix):
   attn_chunk_partial   one ring hop: (O_c, LSE_c) of Q over one K/V chunk
   lse_merge            merge of P fp32 partials into full attention
   ring_attention       one ring rank: Q over P chunks in visit order, fused fp32 merge
+  ring_attention_noalloc
+                       the same with the library's static scratch (allocates nothing)
   ulysses_seq2head     Ulysses regrouping before attention (all P ranks)
   ulysses_head2seq     Ulysses regrouping after attention (inverse)
                        (both also take a stack of tensors, e.g. Q, K, V, in one launch)
@@ -45,6 +47,7 @@ CP_BF16, CP_F32 = 0, 1
 STATUS = {0: "CP_OK", 1: "CP_E_INVALID", 2: "CP_E_UNSUPPORTED", 3: "CP_E_DIVISIBILITY",
           4: "CP_E_WORKSPACE", 5: "CP_E_HIP"}
 MAX_RING_CHUNKS = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CP_NOALLOC_SCRATCH_BYTES
 BWD_ACCUMULATE_DQ, BWD_ACCUMULATE_DKV = 1, 2
 
 _i64, _vp, _f32, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
@@ -71,6 +74,9 @@ _lse_merge = _sig("cp_lse_merge", [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _
 _ring_ws = _sig("cp_ring_attention_workspace_bytes", [_i64] * 5, ctypes.c_size_t)
 _ring = _sig("cp_ring_attention", [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp, _i64, _i64, _i64,
                                    _i64, _int, _f32, _int, _i64, _vp, ctypes.c_size_t, _vp])
+_ring_noalloc = _sig("cp_ring_attention_noalloc",
+                     [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                      _f32, _int, _i64, _vp])
 _seq2head = _sig("cp_ulysses_seq2head", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _head2seq = _sig("cp_ulysses_head2seq", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _seq2head_n = _sig("cp_ulysses_seq2head_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
@@ -251,6 +257,34 @@ def ring_attention(q: torch.Tensor, chunks: Sequence[Tuple[torch.Tensor, torch.T
         # the workspace was allocated on the current stream but is used on `stream`:
         # keep the caching allocator from reusing it before that work is done
         workspace.record_stream(stream)
+    return o, lse
+
+
+def ring_attention_noalloc(q: torch.Tensor,
+                           chunks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
+                           o: torch.Tensor, lse: torch.Tensor, *, scale: Optional[float] = None,
+                           causal: bool = False, q_pos0: int = 0,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``ring_attention`` through cp_ring_attention_noalloc: the library keeps the
+    key-split partials in its static device scratch, so the call allocates
+    nothing (``o`` and ``lse`` are required). Calls that overlap on one GPU race."""
+    B, Sq, H, D = _bshd(q, "q")
+    arr = (KVChunk * max(1, len(chunks)))()
+    for c, (k, v, pos0) in enumerate(chunks):
+        Bk, L, Hk, Dk = _bshd(k, "k")
+        if (Bk, Hk, Dk) != (B, H, D) or tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"chunk {c} shape disagrees with q")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise TypeError(f"chunk {c} dtype disagrees with q")
+        _want(k, f"chunk {c} k", k.shape, q.dtype, q.device)
+        _want(v, f"chunk {c} v", k.shape, q.dtype, q.device)
+        arr[c] = KVChunk(_ptr(k), _ptr(v), k.shape[1], int(pos0))
+    _want(o, "o", (B, Sq, H, D), q.dtype, q.device)
+    _want(lse, "lse", (B, H, Sq), torch.float32, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check("cp_ring_attention_noalloc", _ring_noalloc(
+        _ptr(q), arr, len(chunks), _ptr(o), _ptr(lse), B, H, Sq, D, _dtype_code(q.dtype), scale,
+        int(causal), q_pos0, _stream(stream)))
     return o, lse
 
 

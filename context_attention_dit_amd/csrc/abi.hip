@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "cp_internal.h"
@@ -198,11 +199,25 @@ size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_
   return static_cast<size_t>(cpattn::attn_split_floats(s, B, H, Sq, D)) * sizeof(float);
 }
 
-cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
-                            float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
-                            cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "cp_ring_attention";
+}  // extern "C"
+
+namespace {
+
+// Workspace cp_ring_attention needs for a call: the bf16 kernel's key-split
+// partials; the fp32 path never splits, so it needs none.
+size_t ring_workspace_need(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                           cp_dtype in_dtype) {
+  return in_dtype == CP_BF16 ? cp_ring_attention_workspace_bytes(P, B, H, Sq, D) : 0;
+}
+
+// Body of cp_ring_attention and cp_ring_attention_noalloc. `scratch_source`
+// (non-null for the no-alloc entry point) yields the device scratch used as
+// workspace, after every argument has been validated.
+cp_status ring_attention_impl(const char* fn, const void* q, const cp_kv_chunk* chunks, int64_t P,
+                              void* o, float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                              cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              cp_status (*scratch_source)(const char*, void**, size_t*)) {
   cp_status s = check_attn_common(fn, B, H, Sq, D, in_dtype, causal, scale);
   if (s != CP_OK) return s;
   if (P < 0) return fail(CP_E_INVALID, "%s: negative P", fn);
@@ -210,11 +225,17 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
     return fail(CP_E_UNSUPPORTED, "%s: P=%lld exceeds %d chunks", fn, (long long)P,
                 CP_MAX_RING_CHUNKS);
   if (P > 0 && !chunks) return fail(CP_E_INVALID, "%s: null chunk array", fn);
-  // the fp32 path never splits keys: only bf16 calls need the workspace
-  const size_t need = in_dtype == CP_BF16 ? cp_ring_attention_workspace_bytes(P, B, H, Sq, D) : 0;
-  if (workspace_bytes < need || (need > 0 && !workspace))
+  const size_t need = ring_workspace_need(P, B, H, Sq, D, in_dtype);
+  if (scratch_source) {
+    if (need > static_cast<size_t>(CP_NOALLOC_SCRATCH_BYTES))
+      return fail(CP_E_WORKSPACE,
+                  "%s: these sizes need %zu bytes of key-split scratch, above the built-in "
+                  "%lld bytes; call cp_ring_attention with a workspace instead",
+                  fn, need, (long long)CP_NOALLOC_SCRATCH_BYTES);
+  } else if (workspace_bytes < need || (need > 0 && !workspace)) {
     return fail(CP_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace_bytes);
+  }
   if (need > 0 && !aligned(workspace, 16))
     return fail(CP_E_INVALID, "%s: workspace must be 16-byte aligned", fn);
   const int64_t es = elem_size(in_dtype);
@@ -266,6 +287,11 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
     a.chunks[c].delta = clamp_delta(q_pos0, chunks[c].pos0, Sq, chunks[c].len);
     tiles += (chunks[c].len + 63) / 64;
   }
+  if (scratch_source && need > 0) {
+    // every argument is valid: only now fetch (and on first use look up) the scratch
+    s = scratch_source(fn, &workspace, &workspace_bytes);
+    if (s != CP_OK) return s;
+  }
   a.nsplit = 1;
   a.groups = 1;
   if (in_dtype == CP_BF16) {
@@ -278,6 +304,68 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
   }
   return launch_attention(fn, a, in_dtype, in_dtype == CP_BF16, causal,
                           static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
+                            float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                            cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return ring_attention_impl("cp_ring_attention", q, chunks, P, o, lse, B, H, Sq, D, in_dtype,
+                             scale, causal, q_pos0, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-alloc
+// cp_ring_attention_noalloc keeps its key-split partials in this file-scope
+// device array instead of a caller workspace. Each GPU the library runs on
+// holds its own copy (at its own address) until the process ends. In host
+// code `scratch` only names the symbol: its device address on the current
+// device comes from hipGetSymbolAddress, looked up once per device and kept
+// in g_scratch_addr; kernels are only ever given that address.
+namespace {
+
+static __device__ __align__(256) char scratch[CP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+cp_status noalloc_scratch(const char* fn, void** ptr, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CP_E_UNSUPPORTED, "%s: device %d beyond the %d the scratch table covers", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p) return fail(CP_E_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  *bytes = static_cast<size_t>(CP_NOALLOC_SCRATCH_BYTES);
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_ring_attention_noalloc(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
+                                    float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                                    cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                                    void* stream) {
+  return ring_attention_impl("cp_ring_attention_noalloc", q, chunks, P, o, lse, B, H, Sq, D,
+                             in_dtype, scale, causal, q_pos0, nullptr, 0, stream,
+                             noalloc_scratch);
 }
 
 static cp_status relayout(const char* fn, const void* in, void* out, int64_t count, int64_t P,

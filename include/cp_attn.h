@@ -16,7 +16,8 @@
  *    key has LSE = -inf and output 0 (never NaN).
  *  - Device pointers are plain device addresses (from hipMalloc or PyTorch).
  *    The caller allocates and owns every device buffer; the library never
- *    allocates or frees device memory. Outputs must not overlap inputs.
+ *    allocates or frees device memory (cp_ring_attention_noalloc keeps its
+ *    scratch in a static device array instead). Outputs must not overlap inputs.
  *    Tensor pointers must be 16-byte aligned; LSE pointers 4-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued on it and no call synchronises: results are valid once
@@ -161,6 +162,36 @@ cp_status cp_ring_attention(const void* q, const cp_kv_chunk* chunks, int64_t P,
                             float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
                             cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the device scratch array cp_ring_attention_noalloc uses (64 MiB). */
+#define CP_NOALLOC_SCRATCH_BYTES 67108864
+
+/*
+ * cp_ring_attention_noalloc — cp_ring_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and no call on its
+ * path allocates or frees memory.
+ *
+ *   Every argument, rule and result is that of cp_ring_attention (same
+ *   kernels, bit-identical outputs), except the workspace: the key-split
+ *   partials live in a file-scope device array of CP_NOALLOC_SCRATCH_BYTES
+ *   that each GPU holds from its first use until the process ends. Sizes
+ *   whose workspace (cp_ring_attention_workspace_bytes) exceeds that limit
+ *   are rejected with CP_E_WORKSPACE before anything is enqueued.
+ *   The array's device address is looked up (hipGetSymbolAddress) on the
+ *   first call that needs it on each device, with that device current: make
+ *   that first call outside graph capture. Work runs on the CURRENT device,
+ *   which must be the stream's.
+ *   Every call on one GPU shares that GPU's array: calls that can overlap in
+ *   time on one GPU (other streams, other threads, other processes' streams
+ *   are separate arrays) race and give undefined results; serialise them on
+ *   one stream. Nothing in the array needs clearing between calls (each split
+ *   writes its whole partial before the merge reads it).
+ */
+cp_status cp_ring_attention_noalloc(const void* q, const cp_kv_chunk* chunks, int64_t P, void* o,
+                                    float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                                    cp_dtype in_dtype, float scale, int causal, int64_t q_pos0,
+                                    void* stream);
 
 /*
  * cp_ulysses_seq2head — the Ulysses regrouping before attention, for all P

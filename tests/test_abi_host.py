@@ -153,6 +153,32 @@ def test_ring_fp32_needs_no_workspace():
     assert "misaligned" in cp.last_error()
 
 
+def test_noalloc_scratch_size_matches_header():
+    m = re.search(r"#define\s+CP_NOALLOC_SCRATCH_BYTES\s+(\d+)", open(HEADER).read())
+    assert cp.NOALLOC_SCRATCH_BYTES == int(m.group(1))
+
+
+def _ring_noalloc(P=4, q=FAKE, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, D=128, dt=BF16, scale=0.1,
+                  causal=0):
+    chunks = [(FAKE2 + c * 4096, FAKE3 + c * 4096, 8, 8 * c) for c in range(max(P, 0))]
+    arr = (cp.KVChunk * max(1, len(chunks)))(*[cp.KVChunk(*c) for c in chunks])
+    return cp._ring_noalloc(q, arr, P, o, lse, B, H, Sq, D, dt, scale, causal, 0, None)
+
+
+def test_noalloc_rejects_before_any_launch():
+    assert _ring_noalloc(Sq=0) == OK
+    assert _ring_noalloc(P=-1) == INVALID
+    assert cp.last_error().startswith("cp_ring_attention_noalloc")
+    assert _ring_noalloc(q=None) == INVALID
+    # sizes whose key-split partials exceed the static scratch: rejected with
+    # CP_E_WORKSPACE, whatever the chunks
+    Sq = next(t * 128 for t in range(257, 100000)
+              if cp.ring_attention_workspace_bytes(4, 1, 1, t * 128, 128)
+              > cp.NOALLOC_SCRATCH_BYTES)
+    assert _ring_noalloc(H=1, Sq=Sq) == WORKSPACE
+    assert "scratch" in cp.last_error()
+
+
 def _relayout(fn, inp=FAKE, out=FAKE2, P=4, B=1, S=8, H=8, D=128, dt=BF16):
     return fn(inp, out, P, B, S, H, D, dt, None)
 
