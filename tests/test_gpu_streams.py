@@ -64,3 +64,49 @@ def test_attention_and_relayout_on_two_streams():
     for l in range(L):
         for name, got, exp in zip(("heads", "O", "LSE"), (heads[l], o[l], lse[l]), want[l]):
             assert torch.equal(_bits(got), _bits(exp)), f"layer {l}: {name}"
+
+
+def test_ring_own_workspace_on_side_stream():
+    """ring_attention() allocating its own key-split workspace while launching on a
+    side stream: the current stream immediately reallocates and overwrites freed
+    blocks of the same size, which must not reach the ring's partials."""
+    import math
+
+    import numpy as np
+
+    import oracle
+    from tests._parity import BF16_MAX, LSE_MAX, to_f64
+
+    H, Sq, D, lens = 32, 1025, 128, [1025, 1025, 1025, 1024]
+    bf = torch.bfloat16
+    need = cp.ring_attention_workspace_bytes(len(lens), 1, H, Sq, D)
+    assert need > 0
+    say(f"ring on a side stream, binding-allocated workspace of {need} bytes")
+    q = synthetic.make_tensor((1, Sq, H, D), bf, 2500).to(DEV)
+    k = synthetic.make_tensor((1, sum(lens), H, D), bf, 2501).to(DEV)
+    v = synthetic.make_tensor((1, sum(lens), H, D), bf, 2502).to(DEV)
+    chunks, s0 = [], 0
+    for n in lens:
+        chunks.append((k[:, s0:s0 + n].contiguous(), v[:, s0:s0 + n].contiguous(), s0))
+        s0 += n
+    ref_o, ref_l = cp.ring_attention(q, chunks)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for rep in range(4):
+        o = torch.empty_like(q)
+        lse = torch.empty((1, H, Sq), dtype=torch.float32, device=DEV)
+        side.wait_stream(torch.cuda.current_stream())
+        cp.ring_attention(q, chunks, o, lse, stream=side)
+        # the binding's workspace is out of scope now: grab blocks of its size on
+        # the current stream and fill them while the side stream still runs
+        junk = [torch.full((need // 4,), float("nan"), device=DEV) for _ in range(4)]
+        outs.append((o, lse, junk))
+    torch.cuda.synchronize()
+    for o, lse, _ in outs:
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
+        assert torch.equal(lse, ref_l)
+    rows = np.array([0, 1, 511, 1024])
+    wo, wl = oracle.attention(to_f64(q)[:, rows], to_f64(k), to_f64(v), 1 / math.sqrt(D))
+    assert np.abs(to_f64(ref_o)[:, rows] - wo).max() <= BF16_MAX
+    assert np.abs(to_f64(ref_l)[:, :, rows] - wl).max() <= LSE_MAX
