@@ -170,6 +170,7 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
   if (!valid_dtype(o_dtype)) return fail(CP_E_INVALID, "%s: unknown o_dtype %d", fn, o_dtype);
   if (D % 4 != 0) return fail(CP_E_UNSUPPORTED, "%s: D=%lld is not a multiple of 4", fn,
                               (long long)D);
+  if (D > 4096) return fail(CP_E_UNSUPPORTED, "%s: D=%lld exceeds 4096", fn, (long long)D);
   if (B == 0 || H == 0 || Sq == 0 || D == 0) return ok();
   if (sat_mul({B, Sq, H, D / 4}) >= kMaxGrid || sat_mul({P, B, Sq, H, D, 4}) >= INT64_MAX / 2)
     return fail(CP_E_UNSUPPORTED, "%s: tensor too large for one launch", fn);

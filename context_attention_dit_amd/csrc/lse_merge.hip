@@ -12,9 +12,12 @@
 // HBM-bound: every partial element is read once. A row's D floats are split
 // over D/8 lanes (D/4 when D is not a multiple of 8), each lane owning two
 // float4 columns half a row apart in every partial, so each load instruction
-// of a wave covers contiguous stretches of rows. A lane issues all its O
-// loads before the weights are known, so they overlap the LSE loads and the
-// weight arithmetic, done in base 2 on the hardware exp2/log2. The P
+// of a wave covers whole rows. A block takes R consecutive query rows of one
+// head, so its LSE loads and stores are contiguous, and consecutive blocks
+// take the next heads of the same query rows, so the blocks in flight cover
+// contiguous stretches of O ([b][i][h][d]) together. A lane issues all
+// its O loads before the weights are known, so they overlap the LSE loads and
+// the weight arithmetic, done in base 2 on the hardware exp2/log2. The P
 // partials are summed in the fixed order c = 0..P-1 (deterministic).
 #include "cp_internal.h"
 
@@ -30,22 +33,25 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Thread layout: `cols` = D/(4*NC) threads per row; a thread owns the NC
 // float4 columns col, col + cols, ... of that row in every partial, so each
-// of its loads is, across a wave, a contiguous stretch of rows.
+// of its loads covers, across a wave, whole rows of O.
+// Block x covers rows i = t*R .. t*R + R-1 of head h in batch b, where
+// x = (b*T + t)*H + h (T = ceil(Sq/R) row tiles of R = blockDim.x / cols rows).
 template <bool OUT_BF16, int NC>
-__global__ __launch_bounds__(kThreads) void lse_merge_kernel(
+__global__ __launch_bounds__(1024) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int P,
-    void* __restrict__ o, float* __restrict__ lse, uint32_t rows, FastDiv heads, FastDiv seq,
+    void* __restrict__ o, float* __restrict__ lse, uint32_t Sq, FastDiv heads, FastDiv tiles,
     FastDiv cols, int64_t part_stride_o, int64_t part_stride_l) {
-  const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t row = cols.div(gid);           // row = (b*Sq + i)*H + h
-  if (row >= rows) return;
-  const uint32_t col = gid - row * cols.d;      // first float4 column
-  const uint32_t seg = cols.d;                  // distance between a thread's columns
-  const uint32_t bi = heads.div(row);
-  const uint32_t h = row - bi * heads.d;
-  const uint32_t b = seq.div(bi);
-  const uint32_t i = bi - b * seq.d;
-  const int64_t lrow = (static_cast<int64_t>(b) * heads.d + h) * seq.d + i;  // [b][h][i]
+  const uint32_t bt = heads.div(blockIdx.x);
+  const uint32_t h = blockIdx.x - bt * heads.d;
+  const uint32_t b = tiles.div(bt);
+  const uint32_t t = bt - b * tiles.d;
+  const uint32_t r = cols.div(threadIdx.x);
+  const uint32_t col = threadIdx.x - r * cols.d;  // first float4 column
+  const uint32_t seg = cols.d;                    // distance between a thread's columns
+  const uint32_t i = t * (blockDim.x / cols.d) + r;
+  if (i >= Sq) return;
+  const uint32_t lrow = (b * heads.d + h) * Sq + i;    // LSE index: (b*H + h)*Sq + i
+  const uint32_t row = (b * Sq + i) * heads.d + h;     // O row: (b*Sq + i)*H + h
 
   const f32x4* src = reinterpret_cast<const f32x4*>(o_parts) + static_cast<int64_t>(row) * NC * seg + col;
   const int64_t so = part_stride_o / 4;
@@ -120,21 +126,23 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(
 template <bool OUT_BF16, int NC>
 void launch_nc(const float* o_parts, const float* lse_parts, int P, void* o, float* lse,
                int64_t B, int64_t H, int64_t Sq, int64_t D, hipStream_t stream) {
-  const uint32_t rows = static_cast<uint32_t>(B * Sq * H);
-  FastDiv heads, seq, cols;
+  const int64_t ncols = D / (4 * NC);         // <= 1024 (D <= 4096)
+  const int64_t R = ncols < kThreads ? kThreads / ncols : 1;  // rows per block
+  const int64_t T = (Sq + R - 1) / R;
+  FastDiv heads, tiles, cols;
   heads.init(static_cast<uint32_t>(H));
-  seq.init(static_cast<uint32_t>(Sq));
-  cols.init(static_cast<uint32_t>(D / (4 * NC)));
-  const int64_t threads = static_cast<int64_t>(rows) * (D / (4 * NC));
-  const uint32_t blocks = static_cast<uint32_t>((threads + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL((lse_merge_kernel<OUT_BF16, NC>), dim3(blocks), dim3(kThreads), 0, stream,
-                     o_parts, lse_parts, P, o, lse, rows, heads, seq, cols, B * Sq * H * D,
+  tiles.init(static_cast<uint32_t>(T));
+  cols.init(static_cast<uint32_t>(ncols));
+  const uint32_t blocks = static_cast<uint32_t>(B * T * H);
+  hipLaunchKernelGGL((lse_merge_kernel<OUT_BF16, NC>), dim3(blocks),
+                     dim3(static_cast<uint32_t>(ncols * R)), 0, stream, o_parts, lse_parts, P, o,
+                     lse, static_cast<uint32_t>(Sq), heads, tiles, cols, B * Sq * H * D,
                      B * H * Sq);
 }
 
 }  // namespace
 
-// Caller guarantees: P >= 1, D % 4 == 0, B*Sq*H*(D/4) < 2^31.
+// Caller guarantees: P >= 1, D % 4 == 0, D <= 4096, B*Sq*H*(D/4) < 2^31.
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, void* o,
                             float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, bool out_bf16,
                             hipStream_t stream) {

@@ -111,8 +111,8 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
  *
  *   o_parts [P][B][Sq][H][D] fp32, lse_parts [P][B][H][Sq] fp32 (P >= 1).
  *   o [B][Sq][H][D] in o_dtype (CP_F32, or CP_BF16 rounded to nearest even);
- *   lse [B][H][Sq] fp32. D must be a multiple of 4. The partials are combined
- *   in the fixed order c = 0..P-1.
+ *   lse [B][H][Sq] fp32. D must be a multiple of 4 and at most 4096. The
+ *   partials are combined in the fixed order c = 0..P-1.
  */
 cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, void* o,
                        float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, cp_dtype o_dtype,

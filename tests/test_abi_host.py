@@ -95,6 +95,7 @@ def _merge(o_parts=FAKE, lse_parts=FAKE2, P=4, o=FAKE3, lse=FAKE4, B=1, H=2, Sq=
 
 @pytest.mark.parametrize("kw,status", [
     (dict(P=0), INVALID), (dict(P=-1), INVALID), (dict(D=6), UNSUPPORTED), (dict(o=None), INVALID),
+    (dict(D=4100), UNSUPPORTED),
     (dict(lse_parts=FAKE2 + 2), INVALID), (dict(o=FAKE + 128), INVALID), (dict(odt=3), INVALID),
     (dict(B=-2), INVALID),
 ])

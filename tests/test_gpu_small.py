@@ -157,7 +157,8 @@ def test_kv_gather_bit_exact(s_lens, B, H, D):
 
 @pytest.mark.parametrize("P,D", [(1, 128), (2, 128), (4, 128), (7, 128), (8, 64),
                                  (11, 128),          # more partials than the unrolled fast path
-                                 (3, 12), (9, 4)])   # D not a multiple of 8: one column per lane
+                                 (3, 12), (9, 4),    # D not a multiple of 8: one column per lane
+                                 (2, 1000), (3, 4096), (2, 4092)])  # wide rows: R = 2, 1, 1
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_merge_matches_oracle(P, D, out_dtype):
     say(f"merge P={P} D={D} out={out_dtype}")
