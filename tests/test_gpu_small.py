@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synthetic
-from tests._parity import (check_lse, check_o, kind_of, say, to_f64)
+from tests._parity import (check_lse, check_o, check_o_scaled, kind_of, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,6 +215,50 @@ def test_chunk_partial(case, in_dtype, out_dtype):
     kind = "bf16" if (in_dtype == torch.bfloat16) else "f32"
     check_o(o, wo, kind)
     check_lse(lse, wl)
+
+
+@pytest.mark.parametrize("scale_of", [lambda D: -1 / math.sqrt(D), lambda D: 0.0,
+                                      lambda D: -0.37])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("in_dtype,out_dtype", [(torch.bfloat16, torch.float32),
+                                                (torch.bfloat16, torch.bfloat16),
+                                                (torch.float32, torch.float32)])
+def test_forward_negative_and_zero_scale(scale_of, causal, in_dtype, out_dtype):
+    """A negative scale flips the sign of every score (the bf16 kernel folds it
+    into Q); a zero scale gives uniform weights over the visible keys (O is
+    their V mean, LSE = ln of their count). Per-hop partial and ring. The fp32
+    partials of bf16 inputs are held to the absolute bf16 bars; bf16-rounded
+    outputs (the ring's O, bf16 partials) to the scaled bars."""
+    B, Sq, Skv, H, D = 1, 150, 211, 2, 128
+    scale = scale_of(D)
+    say(f"forward scale={scale:.4f} causal={causal} {in_dtype}->{out_dtype}")
+    q, k, v = _qkv(B, Sq, Skv, H, D, in_dtype, seed=911)
+    qp, kp = (60, 0) if causal else (0, 0)
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal,
+                                   q_pos0=qp, kv_pos0=kp, out_dtype=out_dtype)
+    lens = (90, 121)
+    kd, vd = k.to(DEV), v.to(DEV)
+    chunks = [(kd[:, :lens[0]].contiguous(), vd[:, :lens[0]].contiguous(), kp),
+              (kd[:, lens[0]:].contiguous(), vd[:, lens[0]:].contiguous(), kp + lens[0])]
+    ro, rl = cp.ring_attention(q.to(DEV), chunks[::-1], scale=scale, causal=causal, q_pos0=qp)
+    torch.cuda.synchronize()
+    wo, wl = oracle.chunk_partial(to_f64(q), to_f64(k), to_f64(v), scale, causal,
+                                  np.arange(qp, qp + Sq), np.arange(kp, kp + Skv))
+    # bf16-rounded outputs: the scaled bars (a large |scale| makes the softmax
+    # peaky and O close to single V rows, not small); fp32 outputs: absolute
+    if out_dtype == torch.bfloat16:
+        check_o_scaled(o, wo, "partial O")
+    else:
+        check_o(o, wo, "bf16" if in_dtype == torch.bfloat16 else "f32", "partial O")
+    check_lse(lse, wl)
+    if in_dtype == torch.bfloat16:
+        check_o_scaled(ro, wo, "ring O")
+    else:
+        check_o(ro, wo, "f32", "ring O")
+    check_lse(rl, wl, "ring LSE")
+    if scale == 0.0:   # closed form: uniform weights over the visible keys
+        counts = np.array([min(Skv, qp + i - kp + 1) if causal else Skv for i in range(Sq)])
+        assert np.abs(to_f64(lse)[0, 0] - np.log(np.maximum(counts, 1))).max() <= 1e-4
 
 
 @pytest.mark.parametrize("in_dtype", [torch.bfloat16, torch.float32])

@@ -195,18 +195,19 @@ def test_kv_gather_wan_rank0():
         check_lse(lse[:, :, idx], wl, f"rank 0 LSE ({tag})")
 
 
-def test_unified_flux_segment0():
+def test_unified_flux_both_segments():
     """FLUX 1024x1024 as Ulysses 2 x ring 2. Ring segment r (2304 tokens) is
     spread over U = 2 Ulysses ranks; within the segment the Ulysses regrouping
     gives each rank all 2304 tokens for 12 heads, ring attention runs over
     both segments' K/V for those heads, and the inverse regrouping returns
-    every rank its own 1152 tokens for all 24 heads. Checked for both ranks of
-    segment 0 against the oracle on sampled rows."""
+    every rank its own 1152 tokens for all 24 heads. Checked for all four
+    ranks (both ranks of both segments): O after the inverse regrouping and
+    each rank's LSE, against the oracle on sampled rows."""
     w = synthetic.FLUX_UNIFIED
     R = len(w.chunk_lens)
     U = w.P // R
     S, H, D, seg = w.S, w.H, w.D, w.chunk_lens[0]
-    sub = seg // U
+    sub, Hu = seg // U, H // U
     say(f"{w.name}: generating inputs")
     q, k, v = synthetic.make_qkv(w)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -216,18 +217,24 @@ def test_unified_flux_segment0():
     for name, x in (("q", qd), ("k", kd), ("v", vd)):
         grp[name] = [cp.ulysses_seq2head(x[:, r * seg:(r + 1) * seg].reshape(U, 1, sub, H, D), U)
                      for r in range(R)]
-    r = 0
-    outs = []
-    for u in range(U):
-        chunks = [(grp["k"][c][u], grp["v"][c][u], c * seg) for c in range(R)]
-        say(f"{w.name}: ring attention for rank (ring {r}, ulysses {u})")
-        o, lse = cp.ring_attention(grp["q"][r][u].contiguous(),
-                                   [chunks[c] for c in synthetic.ring_order(r, R)])
-        outs.append(o)
-    back = cp.ulysses_head2seq(torch.stack(outs), U)          # [U][1][sub][H][D]
-    torch.cuda.synchronize()
-    got = torch.cat([back[u] for u in range(U)], dim=1)        # segment 0's tokens, all heads
     rows = _rows(seg, 32, 96, seed=w.seed)
-    say(f"{w.name}: oracle on {len(rows)} rows x {H} heads")
-    wo, wl = oracle.attention(to_f64(q[:, rows]), to_f64(k), to_f64(v), 1 / math.sqrt(D))
-    check_o(got[:, torch.from_numpy(rows).to(DEV)], wo, "bf16", "segment 0 O (sampled rows)")
+    say(f"{w.name}: oracle on {len(rows)} rows of each segment x {H} heads")
+    for r in range(R):
+        outs, lses = [], []
+        for u in range(U):
+            chunks = [(grp["k"][c][u], grp["v"][c][u], c * seg) for c in range(R)]
+            say(f"{w.name}: ring attention for rank (ring {r}, ulysses {u})")
+            o, lse = cp.ring_attention(grp["q"][r][u].contiguous(),
+                                       [chunks[c] for c in synthetic.ring_order(r, R)])
+            outs.append(o)
+            lses.append(lse)
+        back = cp.ulysses_head2seq(torch.stack(outs), U)          # [U][1][sub][H][D]
+        torch.cuda.synchronize()
+        got = torch.cat([back[u] for u in range(U)], dim=1)        # segment r's tokens
+        wo, wl = oracle.attention(to_f64(q[:, r * seg + rows]), to_f64(k), to_f64(v),
+                                  1 / math.sqrt(D))
+        check_o(got[:, torch.from_numpy(rows).to(DEV)], wo, "bf16",
+                f"segment {r} O (sampled rows)")
+        for u in range(U):
+            check_lse(lses[u][:, :, torch.from_numpy(rows).to(DEV)],
+                      wl[:, u * Hu:(u + 1) * Hu], f"segment {r} rank {u} LSE")
