@@ -119,19 +119,15 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
 }
 
 // A query tile is kBM = 128 rows of one (batch, head), covered by a group of
-// 4/QB waves, each owning QB blocks of 32 rows (QB = 2: every K and V fragment
-// read from LDS feeds two MFMAs, halving LDS reads per MFMA, at one wave per
-// SIMD and up to 512 registers). G = 1: a block is one group. G = 2: a block is
-// two groups over the same query tile, group g taking half g of the tile's
-// keys with its own LDS slots; the halves are merged through LDS at the end
-// (grids with fewer query tiles than CUs: every tile gets a whole CU).
-template <int D, bool CAUSAL, bool OUT_BF16, int G, int QB>
-__global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_bf16_kernel(
-    AttnArgs a) {
-  constexpr int WPG = 4 / QB;          // waves per group
+// 4 waves of 32 rows each. G = 1: a block is one group. G = 2: a block is two
+// groups over the same query tile, group g taking half g of the tile's keys
+// with its own LDS slots; the halves are merged through LDS at the end (grids
+// with fewer query tiles than CUs: every tile gets a whole CU).
+template <int D, bool CAUSAL, bool OUT_BF16, int G>
+__global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int WPG = 4;               // waves per group
   constexpr int TPG = WPG * 64;        // threads per group
-  constexpr int RPW = 32 * QB;         // query rows per wave
-  constexpr int KB = 64 / QB;          // keys per tile (32 when QB = 2: registers)
+  constexpr int KB = 64;               // keys per tile
   constexpr int NMB = KB / 32;         // 32-key blocks of S per tile
   constexpr int NT = KB / 16;          // 16-key steps of P*V per tile
   constexpr int UPR = Geo<D>::kUPR;
@@ -146,11 +142,6 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
   __shared__ __attribute__((aligned(1024))) char s_k1[G * TB];
   __shared__ __attribute__((aligned(1024))) char s_v0[G * TB];
   __shared__ __attribute__((aligned(1024))) char s_v1[G * TB];
-  // G = 2 merge of the two key halves: group 1's unnormalised O, when the V
-  // stage arrays cannot hold it
-  constexpr int XO_FLOATS = WPG * QB * (D / 32) * 16 * 64;
-  constexpr bool kXoInStages = 2 * G * TB >= 4 * XO_FLOATS;
-  __shared__ __attribute__((aligned(16))) float s_xo[(G == 2 && !kXoInStages) ? XO_FLOATS : 1];
 
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   const int tid = threadIdx.x;
@@ -182,28 +173,25 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
   // (uniform: kept in scalar registers for the tile addresses)
   const int b = uni(bh / a.H);
   const int h = uni(bh - b * a.H);
-  int irow[QB];  // this lane's query row in each of its blocks
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) irow[qb] = qt * kBM + wave * RPW + qb * 32 + col;
+  const int irow = qt * kBM + wave * 32 + col;  // this lane's query row
   const int q_first = qt * kBM;
   const int q_last = min(q_first + kBM - 1, a.Sq - 1);
 
   // ---- Q^T fragments (B operand), resident for the whole kernel. A negative
   //      scale is folded into Q (bf16 negation is exact).
   const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
-  bf16x8 qf[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+  bf16x8 qf[D / 16];
+  {
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                       ((static_cast<int64_t>(b) * a.Sq + min(irow[qb], a.Sq - 1)) * a.H + h) * D +
+                       ((static_cast<int64_t>(b) * a.Sq + min(irow, a.Sq - 1)) * a.H + h) * D +
                        8 * half;
     const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
       w ^= flip;
-      if (irow[qb] >= a.Sq) w = u32x4{0, 0, 0, 0};
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+      if (irow >= a.Sq) w = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -286,30 +274,24 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
   for (int md = 0; md < D / 32; ++md)
     v_rd[md] = gbase + v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
 
-  // S^T = K Q^T for the KB keys of the K tile in stage array `kl`: sacc[NMB qb + mb]
-  // holds keys 32 mb .. +31 against query block qb; each K fragment feeds QB MFMAs
+  // S^T = K Q^T for the KB keys of the K tile in stage array `kl`: sacc[mb]
+  // holds keys 32 mb .. +31 against the wave's 32 queries
   auto qk = [&](const char* kl, f32x16* sacc) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + k_rd[ks] + mb * 32 * RB);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[NMB * qb + mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              kf, qf[qb][ks], ks == 0 ? f32x16{} : sacc[NMB * qb + mb], 0, 0, 0);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks],
+                                                           ks == 0 ? f32x16{} : sacc[mb], 0, 0, 0);
       }
   };
 
-  f32x16 oacc[QB][D / 32];
-  float m_run[QB], l_run[QB];  // exponent offset (log2 domain); this lane's share of the row sum
+  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int md = 0; md < D / 32; ++md) oacc[qb][md] = f32x16{};
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
+  for (int md = 0; md < D / 32; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY;  // exponent offset, log2 domain
+  float l_run = 0.f;        // this lane's share of the row sum
 
   // this block's share of the query tile's tiles, in chunk order
   Cur cur0{0, 0};
@@ -355,67 +337,55 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
     const int delta = a.chunks[c0].delta;
     const int key0 = uni(cur0.kt) * KB;
 
-    // softmax of tile j (lane = query column; register r of s_cur[NMB qb + mb]
-    // is key key0 + 32*mb + 16*(r/8) + 8*half + r%8)
+    // softmax of tile j (lane = query column; register r of s_cur[mb] is key
+    // key0 + 32*mb + 16*(r/8) + 8*half + r%8)
     const bool masked = (key0 + KB > len) || (CAUSAL && key0 + KB - 1 > q_first + delta);
     if (masked) {
       asm volatile("" ::: "memory");  // keeps this a real (uniform) branch
+      // visible iff the key index relative to key0 is < lim
+      int lim = len - key0;
+      if (CAUSAL) lim = min(lim, irow + delta - key0 + 1);
+      lim -= 8 * half;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        // visible iff the key index relative to key0 is < lim
-        int lim = len - key0;
-        if (CAUSAL) lim = min(lim, irow[qb] + delta - key0 + 1);
-        lim -= 8 * half;
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s_cur[NMB * qb + mb][r] = -INFINITY;
-      }
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s_cur[mb][r] = -INFINITY;
     }
-    float neg_m[QB];
+    float mx = fmaxf(fmaxf(s_cur[0][0], s_cur[0][1]), s_cur[0][2]);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const f32x16* sc = s_cur + NMB * qb;
-      constexpr int NR = 16 * NMB;  // scores of this lane in the tile
-      float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+    for (int r = 3; r < 31; r += 2)
+      mx = fmaxf(fmaxf(mx, s_cur[r >> 4][r & 15]), s_cur[(r + 1) >> 4][(r + 1) & 15]);
+    mx = fmaxf(mx, s_cur[1][15]);
+    mx = pair_max(mx) * sl2;
+    if (__ballot(mx > m_run + kTau)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int r = 3; r + 1 < NR; r += 2)
-        mx = fmaxf(fmaxf(mx, sc[r >> 4][r & 15]), sc[(r + 1) >> 4][(r + 1) & 15]);
-      if (NR % 2 == 0) mx = fmaxf(mx, sc[(NR - 1) >> 4][(NR - 1) & 15]);
-      mx = pair_max(mx) * sl2;
-      if (__ballot(mx > m_run[qb] + kTau)) {
-        asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int md = 0; md < D / 32; ++md) oacc[qb][md] *= alpha;
-        m_run[qb] = m_new;
-      }
-      neg_m[qb] = m_run[qb] == -INFINITY ? 0.f : -m_run[qb];
+      for (int md = 0; md < D / 32; ++md) oacc[md] *= alpha;
+      m_run = m_new;
     }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
 
     // S of tile j+1 on the matrix cores while the exponentials run (for the
     // last tile this reads a stale slot and the result is never used)
     qk(PAR == 0 ? s_k1 : s_k0, s_next);
-    bf16x8 pf[QB][NT];
+    bf16x8 pf[NT];
+    float psum = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float psum = 0.f;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(s_cur[NMB * qb + (t >> 1)][(t & 1) * 8 + e], sl2, neg_m[qb]));
-          psum += p;
-          pf[qb][t][e] = static_cast<__bf16>(p);
-        }
-      l_run[qb] += psum;
-    }
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(s_cur[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
+        psum += p;
+        pf[t][e] = static_cast<__bf16>(p);
+      }
+    l_run += psum;
 
-    // O^T += V^T P^T for tile j; each V^T fragment feeds QB MFMAs
+    // O^T += V^T P^T for tile j
     const char* vl = PAR == 0 ? s_v0 : s_v1;
 #pragma unroll
     for (int md = 0; md < D / 32; ++md) {
@@ -425,19 +395,16 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
         const bf16x4 lo = read_tr(vr);
         const bf16x4 hi = read_tr(vr + 4 * RB);
         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][t], oacc[qb][md], 0, 0,
-                                                                 0);
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
       }
     }
-    // Instruction interleave for the block above: S of tile j+1 (the QB MFMAs
-    // of each K-fragment read, reads kRA fragments ahead) with the
-    // exponentials of tile j in between; the transposed V reads of the first
-    // kVA V fragments go out under the last S MFMAs, then the MFMAs of each V
-    // fragment are followed by the two reads of the fragment kVA later, so no
-    // MFMA waits on a fresh LDS read.
-    constexpr int kRA = 4, kVA = QB == 1 ? 4 : 2, NKF = NMB * (D / 16), NVF = NT * (D / 32);
+    // Instruction interleave for the block above: S of tile j+1 (one MFMA
+    // per K-fragment read, reads kRA fragments ahead) with the exponentials
+    // of tile j in between; the transposed V reads of the first kVA V
+    // fragments go out under the last S MFMAs, then each P*V MFMA is
+    // followed by the two reads of the fragment kVA later, so no MFMA waits
+    // on a fresh LDS read.
+    constexpr int kRA = 4, kVA = 4, NKF = NMB * (D / 16), NVF = NT * (D / 32);
     __builtin_amdgcn_sched_group_barrier(0x100, kRA, 0);    // LDS reads run ahead
 #pragma unroll
     for (int k = 0; k < NKF; ++k) {                         // S MFMAs of qk()
@@ -446,13 +413,13 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
       else
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5 * QB, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);    // VALU
     }
 #pragma unroll
     for (int k = 0; k < NVF; ++k) {                         // P*V MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2 * QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     }
@@ -460,7 +427,7 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
     __syncthreads();
   };
 
-  f32x16 s_a[NMB * QB], s_b[NMB * QB];
+  f32x16 s_a[NMB], s_b[NMB];
   if (steps > 0) {
     if (G == 1 || left > 0) {
       issue(s_k0, cur0, false);
@@ -484,97 +451,79 @@ __global__ __launch_bounds__(256 / QB * G, QB == 1 && G == 1 ? 2 : 1) void attn_
   }
 
   // ---- epilogue: merge the two key halves (G = 2), normalise, write O and LSE
-  float l_tot[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  float l_tot = l_run + __shfl_xor(l_run, 32);
   if (G == 2) {
     // group 1 hands its running max, row sum and unnormalised O to group 0
     // through LDS (every wave is past its last tile read after this barrier).
-    // O blocks e = qb*(D/32) + md < HE go to s_v0, the rest to s_v1:
-    // [wave][e % HE][r][lane] (WPG*HE*16*64 floats = G*TB bytes per array)
+    // O blocks md < D/64 go to s_v0, the rest to s_v1: [wave][md % (D/64)][r][lane]
     __syncthreads();
-    constexpr int HE = QB * D / 64;
-    auto xo = [&](int e, int r) -> float& {
-      if (!kXoInStages) return s_xo[((wave * 2 * HE + e) * 16 + r) * 64 + lane];
-      float* base = reinterpret_cast<float*>(e < HE ? s_v0 : s_v1);
-      return base[((wave * HE + e % HE) * 16 + r) * 64 + lane];
+    constexpr int HM = D / 64;
+    auto xo = [&](int md, int r) -> float& {
+      float* base = reinterpret_cast<float*>(md < HM ? s_v0 : s_v1);
+      return base[((wave * HM + md % HM) * 16 + r) * 64 + lane];
     };
-    float* xs = reinterpret_cast<float*>(s_k0);  // [wave][qb][m, l][lane]
+    float* xs = reinterpret_cast<float*>(s_k0);  // [wave][m, l][lane]
     if (grp == 1) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+      for (int md = 0; md < D / 32; ++md)
 #pragma unroll
-        for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) xo(qb * (D / 32) + md, r) = oacc[qb][md][r];
-        xs[((wave * QB + qb) * 2) * 64 + lane] = m_run[qb];
-        xs[((wave * QB + qb) * 2 + 1) * 64 + lane] = l_tot[qb];
-      }
+        for (int r = 0; r < 16; ++r) xo(md, r) = oacc[md][r];
+      xs[(wave * 2) * 64 + lane] = m_run;
+      xs[(wave * 2 + 1) * 64 + lane] = l_tot;
     }
     __syncthreads();
     if (grp == 1) return;
+    const float m1 = xs[(wave * 2) * 64 + lane], l1 = xs[(wave * 2 + 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    l_tot = a0 * l_tot + a1 * l1;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m1 = xs[((wave * QB + qb) * 2) * 64 + lane];
-      const float l1 = xs[((wave * QB + qb) * 2 + 1) * 64 + lane];
-      const float mm = fmaxf(m_run[qb], m1);
-      const float a0 = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - mm);
-      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-      l_tot[qb] = a0 * l_tot[qb] + a1 * l1;
+    for (int md = 0; md < D / 32; ++md)
 #pragma unroll
-      for (int md = 0; md < D / 32; ++md)
+      for (int r = 0; r < 16; ++r) oacc[md][r] = a0 * oacc[md][r] + a1 * xo(md, r);
+    m_run = mm;
+  }
+  const int i = irow;
+  if (i >= a.Sq) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
+  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
+  const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (nsplit > 1) {  // fp32 partial of split sp
+    float* po = a.part_o + static_cast<int64_t>(sp) * a.B * a.Sq * a.H * D + orow;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          oacc[qb][md][r] = a0 * oacc[qb][md][r] + a1 * xo(qb * (D / 32) + md, r);
-      m_run[qb] = mm;
-    }
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + 32 * md + 8 * g + 4 * half) =
+            make_float4(oacc[md][4 * g] * inv, oacc[md][4 * g + 1] * inv,
+                        oacc[md][4 * g + 2] * inv, oacc[md][4 * g + 3] * inv);
+    if (half == 0) a.part_lse[static_cast<int64_t>(sp) * a.B * a.H * a.Sq + lrow] = lse_val;
+    return;
   }
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int i = irow[qb];
-    if (i >= a.Sq) continue;
-    const float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
-    const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
-    const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
-    const float lse_val = l_tot[qb] > 0.f ? (m_run[qb] + __log2f(l_tot[qb])) * kLn2 : -INFINITY;
-    if (nsplit > 1) {  // fp32 partial of split sp
-      float* po = a.part_o + static_cast<int64_t>(sp) * a.B * a.Sq * a.H * D + orow;
+  for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
-      for (int md = 0; md < D / 32; ++md)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(po + 32 * md + 8 * g + 4 * half) = make_float4(
-              oacc[qb][md][4 * g] * inv, oacc[qb][md][4 * g + 1] * inv,
-              oacc[qb][md][4 * g + 2] * inv, oacc[qb][md][4 * g + 3] * inv);
-      if (half == 0) a.part_lse[static_cast<int64_t>(sp) * a.B * a.H * a.Sq + lrow] = lse_val;
-      continue;
-    }
-#pragma unroll
-    for (int md = 0; md < D / 32; ++md) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * md + 8 * g + 4 * half;
-        const float x0 = oacc[qb][md][4 * g] * inv, x1 = oacc[qb][md][4 * g + 1] * inv;
-        const float x2 = oacc[qb][md][4 * g + 2] * inv, x3 = oacc[qb][md][4 * g + 3] * inv;
-        if (OUT_BF16) {
-          bf16x4 r;
-          r[0] = static_cast<__bf16>(x0);
-          r[1] = static_cast<__bf16>(x1);
-          r[2] = static_cast<__bf16>(x2);
-          r[3] = static_cast<__bf16>(x3);
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + orow + d0) = r;
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) =
-              make_float4(x0, x1, x2, x3);
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * md + 8 * g + 4 * half;
+      const float x0 = oacc[md][4 * g] * inv, x1 = oacc[md][4 * g + 1] * inv;
+      const float x2 = oacc[md][4 * g + 2] * inv, x3 = oacc[md][4 * g + 3] * inv;
+      if (OUT_BF16) {
+        bf16x4 r;
+        r[0] = static_cast<__bf16>(x0);
+        r[1] = static_cast<__bf16>(x1);
+        r[2] = static_cast<__bf16>(x2);
+        r[3] = static_cast<__bf16>(x3);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + orow + d0) = r;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) =
+            make_float4(x0, x1, x2, x3);
       }
     }
-    if (half == 0) a.lse[lrow] = lse_val;
   }
+  if (half == 0) a.lse[lrow] = lse_val;
 }
-
-// query blocks of 32 rows per wave
-constexpr int kQB = 1;
 
 template <int D, bool CAUSAL, bool OUT_BF16, int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
@@ -582,8 +531,8 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   const int64_t nsplit = (CAUSAL || G == 2) ? 1 : a.nsplit;
   const int64_t nitems = nqt * a.B * a.H * nsplit;
   const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, OUT_BF16, G, kQB>),
-                     dim3(static_cast<uint32_t>(blocks)), dim3(256 / kQB * G), 0, stream, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, OUT_BF16, G>),
+                     dim3(static_cast<uint32_t>(blocks)), dim3(256 * G), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   // combine the splits' fp32 partials in split order

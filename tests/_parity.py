@@ -47,16 +47,17 @@ def check_o(got: torch.Tensor, want: np.ndarray, kind: str, what: str = "O") -> 
         assert err.max() <= F32_MAX, f"{what}: max-abs {err.max():.3e} > {F32_MAX}"
 
 
-def check_o_scaled(got: torch.Tensor, want: np.ndarray, what: str = "O") -> None:
+def check_o_scaled(got: torch.Tensor, want: np.ndarray, what: str = "O",
+                   mean_rel: float = 2.0 ** -7) -> None:
     """bf16-rounded outputs that need not be small (few visible keys, peaky
     softmax): bf16 rounds a value of size |x| by up to 2^-8 |x| on its own, so
     the bars scale with the reference: max-abs <= 1e-2 * max(1, max|ref|),
-    mean-abs <= max(1e-3, 2^-7 * mean|ref|)."""
+    mean-abs <= max(1e-3, mean_rel * mean|ref|)."""
     g = to_f64(got)
     assert g.shape == want.shape and not np.any(np.isnan(g)), what
     err = np.abs(g - want)
     big = max(1.0, float(np.abs(want).max()))
-    mean_bar = max(BF16_MEAN, 2.0 ** -7 * float(np.abs(want).mean()))
+    mean_bar = max(BF16_MEAN, mean_rel * float(np.abs(want).mean()))
     assert err.max() <= BF16_MAX * big, f"{what}: max-abs {err.max():.3e} > {BF16_MAX} * {big:.2f}"
     assert err.mean() <= mean_bar, f"{what}: mean-abs {err.mean():.3e} > {mean_bar:.3e}"
 

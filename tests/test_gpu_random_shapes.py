@@ -10,7 +10,7 @@ draws are seeded, so every run checks the same cases.
 Tolerances: LSE max-abs 1e-4, gradients as in the other backward tests. The
 per-hop fp32 partials (cp_attn_chunk_partial, no final rounding) are held to
 the absolute bars, max-abs 1e-2 and mean-abs 1e-3. For bf16 outputs: max-abs <= 1e-2 * max(1, max|ref|) and
-mean-abs <= max(1e-3, 2^-7 * mean|ref|). With only a few visible keys O is
+mean-abs <= max(1e-3, 2^-8 * mean|ref|). With only a few visible keys O is
 close to single value rows (|O| up to ~4), and bf16 itself rounds such values
 by up to 2^-8 of their size (half a bf16 step is 0.0078 at |O| = 2; about a
 quarter step on average), before the 2^-8 rounding of P. The absolute bars
@@ -35,6 +35,10 @@ if torch.cuda.is_available():
 DEV = "cuda:0"
 
 N_CASES = 64
+# mean-abs bar relative to mean|ref|: 2^-8 (the sweep measures at most ~2^-8.8,
+# about the mean bf16 rounding of O plus that of P), so a systematic bias of
+# 0.4% or more fails
+MEAN_REL = 2.0 ** -8
 
 
 def _case(seed):
@@ -84,9 +88,9 @@ def test_random_shape_forward_and_backward(seed):
     mo, ml = cp.lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
                           out_dtype=bf)
     torch.cuda.synchronize()
-    check_o_scaled(o, wo, "ring O")
+    check_o_scaled(o, wo, "ring O", mean_rel=MEAN_REL)
     check_lse(lse, wl, "ring LSE")
-    check_o_scaled(mo, wo, "partials + merge O")
+    check_o_scaled(mo, wo, "partials + merge O", mean_rel=MEAN_REL)
     check_lse(ml, wl, "partials + merge LSE")
     # each hop's fp32 partial (no final bf16 rounding) at the absolute bars
     for (kc, vc, p0), (po, pl) in zip(visit, parts):
