@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROTATE_BYTES = 1 << 30        # footprint of the buffer sets an HBM-bound kernel rotates over
 WARM_MS = 30.0                # sustained GPU work before a detail entry's timed region
 MIN_TIMED_MS = 20.0           # shortest timed region of a detail entry
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llm_causal_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llm_causal_counters.json")
 FLUX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_flux_ring_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "context_attention_dit_amd", "csrc", "attn_bf16.hip")
 
@@ -143,16 +143,23 @@ def median(xs):
     return xs[len(xs) // 2]
 
 
-def traffic_record(path=TRAFFIC_FILE):
-    """HBM bytes per launch of the attention kernel, if taken on the current source."""
+def counter_record(path=TRAFFIC_FILE):
+    """rocprofv3 counter record of the attention kernel (profiles/), if it was
+    taken on the current kernel source; else None."""
     try:
         rec = json.load(open(path))
         src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
         if rec.get("attn_bf16_sha256") == src_hash:
-            return rec.get("bytes_per_launch")
+            return rec
     except (OSError, ValueError):
         pass
     return None
+
+
+def traffic_record(path=TRAFFIC_FILE):
+    """HBM bytes per launch of the attention kernel, if taken on the current source."""
+    rec = counter_record(path)
+    return None if rec is None else rec.get("bytes_per_launch")
 
 
 def cpu_baseline(qkv_cpu, budget_s: float = 15.0):
@@ -214,78 +221,6 @@ def cpu_oracle_relayout(budget_s: float = 2.0):
             "sample": f"seq2head of the Qwen-Image rank's Q ({bits.nbytes / 1e6:.1f} MB, "
                       f"[{w.P}][1][{w.S_local}][{w.H}][{w.D}] bf16 bits) {n} times in {dt:.1f} s "
                       f"(numpy transpose copy)"}
-
-
-def sample_sclk(torch, fn, seconds: float = 2.0):
-    """Graphics clock while `fn` runs back to back for ~`seconds`: amd-smi (else
-    rocm-smi) is queried from a side thread during the sustained run. Returns
-    (MHz or None, source/reason)."""
-    import re
-    import subprocess
-    import threading
-
-    readings, errors = [], []
-
-    def walk(x, path=""):
-        if isinstance(x, dict):
-            for key, val in x.items():
-                yield from walk(val, path + "/" + str(key).lower())
-        elif isinstance(x, list):
-            for val in x:
-                yield from walk(val, path)
-        else:
-            yield path, x
-
-    def query():
-        cmds = [["amd-smi", "metric", "-g", "0", "-c", "--json"],
-                ["rocm-smi", "-d", "0", "--showclocks", "--json"]]
-        for cmd in cmds:
-            try:
-                r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-                data = json.loads(r.stdout)
-            except Exception as e:  # tool missing, no JSON, timeout
-                errors.append(f"{cmd[0]}: {type(e).__name__}")
-                continue
-            mhz = []
-            for path, val in walk(data):
-                # amd-smi: .../gfx_N/clk[/value]; rocm-smi: "sclk clock speed:" "(2100Mhz)"
-                if re.search(r"/gfx_\d+/clk(/value)?$", path) or "sclk clock speed" in path:
-                    m = re.search(r"(\d+(\.\d+)?)", str(val))
-                    if m and float(m.group(1)) > 100:
-                        mhz.append(float(m.group(1)))
-            if mhz:
-                readings.append((cmd[0], sum(mhz) / len(mhz)))
-                return
-            errors.append(f"{cmd[0]}: no clock field")
-
-    stop = threading.Event()
-
-    def sampler():
-        while not stop.is_set() and len(readings) < 3:
-            query()
-            if errors and not readings:
-                return
-
-    th = threading.Thread(target=sampler, daemon=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    th.start()
-    n = 0
-    while time.perf_counter() - t0 < seconds or (th.is_alive() and time.perf_counter() - t0 < 30):
-        fn()
-        n += 1
-        if n % 2 == 0:
-            torch.cuda.synchronize()
-        if not th.is_alive():
-            break
-    stop.set()
-    torch.cuda.synchronize()
-    th.join(timeout=30)
-    if readings:
-        vals = sorted(v for _, v in readings)
-        return vals[len(vals) // 2], f"{readings[0][0]} during back-to-back calls " \
-                                     f"({len(readings)} readings, median)"
-    return None, "; ".join(errors) or "no reading"
 
 
 def copy_ceiling(torch, cp, dev) -> float:
@@ -365,8 +300,6 @@ def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
     h2s = time_rotating(torch, [lambda: cp.ulysses_head2seq(o_all, P, back)], 1, 5)
     s2h_bytes = 3 * 2 * qkv[0].numel() * qkv.element_size()
     h2s_bytes = 2 * o_all.numel() * o_all.element_size()
-    sclk, sclk_src = sample_sclk(torch, attend)
-    log(f"{w.name}: sclk {sclk} MHz ({sclk_src})")
     res = {
         "value": value, "ms_per_step": ms_step, "flops": flops,
         "attn_ms": attn_ms, "achieved": achieved, "warm_ms_per_step": warm_ms_per_step,
@@ -375,7 +308,6 @@ def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
         "seq2head_qkv_us": s2h_qkv * 1e3,
         "seq2head_qkv_gbs": s2h_bytes / (s2h_qkv * 1e-3) / 1e9,
         "head2seq_us": h2s * 1e3, "head2seq_gbs": h2s_bytes / (h2s * 1e-3) / 1e9,
-        "sclk_mhz": sclk, "sclk_source": sclk_src,
     }
     del qkv, heads, o_all, back, lse, rq, rk, rv, ro
     torch.cuda.empty_cache()
@@ -465,8 +397,9 @@ def main() -> int:
         detail.update(other_workloads(torch, cp, synthetic, dev, q0, vis, synthetic.FLUX_RING,
                                       args.only))
 
-    traffic = traffic_record()
-    sclk = h["sclk_mhz"]
+    rec = counter_record()
+    traffic = None if rec is None else rec.get("bytes_per_launch")
+    sclk = None if rec is None else rec.get("clock_mhz")
     line = {
         "metric": "attention TFLOP/s (bf16, 1 MI355X) + % MFMA peak; relayout GB/s",
         "value": h["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -484,7 +417,10 @@ def main() -> int:
                      "traffic": traffic,
                      "kernel": "attn_bf16_kernel<128, causal=true, out_bf16=true, groups=1>",
                      "flop_per_launch": h["flops"], "kernel_ms": h["attn_ms"],
-                     "measured_sclk_mhz": sclk, "sclk_source": h["sclk_source"],
+                     # clock and MFMA busy of this kernel from the rocprofv3
+                     # counter pass on the current source (profiles/), or null
+                     "measured_sclk_mhz": sclk,
+                     "mfma_busy": None if rec is None else rec.get("mfma_busy"),
                      "peak_at_measured_sclk": (PEAK_BF16_TFLOPS * sclk / 2400.0
                                                if sclk else None)},
         "relayout": {"seq2head_qkv_gbs": h["seq2head_qkv_gbs"],
