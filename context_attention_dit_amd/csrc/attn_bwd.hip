@@ -42,8 +42,8 @@
 //    half-wave, which is exactly the B-operand layout of the next product, so
 //    P and dS feed the second products without data movement; the transposed
 //    reads of the same tile find those rows as two groups of four.
-//  * Direct global->LDS loads (global_load_lds_dwordx4) fill the tiles with
-//    no staging registers; one barrier per tile.
+//  * Direct buffer->LDS loads (buffer_load_dwordx4 ... lds) fill the tiles
+//    with no staging registers; one barrier per tile.
 //  * Weights are exp2 of one FMA per score, with the signed scale*log2(e) and
 //    -log2(e)*LSE (no row maximum is needed, so no sign trick either). A row
 //    whose LSE is -inf saw no key anywhere and gets weight 0; a masked pair
@@ -85,9 +85,24 @@ __device__ __forceinline__ uint32_t unit_off(int row, int unit) {
   return row * Geo<D>::kRowBytes + ((unit ^ (row & Geo<D>::kMask)) << 4);
 }
 
-__device__ __forceinline__ void lds_load16(const char* g, char* l) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), reinterpret_cast<void*>(l),
-                                   16, 0, 0);
+// Buffer resource over the bytes from the wave-uniform `base` on (raw, stride
+// 0, no range limit that offsets below 2^31 could reach), built in scalar
+// registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p >> 32)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(hi << 32 | lo), 0, -1,
+                                           0x00020000);
+}
+
+// buffer_load_dwordx4 ... lds: lane i's 16 bytes at byte offset `voff` land in
+// LDS at l + 16 i (l wave-uniform). The MUBUF form is counted on the
+// vector-memory counter only, so LDS reads issued after it keep partial wait
+// counts (the FLAT global_load_lds made every later LDS wait a full drain).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, char* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(l), 16,
+                                           voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x4 read_tr(const char* p) {
@@ -150,18 +165,18 @@ struct TileGeo {
   // (`base` points at row 0, head offset included) into the tile at `dst`.
   // Rows at or beyond n_rows are redirected to the last valid row.
   __device__ void issue(const char* base, int row0, int n_rows, int rs, char* dst, int wave) const {
-    const char* g = base + 2 * static_cast<int64_t>(row0) * rs;
+    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(base + 2 * static_cast<int64_t>(row0) * rs);
     char* l = dst + wave * NL * 1024;
     const int n_valid = n_rows - row0;
     if (n_valid >= kTile) {
 #pragma unroll
-      for (int n = 0; n < NL; ++n) lds_load16(g + src[n], l + n * 1024);
+      for (int n = 0; n < NL; ++n) lds_load16(rsrc, src[n], l + n * 1024);
     } else {
 #pragma unroll
       for (int n = 0; n < NL; ++n) {
         const int r = src_row(n);
         const uint32_t fix = r < n_valid ? 0u : 2u * static_cast<uint32_t>((r - n_valid + 1) * rs);
-        lds_load16(g + (src[n] - fix), l + n * 1024);
+        lds_load16(rsrc, src[n] - fix, l + n * 1024);
       }
     }
   }
@@ -366,6 +381,13 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
           dp[mb] = mfma(g.frag(vl, mb, ks), df[ks], dp[mb]);
         }
       }
+      // interleave: each fragment read runs 4 MFMAs ahead of its product
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < 4 * (D / 16); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
       const bool masked = key0 + kTile > len || (CAUSAL && key0 + kTile - 1 > q_first + diag);
       if (masked) {
         asm volatile("" ::: "memory");
@@ -378,21 +400,30 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
           for (int r = 0; r < 16; ++r)
             if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) s[mb][r] = s_mask;
       }
-      // dS^T, rounded to bf16: B operand of k-step t (keys 16 t + 8 half + e)
-      bf16x8 dsf[4];
+      // k-step t: dS^T rounded to bf16 (B operand: keys 16 t + 8 half + e), then
+      // dQ^T += K^T dS^T over its 16 keys
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 dsf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int mb = t >> 1, r = (t & 1) * 8 + e;
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, nl));
-          dsf[t][e] = static_cast<__bf16>(p * (dp[mb][r] - dlt));
+          dsf[e] = static_cast<__bf16>(p * (dp[mb][r] - dlt));
         }
-      // dQ^T += K^T dS^T
 #pragma unroll
-      for (int md = 0; md < D / 32; ++md)
+        for (int md = 0; md < D / 32; ++md) acc[md] = mfma(g.tr_frag(kl, md, t), dsf, acc[md]);
+      }
+      // interleave: the transposed reads run 4 MFMAs ahead; the next k-step's
+      // dS arithmetic fills the gaps between this k-step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 36, 0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[md] = mfma(g.tr_frag(kl, md, t), dsf[t], acc[md]);
+      for (int k = 0; k < 4 * (D / 32); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 36 / (D / 32), 0);
+      }
       cur = nx;
     }
     __builtin_amdgcn_s_waitcnt(0);
