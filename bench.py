@@ -143,13 +143,23 @@ def median(xs):
     return xs[len(xs) // 2]
 
 
+def code_digest(path=ATTN_SRC) -> str:
+    """SHA-256 of a HIP source's code: comments removed and whitespace runs
+    collapsed, so an edit to comments alone keeps the digest and any change to
+    the code changes it."""
+    import re
+    src = open(path, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
+
+
 def counter_record(path=TRAFFIC_FILE):
     """rocprofv3 counter record of the attention kernel (profiles/), if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel code; else None."""
     try:
         rec = json.load(open(path))
-        src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("attn_bf16_sha256") == src_hash:
+        if rec.get("attn_bf16_code_sha256") == code_digest():
             return rec
     except (OSError, ValueError):
         pass

@@ -12,9 +12,10 @@
 // How it maps to the hardware:
 //  * A block is 4 wavefronts; each wave owns 32 query rows, so a block covers
 //    128 rows of one (batch, head). K/V tiles of 64 keys are shared by the 4
-//    waves through double-buffered LDS, filled by direct global->LDS loads
-//    (global_load_lds_dwordx4: no staging registers, no LDS store
-//    instructions); one barrier per tile.
+//    waves through double-buffered LDS, filled by direct memory->LDS loads
+//    (buffer_load_dwordx4 ... lds: no staging registers, no LDS store
+//    instructions, counted on the vector-memory counter only); one barrier
+//    per tile. K runs two tiles ahead of the tile being scored, V one.
 //  * The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = a K
 //    tile from LDS, B = Q^T held in registers for the whole kernel). In the
 //    32x32 accumulator layout lane l holds query column l%32, so every

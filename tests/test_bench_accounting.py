@@ -49,3 +49,15 @@ def test_rotation_spans_the_caches(nbytes):
     n = bench.buffer_sets(nbytes)
     assert n >= 2 and n * nbytes >= bench.ROTATE_BYTES
     assert (n - 1) * nbytes < bench.ROTATE_BYTES or n == 2
+
+
+def test_code_digest_ignores_comments_only(tmp_path):
+    """The counter records are tied to the attention kernel's code: a comment
+    edit keeps the digest, a code edit changes it."""
+    base = "// header\nint f(int x) {\n  return x + 1;  // one\n}\n/* block\n comment */\n"
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text(base)
+    b.write_text(base.replace("// one", "// plus one, reworded").replace("// header\n", ""))
+    c.write_text(base.replace("x + 1", "x + 2"))
+    assert bench.code_digest(str(a)) == bench.code_digest(str(b))
+    assert bench.code_digest(str(a)) != bench.code_digest(str(c))
