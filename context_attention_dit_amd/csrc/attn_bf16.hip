@@ -92,15 +92,17 @@ __device__ __forceinline__ uint32_t v_unit_off(int row, int unit) {
   return row * Geo<D>::kRowBytes + ((unit ^ ((row & 3) << 1)) << 4);
 }
 
-// Buffer resource over the bytes from `base` on (raw, stride 0, no range
-// limit that offsets below 2^31 could reach).
+// Buffer resource over the `bytes` bytes from `base` on (raw, stride 0). A
+// load at or past `bytes` is out of range: the hardware fetches nothing and
+// returns zeros, which a direct load writes to LDS like any other data.
 // `base` must be wave-uniform; it is moved to scalar registers explicitly so
 // the descriptor is built there.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
   const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p)));
   const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p >> 32)));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(hi << 32 | lo), 0, -1,
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(hi << 32 | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)),
                                            0x00020000);
 }
 
@@ -200,13 +202,11 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
   //      of each tensor tile; slot s is (row s/UPR, swizzled unit s%UPR). The
   //      lane's source offsets (bytes from the tile's first key) are fixed.
   const int rs = a.H * D;  // elements between consecutive keys (host checks 64*rs < 2^31)
-  int ld_row[NL];
   uint32_t k_src[NL], v_src[NL];
 #pragma unroll
   for (int n = 0; n < NL; ++n) {
     const int s = (wave * NL + n) * 64 + lane;
     const int row = s / UPR, pu = s % UPR;
-    ld_row[n] = row;
     const int k_key = swap_bits23(row), k_unit = pu ^ (row & Geo<D>::kKMask);
     const int v_unit = pu ^ ((row & 3) << 1);
     k_src[n] = 2u * static_cast<uint32_t>(k_key * rs + k_unit * 8);
@@ -221,42 +221,56 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
     if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].delta + 1));
     return n;
   };
+  // A cursor carries its chunk's descriptor (visible keys nk, stored keys len,
+  // position offset delta) and the addresses of its K and V tile for this
+  // (batch, head), set when it enters the chunk and stepped by one tile
+  // stride after that, so the pipeline steps issue no scalar loads and no
+  // 64-bit address arithmetic of their own.
   struct Cur {
     int c, kt;
+    int nk, len, delta;
+    const char* tk;
+    const char* tv;
+  };
+  const int64_t tile_bytes = 2 * static_cast<int64_t>(KB) * rs;
+  auto enter = [&](Cur& x) {
+    const int c = uni(x.c);
+    if (c < a.nchunks) {  // (a cursor past the list is never used)
+      x.len = a.chunks[c].len;
+      x.delta = a.chunks[c].delta;
+      x.nk = CAUSAL ? max(0, min(x.len, q_last + x.delta + 1)) : x.len;
+      const int64_t off =
+          2 * ((static_cast<int64_t>(b) * x.len + uni(x.kt) * KB) * rs + h * D);
+      x.tk = reinterpret_cast<const char*>(a.chunks[c].k) + off;
+      x.tv = reinterpret_cast<const char*>(a.chunks[c].v) + off;
+    }
   };
   auto next_of = [&](Cur x) {
-    x.c = uni(x.c);
     x.kt = uni(x.kt) + 1;
-    if (x.kt * KB >= keys_of(x.c)) {
+    if (x.kt * KB >= x.nk) {
       x.kt = 0;
-      ++x.c;
+      x.c = uni(x.c) + 1;
       while (x.c < a.nchunks && keys_of(x.c) == 0) ++x.c;
+      enter(x);
+    } else {
+      x.tk += tile_bytes;
+      x.tv += tile_bytes;
     }
     return x;
   };
   // Direct loads of one K or V tile into `dst`: a uniform base address plus
-  // the lane's fixed byte offset. Keys at or beyond the tile's valid count
-  // are redirected to its last valid key (their probabilities are exactly 0).
-  auto issue = [&](char* dst, Cur x, bool is_v) {
-    const int c = uni(x.c);
-    x.kt = uni(x.kt);
-    const int n_valid = keys_of(c) - x.kt * KB;
-    const char* base =
-        reinterpret_cast<const char*>(is_v ? a.chunks[c].v : a.chunks[c].k) +
-        2 * ((static_cast<int64_t>(b) * a.chunks[c].len + x.kt * KB) * rs + h * D);
+  // the lane's fixed byte offset. The buffer's range ends after the tile's
+  // last valid key, so rows past it (a chunk's ragged end, keys beyond the
+  // causal limit) arrive as zeros; their scores are masked, so they add
+  // nothing.
+  auto issue = [&](char* dst, const Cur& x, bool is_v) {
+    const int n_valid = min(x.nk - uni(x.kt) * KB, KB);  // >= 1 for every issued tile
+    const char* base = is_v ? x.tv : x.tk;
     char* l = dst + gbase + wave * NL * 1024;
-    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(base);
-    if (n_valid >= KB) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
 #pragma unroll
-      for (int n = 0; n < NL; ++n) lds_load16(rsrc, is_v ? v_src[n] : k_src[n], l + n * 1024);
-    } else {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int key = is_v ? ld_row[n] : swap_bits23(ld_row[n]);
-        const uint32_t fix = key < n_valid ? 0u : 2u * static_cast<uint32_t>((key - n_valid + 1) * rs);
-        lds_load16(rsrc, (is_v ? v_src[n] : k_src[n]) - fix, l + n * 1024);
-      }
-    }
+    for (int n = 0; n < NL; ++n) lds_load16(rsrc, is_v ? v_src[n] : k_src[n], l + n * 1024);
   };
 
   // ---- fragment read addresses (byte offsets within a tile)
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
   float l_run = 0.f;        // this lane's share of the row sum
 
   // this block's share of the query tile's tiles, in chunk order
-  Cur cur0{0, 0};
+  Cur cur0{0, 0, 0, 0, 0, nullptr, nullptr};
   int left, steps;
   {
     int total = 0;
@@ -314,6 +328,7 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
       ++cur0.c;
     }
     cur0.kt = skip;
+    enter(cur0);
   }
 
   // One pipeline step for tile j (cursor cur0; cur1/cur2 are tiles j+1/j+2):
@@ -333,9 +348,8 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
     }
     if (j + 2 < left) issue(PAR == 0 ? s_k0 : s_k1, cur2, false);
     if (j + 1 < left) issue(PAR == 0 ? s_v1 : s_v0, cur1, true);
-    const int c0 = uni(cur0.c);
-    const int len = a.chunks[c0].len;
-    const int delta = a.chunks[c0].delta;
+    const int len = cur0.len;
+    const int delta = cur0.delta;
     const int key0 = uni(cur0.kt) * KB;
 
     // softmax of tile j (lane = query column; register r of s_cur[mb] is key
