@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
   // causal limit) arrive as zeros; their scores are masked, so they add
   // nothing.
   auto issue = [&](char* dst, const Cur& x, bool is_v) {
-    const int n_valid = min(x.nk - uni(x.kt) * KB, KB);  // >= 1 for every issued tile
+    const int n_valid = max(0, min(x.nk - uni(x.kt) * KB, KB));  // (0: nothing is fetched)
     const char* base = is_v ? x.tv : x.tk;
     char* l = dst + gbase + wave * NL * 1024;
     const __amdgpu_buffer_rsrc_t rsrc =

@@ -85,14 +85,15 @@ __device__ __forceinline__ uint32_t unit_off(int row, int unit) {
   return row * Geo<D>::kRowBytes + ((unit ^ (row & Geo<D>::kMask)) << 4);
 }
 
-// Buffer resource over the bytes from the wave-uniform `base` on (raw, stride
-// 0, no range limit that offsets below 2^31 could reach), built in scalar
-// registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
+// Buffer resource over the `bytes` bytes from the wave-uniform `base` on (raw,
+// stride 0), built in scalar registers. A load at or past `bytes` is out of
+// range: nothing is fetched and zeros arrive (in LDS, for a direct load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
   const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p)));
   const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p >> 32)));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(hi << 32 | lo), 0, -1,
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(hi << 32 | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)),
                                            0x00020000);
 }
 
@@ -128,12 +129,6 @@ struct TileGeo {
   uint32_t t_lo[D / 32]; // transposed fragment, k-step 0, rows r0 .. r0+3 (add 16 t rows)
   int w8, lane;
 
-  // Tile row fetched by direct load n of this lane.
-  __device__ int src_row(int n) const {
-    const int s = (w8 * NL + n) * 64 + lane;
-    return swap_bits23(s / Geo<D>::kUPR);
-  }
-
   __device__ void init(int wave, int ln, int rs) {
     constexpr int UPR = Geo<D>::kUPR;
     w8 = wave;
@@ -163,22 +158,16 @@ struct TileGeo {
 
   // Direct loads of tile rows [row0, row0 + 64) of a [.][rs] bf16 tensor
   // (`base` points at row 0, head offset included) into the tile at `dst`.
-  // Rows at or beyond n_rows are redirected to the last valid row.
+  // The buffer's range ends after row n_rows - 1, so rows at or beyond n_rows
+  // arrive as zeros (their weights are zero wherever they are used).
   __device__ void issue(const char* base, int row0, int n_rows, int rs, char* dst, int wave) const {
-    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(base + 2 * static_cast<int64_t>(row0) * rs);
+    const int n_valid = max(0, min(n_rows - row0, kTile));  // (0: nothing is fetched)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        tile_rsrc(base + 2 * static_cast<int64_t>(row0) * rs,
+                  static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
     char* l = dst + wave * NL * 1024;
-    const int n_valid = n_rows - row0;
-    if (n_valid >= kTile) {
 #pragma unroll
-      for (int n = 0; n < NL; ++n) lds_load16(rsrc, src[n], l + n * 1024);
-    } else {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int r = src_row(n);
-        const uint32_t fix = r < n_valid ? 0u : 2u * static_cast<uint32_t>((r - n_valid + 1) * rs);
-        lds_load16(rsrc, src[n] - fix, l + n * 1024);
-      }
-    }
+    for (int n = 0; n < NL; ++n) lds_load16(rsrc, src[n], l + n * 1024);
   }
 
   // A operand: tile^T rows d = 32 md + lane%32, k = tile rows 16 t + 8 half + 0..7

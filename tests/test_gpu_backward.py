@@ -303,6 +303,46 @@ def test_ring_backward_matches_oracle(lens, causal, H):
     check_grad(dq2, wq, "dQ per chunk")
 
 
+def _nan_padded(x: torch.Tensor) -> torch.Tensor:
+    """x ([1][S][H][D]) on the GPU as a view whose memory continues with 64 NaN rows."""
+    buf = torch.full((1, x.shape[1] + 64) + tuple(x.shape[2:]), float("nan"), dtype=x.dtype)
+    buf[:, :x.shape[1]] = x
+    return buf.to(DEV)[:, :x.shape[1]]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ring_backward_never_reads_past_its_tensors(causal):
+    """Q, dO and every K/V chunk are views followed by NaN rows. The backward
+    kernels must not read past any of them (a ragged tile's missing rows come
+    in as zeros through the load's range check): a NaN row that entered a
+    product would turn gradients into NaN."""
+    lens, H, D = (201, 64, 150, 37), 2, 128
+    say(f"ring backward, NaN rows after every tensor, causal={causal}")
+    S = sum(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    r = 2
+    q0, n = int(starts[r]), lens[r]
+    q, k, v, do = _inputs(1, n, S, H, D, seed=77)
+    q64, k64, v64, do64 = (to_f64(x) for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    q_pos = np.arange(q0, q0 + n)
+    o, lse, delta, o_bf, lse_f = _saved_stats(q64, k64, v64, do64, scale, causal, q_pos,
+                                              np.arange(S))
+    wq, wk, wv = oracle.chunk_grad(q64, k64, v64, do64, lse, delta, scale, causal, q_pos,
+                                   np.arange(S))
+    chunks = [(_nan_padded(k[:, s:s + m]), _nan_padded(v[:, s:s + m]), int(s))
+              for s, m in zip(starts, lens)]
+    order = synthetic.ring_order(r, len(lens))
+    qd, dod = _nan_padded(q), _nan_padded(do)
+    delta_d = cp.attn_backward_delta(_nan_padded(o_bf), dod)
+    dq, grads = cp.ring_attention_backward(qd, [chunks[c] for c in order], dod, lse_f.to(DEV),
+                                           delta_d, scale=scale, causal=causal, q_pos0=q0)
+    torch.cuda.synchronize()
+    check_grad(dq, wq, "dQ")
+    check_grad(torch.cat([grads[order.index(c)][0] for c in range(len(lens))], dim=1), wk, "dK")
+    check_grad(torch.cat([grads[order.index(c)][1] for c in range(len(lens))], dim=1), wv, "dV")
+
+
 def test_ring_backward_accumulates_into_existing_buffers():
     say("ring backward accumulate flags")
     B, Sq, H, D = 1, 100, 2, 128

@@ -525,6 +525,44 @@ def test_outputs_stay_inside_their_buffers():
         assert torch.all(buf[:pad] == val) and torch.all(buf[pad + n:] == val)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_keys_past_a_chunk_are_never_read(causal):
+    """Each K/V chunk is a view whose memory continues with NaN rows. The
+    kernels must not read past a chunk's length (a ragged last tile's missing
+    keys come in as zeros through the load's range check): any NaN V row
+    read would turn O into NaN, as would a NaN K row that escaped the mask."""
+    B, Sq, H, D = 1, 150, 3, 128
+    lens = (201, 64, 1000, 37)
+    say(f"NaN rows after every chunk, causal={causal}")
+    q, k, v = _qkv(B, Sq, sum(lens), H, D, torch.bfloat16, seed=41)
+    chunks, k_parts, v_parts, pos = [], [], [], 0
+    for n in lens:
+        kb = torch.full((B, n + 64, H, D), float("nan"), dtype=torch.bfloat16)
+        vb = torch.full((B, n + 64, H, D), float("nan"), dtype=torch.bfloat16)
+        kb[:, :n] = k[:, pos:pos + n]
+        vb[:, :n] = v[:, pos:pos + n]
+        kb, vb = kb.to(DEV), vb.to(DEV)
+        chunks.append((kb[:, :n], vb[:, :n], pos))
+        pos += n
+    qd = q.to(DEV)
+    qp = 700 if causal else 0
+    ro, rl = cp.ring_attention(qd, chunks[::-1], causal=causal, q_pos0=qp)
+    po, pl = cp.attn_chunk_partial(qd, chunks[2][0], chunks[2][1], causal=causal, q_pos0=qp,
+                                   kv_pos0=chunks[2][2], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ro.float()).all() and torch.isfinite(po).all()
+    wo, wl = oracle.chunk_partial(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(D), causal,
+                                  np.arange(qp, qp + Sq), np.arange(0, pos))
+    check_o(ro, wo, "bf16", "ring O")
+    check_lse(rl, wl, "ring LSE")
+    p0 = chunks[2][2]
+    wpo, wpl = oracle.chunk_partial(to_f64(q), to_f64(k[:, p0:p0 + lens[2]]),
+                                    to_f64(v[:, p0:p0 + lens[2]]), 1.0 / math.sqrt(D), causal,
+                                    np.arange(qp, qp + Sq), np.arange(p0, p0 + lens[2]))
+    check_o(po, wpo, "bf16", "partial O")
+    check_lse(pl, wpl, "partial LSE")
+
+
 def test_rejected_call_leaves_outputs_untouched():
     q = synthetic.make_tensor((1, 64, 6, 128), torch.bfloat16, 1).to(DEV)
     o = torch.full((1, 64, 6, 128), 5.0, device=DEV)
