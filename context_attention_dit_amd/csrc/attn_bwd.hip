@@ -161,10 +161,14 @@ struct TileGeo {
   // The buffer's range ends after row n_rows - 1, so rows at or beyond n_rows
   // arrive as zeros (their weights are zero wherever they are used).
   __device__ void issue(const char* base, int row0, int n_rows, int rs, char* dst, int wave) const {
-    const int n_valid = max(0, min(n_rows - row0, kTile));  // (0: nothing is fetched)
+    issue_tile(base + 2 * static_cast<int64_t>(row0) * rs, n_rows - row0, rs, dst, wave);
+  }
+  // The same with `tile` pointing at the tile's first row and `n_valid` rows
+  // from there on that exist.
+  __device__ void issue_tile(const char* tile, int n_valid, int rs, char* dst, int wave) const {
+    n_valid = max(0, min(n_valid, kTile));  // (0: nothing is fetched)
     const __amdgpu_buffer_rsrc_t rsrc =
-        tile_rsrc(base + 2 * static_cast<int64_t>(row0) * rs,
-                  static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
+        tile_rsrc(tile, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
     char* l = dst + wave * NL * 1024;
 #pragma unroll
     for (int n = 0; n < NL; ++n) lds_load16(rsrc, src[n], l + n * 1024);
@@ -293,32 +297,53 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
     if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].diag + 1));
     return n;
   };
+  // A cursor carries its chunk's descriptor (visible keys nk, stored keys len,
+  // diagonal offset diag) and the addresses of its K and V tile for this
+  // (batch, head), set when it enters the chunk and stepped by one tile stride
+  // after that, so the steps issue no scalar loads of their own.
   struct Cur {
     int c, kt;
+    int nk, len, diag;
+    const char* tk;
+    const char* tv;
+  };
+  const int64_t tile_bytes = 2 * static_cast<int64_t>(kTile) * rs;
+  auto enter = [&](Cur& x) {
+    const int c = uni(x.c);
+    if (c < a.nchunks) {  // (a cursor past the list is never used)
+      x.len = a.chunks[c].len;
+      x.diag = a.chunks[c].diag;
+      x.nk = CAUSAL ? max(0, min(x.len, q_last + x.diag + 1)) : x.len;
+      const int64_t off =
+          2 * ((static_cast<int64_t>(b) * x.len + uni(x.kt) * kTile) * rs + static_cast<int64_t>(h) * D);
+      x.tk = reinterpret_cast<const char*>(a.chunks[c].k) + off;
+      x.tv = reinterpret_cast<const char*>(a.chunks[c].v) + off;
+    }
   };
   auto next_of = [&](Cur x) {
-    x.c = uni(x.c);
     x.kt = uni(x.kt) + 1;
-    if (x.kt * kTile >= keys_of(x.c)) {
+    if (x.kt * kTile >= x.nk) {
       x.kt = 0;
-      ++x.c;
+      x.c = uni(x.c) + 1;
       while (x.c < a.nchunks && keys_of(x.c) == 0) ++x.c;
+      enter(x);
+    } else {
+      x.tk += tile_bytes;
+      x.tv += tile_bytes;
     }
     return x;
   };
 
   TileGeo<D> g;
   g.init(wave, lane, rs);
-  auto issue = [&](char* dst, Cur x) {
-    const int c = uni(x.c), key0 = uni(x.kt) * kTile;
-    const BwdChunk& ch = a.chunks[c];
-    const int64_t off = (static_cast<int64_t>(b) * ch.len * a.H + h) * D;
-    g.issue(reinterpret_cast<const char*>(ch.k + off), key0, ch.len, rs, dst, wave);
-    g.issue(reinterpret_cast<const char*>(ch.v + off), key0, ch.len, rs, dst + TB, wave);
+  auto issue = [&](char* dst, const Cur& x) {
+    const int n_valid = x.nk - uni(x.kt) * kTile;
+    g.issue_tile(x.tk, n_valid, rs, dst, wave);
+    g.issue_tile(x.tv, n_valid, rs, dst + TB, wave);
   };
 
   // this group's share of the tiles, in chunk order
-  Cur cur{0, 0};
+  Cur cur{0, 0, 0, 0, 0, nullptr, nullptr};
   int left, steps;
   {
     int total = 0;
@@ -335,6 +360,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
       ++cur.c;
     }
     cur.kt = skip;
+    enter(cur);
   }
 
   f32x16 acc[D / 32];
@@ -354,8 +380,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* smem, int blk) {
         nx = next_of(cur);
         issue(gsm + 2 * (st ^ 1) * TB, nx);
       }
-      const int c = uni(cur.c);
-      const int len = a.chunks[c].len, diag = a.chunks[c].diag;
+      const int len = cur.len, diag = cur.diag;
       const int key0 = uni(cur.kt) * kTile;
       // S^T and dP^T for the tile's 64 keys (two 32-key blocks); register r
       // of block mb is key key0 + 32 mb + 16 (r/8) + 8 half + r%8
