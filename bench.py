@@ -547,8 +547,18 @@ def merge_workload(torch, cp, dev, q0, vis, wf):
             for _ in range(buffer_sets(mbytes))]
     d = time_rotating(torch, [lambda s=s: cp.lse_merge(*s) for s in sets], 1, 10)
     del sets
+    # the ceiling at this size: a plain copy moving the same bytes (read plus
+    # write), timed the same way
+    x = torch.ones((1, 1, mbytes // 4096, 8, 128), dtype=torch.bfloat16, device=dev)
+    cbytes = 2 * x.numel() * x.element_size()
+    pairs = rotating_pairs(x, x, cbytes)
+    dc = time_rotating(torch, [lambda a=a, b=b: cp.ulysses_seq2head(a, 1, b) for a, b in pairs],
+                       1, 10)
+    del pairs, x
     out["flux_lse_merge"] = {"us": d * 1e3, "gbs": mbytes / (d * 1e-3) / 1e9, "bytes": mbytes,
-                             "hbm_frac": mbytes / (d * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                             "hbm_frac": mbytes / (d * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "copy_same_bytes_gbs": cbytes / (dc * 1e-3) / 1e9,
+                             "copy_same_bytes_us": dc * 1e3}
     # the per-hop form of the same rank: one partial per chunk into its slot of
     # the stacked fp32 partials, then the merge (what a P2P ring does per hop)
     flops = attn_flops(q0.shape[1], wf.S, wf.H, wf.D, False)
