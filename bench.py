@@ -430,6 +430,10 @@ def main() -> int:
                      # clock and MFMA busy of this kernel from the rocprofv3
                      # counter pass on the current source (profiles/), or null
                      "measured_sclk_mhz": sclk,
+                     "sclk_source": None if rec is None else
+                     "rocprofv3 counter pass of this kernel code (GRBM_GUI_ACTIVE / 8 over the "
+                     "dispatch), profiles/attn_llm_causal_counters.json; boxes of the pool differ "
+                     "by a few percent",
                      "mfma_busy": None if rec is None else rec.get("mfma_busy"),
                      "peak_at_measured_sclk": (PEAK_BF16_TFLOPS * sclk / 2400.0
                                                if sclk else None)},
