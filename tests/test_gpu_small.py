@@ -447,6 +447,33 @@ def test_ring_small_grids(Sq, H, D, lens):
         assert torch.equal(l.view(torch.uint8), l1.view(torch.uint8))
 
 
+@pytest.mark.parametrize("B,H,Sq,lens,causal,q0", [
+    (2, 16, 1025, (600, 555), False, 0),      # a 1-row last tile
+    (2, 16, 1041, (1041, 200), True, 0),      # 17 rows, causal: the tail sees part of the keys
+    (1, 32, 1056, (700, 0, 900), False, 0),   # 32 rows, an empty chunk
+    (1, 32, 1030, (1030, 1030), True, 1030),  # causal, queries in the second chunk
+])
+def test_ring_short_last_tile(B, H, Sq, lens, causal, q0):
+    """Grids of one to two query tiles per CU (non-causal: keys split across
+    blocks through the workspace) whose last tile holds at most 32 rows. The
+    first rows, the rows before the last tile and the last tile itself
+    against the oracle."""
+    D = 128
+    say(f"ring short last tile B={B} H={H} Sq={Sq} lens={lens} causal={causal}")
+    q, k, v = _qkv(B, Sq, sum(lens), H, D, torch.bfloat16, seed=Sq + H)
+    kd, vd = k.to(DEV), v.to(DEV)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    chunks = [(kd[:, s:s + n].contiguous(), vd[:, s:s + n].contiguous(), int(s))
+              for s, n in zip(starts, lens)]
+    o, lse = cp.ring_attention(q.to(DEV), chunks[::-1], causal=causal, q_pos0=q0)
+    torch.cuda.synchronize()
+    rows = np.r_[0:40, Sq - 200:Sq]   # first rows, the rows before the seam, the tail
+    wo, wl = oracle.chunk_partial(to_f64(q)[:, rows], to_f64(k), to_f64(v), 1 / math.sqrt(D),
+                                  causal, q0 + rows, np.arange(sum(lens)))
+    check_o(o[:, rows], wo, "bf16", "O")
+    check_lse(lse[:, :, rows], wl, "LSE")
+
+
 def test_ring_zero_chunks():
     say("ring with P = 0")
     q = synthetic.make_tensor((1, 40, 2, 64), torch.bfloat16, 1).to(DEV)

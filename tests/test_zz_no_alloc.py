@@ -65,8 +65,9 @@ def test_noalloc_matches_ring_twice_then_smaller():
     need1 = _compare(q, k, v, ch)
     assert 0 < need1 <= cp.NOALLOC_SCRATCH_BYTES
     del q, k, v, ch
-    say("noalloc: call 2 (smaller), Sq 1300 H 24, chunks 1300/777/513")
-    q, k, v, ch = _case(24, 1300, [1300, 777, 513], 4200)
+    # 260 query tiles, two key splits over blocks
+    say("noalloc: call 2 (smaller), Sq 1250 H 26, chunks 1250/777/513")
+    q, k, v, ch = _case(26, 1250, [1250, 777, 513], 4200)
     need2 = _compare(q, k, v, ch)
     assert 0 < need2 < need1
 
