@@ -540,6 +540,327 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
   if (half == 0) a.lse[lrow] = lse_val;
 }
 
+// ---- Ping-pong kernel for one K/V chunk (a Ulysses rank's local attention,
+// a single ring hop). A block is 8 waves over 256 query rows: two groups of
+// 4 waves, 128 rows each, that share every K/V tile in LDS. Each wave
+// alternates two phases per key tile: S(j), the masking and softmax of tile
+// j (vector ALU only), and M(j), O += P(j) V(j) and S(j+1) = K(j+1) Q^T
+// (matrix cores and LDS reads only). Group 1 runs half a step behind
+// group 0, and waves w and w+4 share a SIMD, so on every SIMD one wave is in
+// its softmax while the other keeps the matrix cores busy. A block barrier
+// separates the half-steps. The arithmetic per row is that of
+// attn_bf16_kernel (same products, same order), so results are identical.
+template <int D, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
+  constexpr int NW = 8;
+  constexpr int KB = 64;
+  constexpr int NMB = KB / 32;
+  constexpr int NT = KB / 16;
+  constexpr int UPR = Geo<D>::kUPR;
+  constexpr int RB = Geo<D>::kRowBytes;
+  constexpr int TB = KB * RB;
+  constexpr int NL = KB * UPR / (NW * 64);   // direct loads per wave per tile
+  constexpr int kTM = 256;                   // query rows per block
+  __shared__ __attribute__((aligned(1024))) char s_k0[TB];
+  __shared__ __attribute__((aligned(1024))) char s_k1[TB];
+  __shared__ __attribute__((aligned(1024))) char s_v0[TB];
+  __shared__ __attribute__((aligned(1024))) char s_v1[TB];
+
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w8 = uni(tid >> 6);
+  const int grp = uni(w8 >> 2);
+  const int wave = uni(w8 & 3);
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- block -> (batch*head, 256-row query tile), as in attn_bf16_kernel
+  const int nqt = (a.Sq + kTM - 1) / kTM;
+  const int BH = a.B * a.H;
+  const int nitems = nqt * BH;
+  int bh, qt;
+  if (CAUSAL) {
+    const int L = blockIdx.x;  // heaviest (last) query tiles first
+    qt = nqt - 1 - L / BH;
+    bh = L % BH;
+  } else {
+    const int per_xcd = (nitems + 7) / 8;  // one head's tiles stay on one XCD
+    const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (L >= nitems) return;
+    bh = L / nqt;
+    qt = L % nqt;
+  }
+  const int b = uni(bh / a.H);
+  const int h = uni(bh - b * a.H);
+  const int blk_first = qt * kTM;
+  const int blk_last = min(blk_first + kTM - 1, a.Sq - 1);
+  const int q_first = blk_first + grp * 128;          // the group's first row
+  const int irow = q_first + wave * 32 + col;
+
+  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  bf16x8 qf[D / 16];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                       ((static_cast<int64_t>(b) * a.Sq + min(irow, a.Sq - 1)) * a.H + h) * D +
+                       8 * half;
+    const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      w ^= flip;
+      if (irow >= a.Sq) w = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int rs = a.H * D;
+  uint32_t k_src[NL], v_src[NL];
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    const int s = (w8 * NL + n) * 64 + lane;
+    const int row = s / UPR, pu = s % UPR;
+    const int k_key = swap_bits23(row), k_unit = pu ^ (row & Geo<D>::kKMask);
+    const int v_unit = pu ^ ((row & 3) << 1);
+    k_src[n] = 2u * static_cast<uint32_t>(k_key * rs + k_unit * 8);
+    v_src[n] = 2u * static_cast<uint32_t>(row * rs + v_unit * 8);
+  }
+
+  // the chunk: its keys this block can see, and its K/V rows of this (b, h)
+  const int len = a.chunks[0].len;
+  const int delta = a.chunks[0].delta;
+  const int nk = CAUSAL ? max(0, min(len, blk_last + delta + 1)) : len;
+  const int64_t tile_bytes = 2 * static_cast<int64_t>(KB) * rs;
+  const char* kbase0 = reinterpret_cast<const char*>(a.chunks[0].k) +
+                       2 * (static_cast<int64_t>(b) * len * rs + h * D);
+  const char* vbase0 = reinterpret_cast<const char*>(a.chunks[0].v) +
+                       2 * (static_cast<int64_t>(b) * len * rs + h * D);
+  auto issue = [&](char* dst, int t_abs, bool is_v) {
+    const int n_valid = max(0, min(nk - t_abs * KB, KB));
+    const char* base = (is_v ? vbase0 : kbase0) + t_abs * tile_bytes;
+    char* l = dst + w8 * NL * 1024;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
+#pragma unroll
+    for (int n = 0; n < NL; ++n) lds_load16(rsrc, is_v ? v_src[n] : k_src[n], l + n * 1024);
+  };
+
+  uint32_t k_rd[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = k_unit_off<D>(col, 2 * ks + half);
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_row = 8 * (g16 >> 1) + (j16 >> 2);
+  const int v_el = 16 * (g16 & 1) + 4 * (j16 & 3);
+  uint32_t v_rd[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+    v_rd[md] = v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+
+  auto qk = [&](const char* kl, f32x16* sacc) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + k_rd[ks] + mb * 32 * RB);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks],
+                                                           ks == 0 ? f32x16{} : sacc[mb], 0, 0, 0);
+      }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int n = uni((nk + KB - 1) / KB);  // key tiles of this block
+
+  // Two phases per tile and wave. S(j): masking and softmax of tile j (VALU
+  // only). M(j): O += P(j) V(j) and S(j+1) = K(j+1) Q^T (matrix cores and LDS
+  // reads only). Group 1 runs half a step behind group 0, so on every SIMD one
+  // wave is in an S phase while the other is in an M phase.
+  f32x16 sacc[NMB];
+  bf16x8 pf[NT];
+  auto phase_s = [&](int j) {
+    const int key0 = j * KB;
+    const bool masked = (key0 + KB > len) || (CAUSAL && key0 + KB - 1 > q_first + delta);
+    if (masked) {
+      asm volatile("" ::: "memory");
+      int lim = len - key0;
+      if (CAUSAL) lim = min(lim, irow + delta - key0 + 1);
+      lim -= 8 * half;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) sacc[mb][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+#pragma unroll
+    for (int r = 3; r < 31; r += 2)
+      mx = fmaxf(fmaxf(mx, sacc[r >> 4][r & 15]), sacc[(r + 1) >> 4][(r + 1) & 15]);
+    mx = fmaxf(mx, sacc[1][15]);
+    mx = pair_max(mx) * sl2;
+    if (__ballot(mx > m_run + kTau)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md) oacc[md] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(sacc[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
+        psum += p;
+        pf[t][e] = static_cast<__bf16>(p);
+      }
+    l_run += psum;
+  };
+  auto phase_m = [&](const char* kl, const char* vl) {
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const char* vr = vl + v_rd[md] + 16 * t * RB;
+        const bf16x4 lo = read_tr(vr);
+        const bf16x4 hi = read_tr(vr + 4 * RB);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
+      }
+    }
+    qk(kl, sacc);
+    // one MFMA per group with its fragment reads two groups ahead
+    constexpr int NVF = NT * (D / 32), NKF = NMB * (D / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < NVF; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (k < NVF - 2)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NKF; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // End of a half-step: copies issued in this half-step may stay in flight,
+  // older ones have landed, this wave's LDS reads are done; then the block
+  // barrier. (A plain s_barrier: the workgroup fence of __syncthreads would
+  // also wait for the copies still in flight.)
+  auto sync = [&](bool issued_now) {
+    if (issued_now) {
+      if (NL == 2) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) expcnt(7) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0x0072);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    }
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // prologue: K(0), K(1), V(0); S(0) for both groups, group 0's softmax of tile 0
+  if (n > 0) {
+    issue(s_k0, 0, false);
+    issue(s_v0, 0, true);
+    if (n > 1) issue(s_k1, 1, false);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n > 0) qk(s_k0, sacc);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (grp == 0 && n > 0) phase_s(0);
+
+  // half-step hs = 2j: copies K(j+2) and V(j+1); group 0 M(j), group 1 S(j).
+  // hs = 2j+1: group 0 S(j+1), group 1 M(j). K(j+1) sits in stage (j+1)&1,
+  // V(j) in stage j&1; Q = hs % 4 fixes them at compile time.
+  auto copies = [&](auto q_tag, int hs) {
+    constexpr int Q = decltype(q_tag)::value;
+    const int j = hs >> 1;
+    bool any = false;
+    if (Q % 2 == 0) {
+      if (j + 2 < n) { issue(Q == 0 ? s_k0 : s_k1, j + 2, false); any = true; }
+      if (j + 1 < n) { issue(Q == 0 ? s_v1 : s_v0, j + 1, true); any = true; }
+    }
+    return any;
+  };
+  auto hs_g0 = [&](auto q_tag, int hs) {
+    constexpr int Q = decltype(q_tag)::value;
+    const int j = hs >> 1;
+    const bool issued = copies(q_tag, hs);
+    if (Q == 0 && j < n) phase_m(s_k1, s_v0);
+    if (Q == 1 && j + 1 < n) phase_s(j + 1);
+    if (Q == 2 && j < n) phase_m(s_k0, s_v1);
+    if (Q == 3 && j + 1 < n) phase_s(j + 1);
+    sync(issued);
+  };
+  auto hs_g1 = [&](auto q_tag, int hs) {
+    constexpr int Q = decltype(q_tag)::value;
+    const int j = hs >> 1;
+    const bool issued = copies(q_tag, hs);
+    if (Q == 0 && j < n) phase_s(j);
+    if (Q == 1 && j < n) phase_m(s_k1, s_v0);
+    if (Q == 2 && j < n) phase_s(j);
+    if (Q == 3 && j < n) phase_m(s_k0, s_v1);
+    sync(issued);
+  };
+  const int nh = 2 * n;
+  if (grp == 0) {
+    for (int hs = 0; hs < nh; hs += 4) {
+      hs_g0(std::integral_constant<int, 0>{}, hs);
+      hs_g0(std::integral_constant<int, 1>{}, hs + 1);
+      if (hs + 2 >= nh) break;
+      hs_g0(std::integral_constant<int, 2>{}, hs + 2);
+      hs_g0(std::integral_constant<int, 3>{}, hs + 3);
+    }
+  } else {
+    for (int hs = 0; hs < nh; hs += 4) {
+      hs_g1(std::integral_constant<int, 0>{}, hs);
+      hs_g1(std::integral_constant<int, 1>{}, hs + 1);
+      if (hs + 2 >= nh) break;
+      hs_g1(std::integral_constant<int, 2>{}, hs + 2);
+      hs_g1(std::integral_constant<int, 3>{}, hs + 3);
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  const int i = irow;
+  if (i >= a.Sq) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
+  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
+  const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * md + 8 * g + 4 * half;
+      const float x0 = oacc[md][4 * g] * inv, x1 = oacc[md][4 * g + 1] * inv;
+      const float x2 = oacc[md][4 * g + 2] * inv, x3 = oacc[md][4 * g + 3] * inv;
+      if (OUT_BF16) {
+        bf16x4 r;
+        r[0] = static_cast<__bf16>(x0);
+        r[1] = static_cast<__bf16>(x1);
+        r[2] = static_cast<__bf16>(x2);
+        r[3] = static_cast<__bf16>(x3);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + orow + d0) = r;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) =
+            make_float4(x0, x1, x2, x3);
+      }
+    }
+  }
+  if (half == 0) a.lse[lrow] = lse_val;
+}
+
 template <int D, bool CAUSAL, bool OUT_BF16, int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBM - 1) / kBM;
@@ -557,8 +878,17 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-  return a.groups == 2 ? launch_g<D, CAUSAL, OUT_BF16, 2>(a, stream)
-                       : launch_g<D, CAUSAL, OUT_BF16, 1>(a, stream);
+  if (a.groups == 2) return launch_g<D, CAUSAL, OUT_BF16, 2>(a, stream);
+  if (a.nchunks == 1 && a.nsplit <= 1) {
+    // one chunk, no key splits: the ping-pong kernel, 256 query rows a block
+    const int64_t nqt = (a.Sq + 255) / 256;
+    const int64_t nitems = nqt * a.B * a.H;
+    const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
+    hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
+  return launch_g<D, CAUSAL, OUT_BF16, 1>(a, stream);
 }
 
 
