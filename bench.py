@@ -425,7 +425,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": h["achieved"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": h["achieved"] / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "attn_bf16_kernel<128, causal=true, out_bf16=true, groups=1>",
+                     "kernel": "attn_pp_kernel<128, causal=true, out_bf16=true> (8-wave blocks of 256 query rows)",
                      "flop_per_launch": h["flops"], "kernel_ms": h["attn_ms"],
                      # clock and MFMA busy of this kernel from the rocprofv3
                      # counter pass on the current source (profiles/), or null
@@ -846,8 +846,14 @@ def ring_anything_workload(torch, cp, synthetic, dev):
             s0, n = starts[r], w.chunk_lens[r]
             qr = q[:, s0:s0 + n].contiguous()
             vis = [chunks[c] for c in synthetic.ring_order(r, w.P)]
+            # outputs and workspace allocated once, as a training step would
+            o = torch.empty_like(qr)
+            lse = torch.empty((1, w.H, n), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(1, cp.ring_attention_workspace_bytes(w.P, 1, w.H, n, w.D)),
+                             dtype=torch.uint8, device=dev)
             d = [time_back_to_back(
-                torch, lambda: cp.ring_attention(qr, vis, causal=causal, q_pos0=s0), 5, 50)]
+                torch, lambda: cp.ring_attention(qr, vis, o, lse, causal=causal, q_pos0=s0,
+                                                 workspace=ws), 5, 50)]
             tot_us += median(d) * 1e3
             tot_flops += attn_flops(n, w.S, w.H, w.D, causal, s0, 0)
         res["causal" if causal else "noncausal"] = {
