@@ -348,7 +348,7 @@ def flux_ring(torch, cp, synthetic, dev):
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                         "traffic": traffic_record(FLUX_TRAFFIC_FILE),
-                        "kernel": "attn_bf16_kernel<128, causal=false, out_bf16=true>"}}
+                        "kernel": "attn_g2pp_kernel<128, causal=false, out_bf16=true> (two-group ping-pong)"}}
     return res, q0, vis
 
 

@@ -861,6 +861,430 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   if (half == 0) a.lse[lrow] = lse_val;
 }
 
+// ---- Two-group ping-pong kernel for small grids (no more query tiles than
+// CUs, at least four key tiles), head dim 128. A block is 8 waves over one
+// 128-row query tile, as in the two-group case of attn_bf16_kernel: group g
+// takes the g-th half of the tile's key tiles (in chunk order) through LDS
+// stages of its own, and the two halves are merged through LDS at the end.
+// Each wave alternates the S and M phases of attn_pp_kernel with group 1
+// half a step behind group 0, so the two waves on a SIMD are always in
+// opposite phases. Same products in the same order as the two-group case of
+// attn_bf16_kernel, so the results are identical. (At head dim 64 the
+// softmax outweighs the matrix work and that kernel is faster.)
+template <int D, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
+  constexpr int WPG = 4;
+  constexpr int TPG = WPG * 64;
+  constexpr int KB = 64;
+  constexpr int NMB = KB / 32;
+  constexpr int NT = KB / 16;
+  constexpr int UPR = Geo<D>::kUPR;
+  constexpr int RB = Geo<D>::kRowBytes;
+  constexpr int TB = KB * RB;
+  constexpr int NL = KB * UPR / TPG;   // direct loads per wave per tile (its group's)
+  __shared__ __attribute__((aligned(1024))) char s_k0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char s_k1[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char s_v0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char s_v1[2 * TB];
+
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto uni_ptr = [](const char* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int grp = uni(tid / TPG);
+  const int wave = uni((tid >> 6) % WPG);
+  const int col = lane & 31, half = lane >> 5;
+  const uint32_t gbase = static_cast<uint32_t>(grp * TB);
+
+  const int nqt = (a.Sq + kBM - 1) / kBM;
+  const int BH = a.B * a.H;
+  const int nitems = nqt * BH;
+  int bh, qt;
+  if (CAUSAL) {
+    const int L = blockIdx.x;
+    qt = nqt - 1 - L / BH;
+    bh = L % BH;
+  } else {
+    const int per_xcd = (nitems + 7) / 8;
+    const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (L >= nitems) return;
+    bh = L / nqt;
+    qt = L % nqt;
+  }
+  const int b = uni(bh / a.H);
+  const int h = uni(bh - b * a.H);
+  const int q_first = qt * kBM;
+  const int irow = q_first + wave * 32 + col;
+  const int q_last = min(q_first + kBM - 1, a.Sq - 1);
+
+  const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  bf16x8 qf[D / 16];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                       ((static_cast<int64_t>(b) * a.Sq + min(irow, a.Sq - 1)) * a.H + h) * D +
+                       8 * half;
+    const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      w ^= flip;
+      if (irow >= a.Sq) w = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int rs = a.H * D;
+  uint32_t k_src[NL], v_src[NL];
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    const int s = (wave * NL + n) * 64 + lane;
+    const int row = s / UPR, pu = s % UPR;
+    const int k_key = swap_bits23(row), k_unit = pu ^ (row & Geo<D>::kKMask);
+    const int v_unit = pu ^ ((row & 3) << 1);
+    k_src[n] = 2u * static_cast<uint32_t>(k_key * rs + k_unit * 8);
+    v_src[n] = 2u * static_cast<uint32_t>(row * rs + v_unit * 8);
+  }
+
+  auto keys_of = [&](int c) {
+    c = uni(c);
+    int n = a.chunks[c].len;
+    if (CAUSAL) n = max(0, min(n, q_last + a.chunks[c].delta + 1));
+    return n;
+  };
+  struct Cur {
+    int c, kt;
+    int nk, len, delta;
+    const char* tk;
+    const char* tv;
+  };
+  const int64_t tile_bytes = 2 * static_cast<int64_t>(KB) * rs;
+  auto enter = [&](Cur& x) {
+    const int c = uni(x.c);
+    if (c < a.nchunks) {
+      x.len = uni(a.chunks[c].len);
+      x.delta = uni(a.chunks[c].delta);
+      x.nk = uni(CAUSAL ? max(0, min(x.len, q_last + x.delta + 1)) : x.len);
+      const int64_t off =
+          2 * ((static_cast<int64_t>(b) * x.len + uni(x.kt) * KB) * rs + h * D);
+      x.tk = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].k) + off);
+      x.tv = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].v) + off);
+    }
+  };
+  auto next_of = [&](Cur x) {
+    x.kt = uni(x.kt) + 1;
+    if (x.kt * KB >= x.nk) {
+      x.kt = 0;
+      x.c = uni(x.c) + 1;
+      while (x.c < a.nchunks && keys_of(x.c) == 0) ++x.c;
+      enter(x);
+    } else {
+      x.tk = uni_ptr(x.tk + tile_bytes);
+      x.tv = uni_ptr(x.tv + tile_bytes);
+    }
+    return x;
+  };
+  // copy one tile (n_valid rows of it from base, zeros for the rest) into dst
+  auto issue = [&](char* dst, const char* base, int n_valid, bool is_v) {
+    char* l = dst + gbase + wave * NL * 1024;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
+#pragma unroll
+    for (int n = 0; n < NL; ++n) lds_load16(rsrc, is_v ? v_src[n] : k_src[n], l + n * 1024);
+  };
+
+  uint32_t k_rd[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) k_rd[ks] = gbase + k_unit_off<D>(col, 2 * ks + half);
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_row = 8 * (g16 >> 1) + (j16 >> 2);
+  const int v_el = 16 * (g16 & 1) + 4 * (j16 & 3);
+  uint32_t v_rd[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+    v_rd[md] = gbase + v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+
+  auto qk = [&](const char* kl, f32x16* sacc) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + k_rd[ks] + mb * 32 * RB);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks],
+                                                           ks == 0 ? f32x16{} : sacc[mb], 0, 0, 0);
+      }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // this group's half of the query tile's key tiles, in chunk order
+  Cur cur0{0, 0, 0, 0, 0, nullptr, nullptr};
+  int n, steps;
+  {
+    int total = 0;
+    for (int cc = 0; cc < a.nchunks; ++cc) total += (keys_of(cc) + KB - 1) / KB;
+    const int t_begin = grp == 0 ? 0 : total / 2;
+    const int t_end = grp == 0 ? total / 2 : total;
+    n = uni(t_end - t_begin);
+    steps = uni(total - total / 2);  // both groups run the longer half's half-steps
+    int skip = t_begin;
+    while (cur0.c < a.nchunks) {
+      const int nt = (keys_of(cur0.c) + KB - 1) / KB;
+      if (skip < nt) break;
+      skip -= nt;
+      ++cur0.c;
+    }
+    cur0.kt = skip;
+    enter(cur0);
+  }
+
+  f32x16 sacc[NMB];
+  bf16x8 pf[NT];
+  // ck = the tile of the next K copy. What later phases need of a tile is
+  // taken when its K copy goes out: the V source and row count (its V copy
+  // follows one S phase later) and the mask bounds relative to its first key,
+  // rl = len - key0 and rd = delta - key0 (its S phase follows two S phases
+  // later). ma/mb: mask bounds of the tiles of the next two S phases; vb_*:
+  // the next V copy.
+  Cur ck = cur0;
+  int ma_rl = 0, ma_rd = 0, mb_rl = 0, mb_rd = 0, vb_n = 0;
+  const char* vb_p = nullptr;
+  auto take = [&](int& rl, int& rd) {
+    const int key0 = uni(ck.kt) * KB;
+    rl = uni(ck.len - key0);
+    rd = uni(ck.delta - key0);
+    vb_p = ck.tv;
+    vb_n = uni(max(0, min(ck.nk - key0, KB)));
+  };
+  auto phase_s = [&]() {
+    const int rl = ma_rl, rd = ma_rd;
+    const bool masked = (rl < KB) || (CAUSAL && rd < KB - 1 - q_first);
+    if (masked) {
+      asm volatile("" ::: "memory");
+      int lim = rl;
+      if (CAUSAL) lim = min(lim, irow + rd + 1);
+      lim -= 8 * half;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 16 * (r >> 3) + (r & 7) >= lim) sacc[mb][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+#pragma unroll
+    for (int r = 3; r < 31; r += 2)
+      mx = fmaxf(fmaxf(mx, sacc[r >> 4][r & 15]), sacc[(r + 1) >> 4][(r + 1) & 15]);
+    mx = fmaxf(mx, sacc[1][15]);
+    mx = pair_max(mx) * sl2;
+    if (__ballot(mx > m_run + kTau)) {
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md) oacc[md] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(sacc[t >> 1][(t & 1) * 8 + e], sl2, neg_m));
+        psum += p;
+        pf[t][e] = static_cast<__bf16>(p);
+      }
+    l_run += psum;
+  };
+  // copies at S(s): V(s+1) and K(s+2) of this group's tiles; then the cursors move on
+  // (pend = tiles copied by this wave's latest S phase: they are read three
+  // half-steps after the copy, so each barrier may leave them in flight)
+  int pend = 0;
+  auto s_copies = [&](int s, char* kdst, char* vdst) {
+    pend = 0;
+    if (s + 1 < n) { issue(vdst, vb_p, vb_n, true); ++pend; }
+    ma_rl = mb_rl;
+    ma_rd = mb_rd;
+    if (s + 2 < n) {
+      take(mb_rl, mb_rd);
+      issue(kdst, ck.tk, vb_n, false);
+      ++pend;
+      if (s + 3 < n) ck = next_of(ck);
+    }
+  };
+  auto phase_m = [&](const char* kl, const char* vl) {
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const char* vr = vl + v_rd[md] + 16 * t * RB;
+        const bf16x4 lo = read_tr(vr);
+        const bf16x4 hi = read_tr(vr + 4 * RB);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
+      }
+    }
+    qk(kl, sacc);
+    constexpr int NVF = NT * (D / 32), NKF = NMB * (D / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < NVF; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (k < NVF - 2)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NKF; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto sync = [&]() {
+    if (pend == 2)
+      __builtin_amdgcn_s_waitcnt(static_cast<short>(0x0070 | (2 * NL)));  // vmcnt(2 NL), lgkmcnt(0)
+    else if (pend == 1)
+      __builtin_amdgcn_s_waitcnt(static_cast<short>(0x0070 | NL));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // prologue: K(0), V(0), K(1) of each group's half; S(0); group 0's S(0)
+  if (n > 0) {
+    take(ma_rl, ma_rd);
+    issue(s_k0, ck.tk, vb_n, false);
+    issue(s_v0, vb_p, vb_n, true);
+    if (n > 1) {
+      ck = next_of(ck);
+      take(mb_rl, mb_rd);
+      issue(s_k1, ck.tk, vb_n, false);
+      if (n > 2) ck = next_of(ck);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n > 0) qk(s_k0, sacc);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // (now: ma = tile 0, mb and vb = tile 1, ck = tile 2)
+  if (grp == 0 && n > 0) {
+    phase_s();
+    s_copies(0, s_k0, s_v1);
+  }
+
+  // Group 0: M(j) at hs = 2j (K(j+1) in stage (j+1)&1, V(j) in stage j&1),
+  // S(j+1) with its copies at hs = 2j+1. Group 1 one half-step later: S(j)
+  // with its copies at hs = 2j, M(j) at hs = 2j+1. Q = hs % 4 fixes the stages.
+  auto hs_g0 = [&](auto q_tag, int hs) {
+    constexpr int Q = decltype(q_tag)::value;
+    const int j = hs >> 1;
+    if (Q == 0 && j < n) phase_m(s_k1, s_v0);
+    if (Q == 2 && j < n) phase_m(s_k0, s_v1);
+    if (Q == 1 && j + 1 < n) { phase_s(); s_copies(j + 1, s_k1, s_v0); }
+    if (Q == 3 && j + 1 < n) { phase_s(); s_copies(j + 1, s_k0, s_v1); }
+    sync();
+  };
+  auto hs_g1 = [&](auto q_tag, int hs) {
+    constexpr int Q = decltype(q_tag)::value;
+    const int j = hs >> 1;
+    if (Q == 0 && j < n) { phase_s(); s_copies(j, s_k0, s_v1); }
+    if (Q == 2 && j < n) { phase_s(); s_copies(j, s_k1, s_v0); }
+    if (Q == 1 && j < n) phase_m(s_k1, s_v0);
+    if (Q == 3 && j < n) phase_m(s_k0, s_v1);
+    sync();
+  };
+  const int nh = 2 * steps;
+  if (grp == 0) {
+    for (int hs = 0; hs < nh; hs += 4) {
+      hs_g0(std::integral_constant<int, 0>{}, hs);
+      hs_g0(std::integral_constant<int, 1>{}, hs + 1);
+      if (hs + 2 >= nh) break;
+      hs_g0(std::integral_constant<int, 2>{}, hs + 2);
+      hs_g0(std::integral_constant<int, 3>{}, hs + 3);
+    }
+  } else {
+    for (int hs = 0; hs < nh; hs += 4) {
+      hs_g1(std::integral_constant<int, 0>{}, hs);
+      hs_g1(std::integral_constant<int, 1>{}, hs + 1);
+      if (hs + 2 >= nh) break;
+      hs_g1(std::integral_constant<int, 2>{}, hs + 2);
+      hs_g1(std::integral_constant<int, 3>{}, hs + 3);
+    }
+  }
+
+  // ---- epilogue: merge the two key halves, normalise, write O and LSE
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  {
+    constexpr int HM = D / 64;
+    auto xo = [&](int md, int r) -> float& {
+      float* base = reinterpret_cast<float*>(md < HM ? s_v0 : s_v1);
+      return base[((wave * HM + md % HM) * 16 + r) * 64 + lane];
+    };
+    float* xs = reinterpret_cast<float*>(s_k0);
+    if (grp == 1) {
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo(md, r) = oacc[md][r];
+      xs[(wave * 2) * 64 + lane] = m_run;
+      xs[(wave * 2 + 1) * 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[(wave * 2) * 64 + lane], l1 = xs[(wave * 2 + 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    l_tot = a0 * l_tot + a1 * l1;
+#pragma unroll
+    for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[md][r] = a0 * oacc[md][r] + a1 * xo(md, r);
+    m_run = mm;
+  }
+  const int i = irow;
+  if (i >= a.Sq) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
+  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
+  const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * md + 8 * g + 4 * half;
+      const float x0 = oacc[md][4 * g] * inv, x1 = oacc[md][4 * g + 1] * inv;
+      const float x2 = oacc[md][4 * g + 2] * inv, x3 = oacc[md][4 * g + 3] * inv;
+      if (OUT_BF16) {
+        bf16x4 r;
+        r[0] = static_cast<__bf16>(x0);
+        r[1] = static_cast<__bf16>(x1);
+        r[2] = static_cast<__bf16>(x2);
+        r[3] = static_cast<__bf16>(x3);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + orow + d0) = r;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) =
+            make_float4(x0, x1, x2, x3);
+      }
+    }
+  }
+  if (half == 0) a.lse[lrow] = lse_val;
+}
+
 template <int D, bool CAUSAL, bool OUT_BF16, int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBM - 1) / kBM;
@@ -878,7 +1302,18 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-  if (a.groups == 2) return launch_g<D, CAUSAL, OUT_BF16, 2>(a, stream);
+  if (a.groups == 2) {
+    if constexpr (D == 64) {
+      return launch_g<D, CAUSAL, OUT_BF16, 2>(a, stream);
+    } else {
+      // one 128-row query tile a block, its keys split between two groups
+      const int64_t nitems = (a.Sq + kBM - 1) / kBM * a.B * a.H;
+      const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
+      hipLaunchKernelGGL((attn_g2pp_kernel<D, CAUSAL, OUT_BF16>),
+                         dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.nchunks == 1 && a.nsplit <= 1) {
     // one chunk, no key splits: the ping-pong kernel, 256 query rows a block
     const int64_t nqt = (a.Sq + 255) / 256;

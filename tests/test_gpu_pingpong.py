@@ -1,12 +1,19 @@
-"""GPU parity of the ping-pong attention kernel (one K/V chunk on grids of
-more query tiles than CUs: 8-wave blocks over 256 query rows, two groups half
-a step apart) against the fp64 oracle.
+"""GPU parity of the ping-pong attention kernels against the fp64 oracle.
 
-Shapes put the last 256-row block's second group partly or wholly past Sq,
-make keys ragged, empty or shorter than a tile, and cover causal offsets,
-D = 64, fp32 outputs, a negative scale and the ring entry point with one
-chunk. Rows are sampled: the first rows, both sides of every block and group
-boundary near the end, and the last rows.
+attn_pp_kernel: one K/V chunk on grids of more query tiles than CUs (8-wave
+blocks over 256 query rows, two groups half a step apart). Shapes put the
+last 256-row block's second group partly or wholly past Sq, make keys
+ragged, empty or shorter than a tile, and cover causal offsets, D = 64, fp32
+outputs, a negative scale and the ring entry point with one chunk.
+
+attn_g2pp_kernel: small grids (no more query tiles than CUs, at least four
+key tiles, D = 128): 8-wave blocks over one 128-row query tile whose two
+groups take the two halves of its key tiles. Shapes give each group one,
+two or three tiles, none at all (a query tile that sees one key tile, or
+none), ragged and empty chunks in ring order, and fp32 outputs.
+
+Rows are sampled: the first rows, both sides of every block and group
+boundary, and the last rows.
 """
 import math
 
@@ -99,3 +106,57 @@ def test_pingpong_through_the_ring_with_one_chunk():
     o, lse = cp.ring_attention(q.to(DEV), [(k.to(DEV), v.to(DEV), 0)], causal=True, q_pos0=300)
     torch.cuda.synchronize()
     _check(o, lse, q, k, v, 1 / math.sqrt(D), True, 300, 0, torch.bfloat16)
+
+
+def _small_grid(B, H, Sq, tiles):
+    # the launcher's choice of the two-group kernel on a 256-CU part
+    return B * H * ((Sq + 127) // 128) <= 256 and tiles >= 4
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,causal,q0,k0,out_dtype", [
+    (1, 24, 300, 256, False, 0, 0, torch.bfloat16),     # 4 key tiles: 2 per group
+    (1, 24, 300, 300, True, 0, 0, torch.bfloat16),      # first query tile: 1 tile per group
+    (2, 12, 640, 320, False, 0, 0, torch.float32),      # 5 tiles: 2 and 3, fp32 out
+    (1, 24, 700, 900, True, 0, 64, torch.bfloat16),     # first query tile: 1 tile, group 0 none
+    (1, 24, 700, 900, True, 0, 200, torch.bfloat16),    # first query tile sees no key at all
+    (1, 20, 1000, 4000, True, 3000, 0, torch.bfloat16), # long, ragged last query tile
+])
+def test_two_group_chunk_partial(B, H, Sq, Skv, causal, q0, k0, out_dtype):
+    D = 128
+    say(f"two-group ping-pong chunk partial B={B} H={H} Sq={Sq} Skv={Skv} causal={causal} "
+        f"q0={q0} k0={k0} {out_dtype}")
+    assert _small_grid(B, H, Sq, (Skv + 63) // 64)
+    q = synthetic.make_tensor((B, Sq, H, D), torch.bfloat16, 3 * Sq + Skv + H)
+    k = synthetic.make_tensor((B, Skv, H, D), torch.bfloat16, 3 * Sq + Skv + H + 1)
+    v = synthetic.make_tensor((B, Skv, H, D), torch.bfloat16, 3 * Sq + Skv + H + 2)
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, q_pos0=q0,
+                                   kv_pos0=k0, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(o, lse, q, k, v, 1 / math.sqrt(D), causal, q0, k0, out_dtype)
+
+
+@pytest.mark.parametrize("H,Sq,lens,pos,order,causal,q0", [
+    # FLUX-like rank: four chunks in ring order, one ragged and one short
+    (24, 1152, (1152, 1000, 77, 1152), (0, 1152, 2152, 2229), (2, 0, 3, 1), False, 0),
+    # causal, reversed visit order, an empty chunk, the diagonal chunk last
+    (8, 900, (512, 0, 700, 300), (0, 512, 512, 1212), (3, 2, 1, 0), True, 700),
+    # causal from position 0: the first query tiles see few keys
+    (16, 500, (400, 400), (0, 400), (1, 0), True, 0),
+])
+def test_two_group_ring(H, Sq, lens, pos, order, causal, q0):
+    B, D = 1, 128
+    say(f"two-group ping-pong ring H={H} Sq={Sq} lens={lens} order={order} causal={causal} "
+        f"q0={q0}")
+    assert _small_grid(B, H, Sq, sum((n + 63) // 64 for n in lens))
+    q = synthetic.make_tensor((B, Sq, H, D), torch.bfloat16, 81 + H)
+    ks = [synthetic.make_tensor((B, n, H, D), torch.bfloat16, 90 + 3 * c) for c, n in enumerate(lens)]
+    vs = [synthetic.make_tensor((B, n, H, D), torch.bfloat16, 91 + 3 * c) for c, n in enumerate(lens)]
+    dev = [(ks[c].to(DEV), vs[c].to(DEV), pos[c]) for c in range(len(lens))]
+    o, lse = cp.ring_attention(q.to(DEV), [dev[c] for c in order], causal=causal, q_pos0=q0)
+    torch.cuda.synchronize()
+    rows = _rows(Sq)
+    ref = [(to_f64(ks[c]), to_f64(vs[c]), pos[c] + np.arange(lens[c])) for c in range(len(lens))]
+    wo, wl = oracle.ring_attention(to_f64(q)[:, rows], ref, order, 1 / math.sqrt(D), causal,
+                                   q0 + rows)
+    check_o(o[:, rows], wo, "bf16", "O")
+    check_lse(lse[:, :, rows], wl, "LSE")
