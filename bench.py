@@ -247,6 +247,19 @@ def copy_ceiling(torch, cp, dev) -> float:
     return nbytes / (d * 1e-3) / 1e9
 
 
+def copy_same_bytes(torch, cp, dev, nbytes: int):
+    """(GB/s, us) of a plain copy that moves nbytes (read plus write), timed
+    like the HBM-bound launch it is compared with: the ceiling at that size,
+    where launch ramp and tail weigh more than on the 512 MiB copy."""
+    x = torch.ones((1, 1, max(1, nbytes // 4096), 8, 128), dtype=torch.bfloat16, device=dev)
+    cbytes = 2 * x.numel() * x.element_size()
+    pairs = rotating_pairs(x, x, cbytes)
+    dc = time_rotating(torch, [lambda a=a, b=b: cp.ulysses_seq2head(a, 1, b) for a, b in pairs],
+                       1, 10)
+    del pairs, x
+    return cbytes / (dc * 1e-3) / 1e9, dc * 1e3
+
+
 def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
     """The 128K causal Ulysses rank's step: stacked seq2head of Q, K, V (all 8
     ranks' regrouping), rank 0's causal attention on its 4 heads, head2seq of O
@@ -551,18 +564,11 @@ def merge_workload(torch, cp, dev, q0, vis, wf):
             for _ in range(buffer_sets(mbytes))]
     d = time_rotating(torch, [lambda s=s: cp.lse_merge(*s) for s in sets], 1, 10)
     del sets
-    # the ceiling at this size: a plain copy moving the same bytes (read plus
-    # write), timed the same way
-    x = torch.ones((1, 1, mbytes // 4096, 8, 128), dtype=torch.bfloat16, device=dev)
-    cbytes = 2 * x.numel() * x.element_size()
-    pairs = rotating_pairs(x, x, cbytes)
-    dc = time_rotating(torch, [lambda a=a, b=b: cp.ulysses_seq2head(a, 1, b) for a, b in pairs],
-                       1, 10)
-    del pairs, x
+    # the ceiling at this size: a plain copy moving the same bytes
+    c_gbs, c_us = copy_same_bytes(torch, cp, dev, mbytes)
     out["flux_lse_merge"] = {"us": d * 1e3, "gbs": mbytes / (d * 1e-3) / 1e9, "bytes": mbytes,
                              "hbm_frac": mbytes / (d * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "copy_same_bytes_gbs": cbytes / (dc * 1e-3) / 1e9,
-                             "copy_same_bytes_us": dc * 1e3}
+                             "copy_same_bytes_gbs": c_gbs, "copy_same_bytes_us": c_us}
     # the per-hop form of the same rank: one partial per chunk into its slot of
     # the stacked fp32 partials, then the merge (what a P2P ring does per hop)
     flops = attn_flops(q0.shape[1], wf.S, wf.H, wf.D, False)
@@ -610,6 +616,8 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
     d_s2h3 = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_seq2head(x, P, y)
                                    for x, y in pairs], 1, 5)
     del pairs
+    copy1 = copy_same_bytes(torch, cp, dev, nbytes)
+    copy3 = copy_same_bytes(torch, cp, dev, 3 * nbytes)
     res = {
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
@@ -623,11 +631,13 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
         "seq2head_qkv_us": d_s2h3 * 1e3,
         "seq2head_qkv_gbs": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9,
         "seq2head_qkv_hbm_frac": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "copy_same_bytes_gbs": copy1[0], "copy_same_bytes_qkv_gbs": copy3[0],
         "causal": w.causal, "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
-        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}")
+        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}; same-size copies "
+        f"{res['copy_same_bytes_gbs']:.0f} / {res['copy_same_bytes_qkv_gbs']:.0f}")
     del qkv, heads, rq, rk, rv
     torch.cuda.empty_cache()
     return res
@@ -654,6 +664,8 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
     d_s2h3 = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_anything_seq2head(
         x, s_lens, h_counts, 1, D, y) for x, y in pairs], 1, 5)
     del pairs
+    copy1 = copy_same_bytes(torch, cp, dev, nbytes)
+    copy3 = copy_same_bytes(torch, cp, dev, 3 * nbytes)
     for x, y in zip(qkv, groups):
         cp.ulysses_anything_seq2head(x, s_lens, h_counts, 1, D, y)
     h0 = h_counts[0]
@@ -677,11 +689,13 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
         "seq2head_qkv_us": d_s2h3 * 1e3,
         "seq2head_qkv_gbs": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9,
         "seq2head_qkv_hbm_frac": 3 * nbytes / (d_s2h3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "copy_same_bytes_gbs": copy1[0], "copy_same_bytes_qkv_gbs": copy3[0],
         "gflop": flops / 1e9,
     }
     log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
-        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}")
+        f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}; same-size copies "
+        f"{res['copy_same_bytes_gbs']:.0f} / {res['copy_same_bytes_qkv_gbs']:.0f}")
     return res
 
 

@@ -296,6 +296,38 @@ cp_status ring_attention_impl(const char* fn, const void* q, const cp_kv_chunk* 
   a.nsplit = 1;
   a.groups = 1;
   if (in_dtype == CP_BF16) {
+    const int ts = cpattn::attn_tail_splits(B, H, Sq, tiles, causal != 0);
+    const int64_t row0 = (Sq - 1) / 128 * 128;  // first row of the last 128-row query tile
+    if (ts > 0 && static_cast<size_t>(cpattn::attn_split_floats(ts, B, H, Sq - row0, D)) *
+                          sizeof(float) <= need) {
+      // the full query tiles, one two-group block each, then the short last
+      // tile's rows with their keys split ts ways; both write into the
+      // caller's O and LSE (B = 1: a row window is a pointer offset)
+      cpattn::AttnArgs m = a, t = a;
+      m.Sq = static_cast<int32_t>(row0);
+      m.lse_stride = static_cast<int32_t>(Sq);
+      m.groups = cpattn::attn_groups(B, H, row0, tiles);
+      t.Sq = static_cast<int32_t>(Sq - row0);
+      t.lse_stride = static_cast<int32_t>(Sq);
+      t.q = static_cast<const char*>(q) + row0 * H * D * es;
+      t.o = static_cast<char*>(o) + row0 * H * D * es;
+      t.lse = lse + row0;
+      t.groups = 1;
+      t.nsplit = ts;
+      if (ts > 1) {
+        t.part_o = static_cast<float*>(workspace);
+        t.part_lse = t.part_o + ts * (Sq - row0) * H * D;
+      }
+      const int64_t q_pos_t = q_pos0 > INT64_MAX - row0 ? INT64_MAX : q_pos0 + row0;
+      for (int64_t c = 0; c < P; ++c) {
+        m.chunks[c].delta = clamp_delta(q_pos0, chunks[c].pos0, row0, chunks[c].len);
+        t.chunks[c].delta = clamp_delta(q_pos_t, chunks[c].pos0, Sq - row0, chunks[c].len);
+      }
+      const hipStream_t st = static_cast<hipStream_t>(stream);
+      const cp_status sm = launch_attention(fn, m, in_dtype, true, causal, st);
+      if (sm != CP_OK) return sm;
+      return launch_attention(fn, t, in_dtype, true, causal, st);
+    }
     a.groups = cpattn::attn_groups(B, H, Sq, tiles);
     a.nsplit = a.groups == 2 ? 1 : cpattn::attn_split_count(B, H, Sq, tiles, causal != 0);
     if (a.nsplit > 1) {

@@ -42,6 +42,7 @@
 //    rounding.
 //  * Non-causal grids map blocks to XCDs so that the tiles of one head stay
 //    on one XCD's L2; causal grids launch the heaviest query tiles first.
+#include <algorithm>
 #include <type_traits>
 
 #include "cp_internal.h"
@@ -60,6 +61,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;      // log2 headroom before the exponent offset is raised
 constexpr int kMaxSplit = 2;      // key splits per query tile on small grids
+constexpr int kTailRows = 32;     // last query tiles at most this short get a launch of their own
+constexpr int kTailSplit = 8;     // key splits of that launch
 
 __device__ __forceinline__ int swap_bits23(int k) {
   return k ^ ((((k >> 2) ^ (k >> 3)) & 1) * 12);
@@ -537,7 +540,10 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
       }
     }
   }
-  if (half == 0) a.lse[lrow] = lse_val;
+  if (half == 0) {
+    const int lstr = a.lse_stride > 0 ? a.lse_stride : a.Sq;
+    a.lse[(static_cast<int64_t>(b) * a.H + h) * lstr + i] = lse_val;
+  }
 }
 
 // ---- Ping-pong kernel for one K/V chunk (a Ulysses rank's local attention,
@@ -836,7 +842,6 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   if (i >= a.Sq) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
-  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
   const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int md = 0; md < D / 32; ++md) {
@@ -858,7 +863,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
       }
     }
   }
-  if (half == 0) a.lse[lrow] = lse_val;
+  if (half == 0) {
+    const int lstr = a.lse_stride > 0 ? a.lse_stride : a.Sq;
+    a.lse[(static_cast<int64_t>(b) * a.H + h) * lstr + i] = lse_val;
+  }
 }
 
 // ---- Two-group ping-pong kernel for small grids (no more query tiles than
@@ -1260,7 +1268,6 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
   if (i >= a.Sq) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
-  const int64_t lrow = (static_cast<int64_t>(b) * a.H + h) * a.Sq + i;
   const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int md = 0; md < D / 32; ++md) {
@@ -1282,7 +1289,10 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
       }
     }
   }
-  if (half == 0) a.lse[lrow] = lse_val;
+  if (half == 0) {
+    const int lstr = a.lse_stride > 0 ? a.lse_stride : a.Sq;
+    a.lse[(static_cast<int64_t>(b) * a.H + h) * lstr + i] = lse_val;
+  }
 }
 
 template <int D, bool CAUSAL, bool OUT_BF16, int G>
@@ -1297,7 +1307,7 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess || nsplit == 1) return e;
   // combine the splits' fp32 partials in split order
   return launch_lse_merge(a.part_o, a.part_lse, static_cast<int>(nsplit), a.o, a.lse, a.B, a.H,
-                          a.Sq, D, OUT_BF16, stream);
+                          a.Sq, D, OUT_BF16, stream, a.lse_stride);
 }
 
 template <int D, bool CAUSAL, bool OUT_BF16>
@@ -1370,6 +1380,20 @@ int attn_split_count(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causa
   int s = 1;
   while (s < kMaxSplit && units * s < slots && tiles / (s + 1) >= 8) ++s;
   return s;
+}
+
+int attn_tail_splits(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal) {
+  // (a causal grid of that size already runs every block in one round: it is
+  // never split, and two launches only add the second one's fixed cost)
+  if (causal || B != 1 || H <= 0) return 0;
+  const int64_t nqt = (Sq + kBM - 1) / kBM;
+  const int64_t tail = Sq - (nqt - 1) * kBM;
+  const int64_t cus = device_cus();
+  if (nqt < 2 || tail > kTailRows || nqt * H <= cus || (nqt - 1) * H > cus || tiles < 4) return 0;
+  // one round of blocks over the CUs; at most kTailSplit partials per row keep
+  // the merge on its path that has every partial's loads in flight at once
+  const int64_t s = std::min<int64_t>(kTailSplit, std::max<int64_t>(1, cus / H));
+  return static_cast<int>(std::min<int64_t>(s, tiles));
 }
 
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D) {

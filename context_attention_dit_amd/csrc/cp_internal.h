@@ -59,9 +59,11 @@ hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc&
                                hipStream_t stream);
 
 // ----- merge (lse_merge.hip)
+// lse_stride: row stride of the output LSE per (batch, head), at least Sq
+// (0 means Sq); the partials' LSE is compact ([P][B][H][Sq]).
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, void* o,
                             float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, bool out_bf16,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t lse_stride = 0);
 
 // ----- attention (attn_bf16.hip, attn_f32.hip)
 struct ChunkDesc {
@@ -88,6 +90,11 @@ struct AttnArgs {
   // bf16 kernel: 1 = four waves per query tile; 2 = eight waves per query tile,
   // its keys split between two groups and merged in LDS (no workspace)
   int32_t groups;
+  // bf16 kernel: row stride of the output LSE per (batch, head); 0 means Sq.
+  // A launch over a window of a longer query shard (B = 1: q and o offset to
+  // the window's first row, lse to its first column) writes its LSE into the
+  // shard's [H][S] array with this stride.
+  int32_t lse_stride;
   ChunkDesc chunks[CP_MAX_RING_CHUNKS];
 };
 
@@ -98,6 +105,12 @@ int attn_split_count(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causa
 // Groups per block (1 or 2) of the bf16 kernel: 2 when there are no more
 // query tiles than CUs and at least 4 key tiles to split.
 int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles);
+// Non-causal single-batch grids just past the CU count whose last query tile
+// is short (at most 32 rows): the full query tiles then fill the CUs once as
+// two-group blocks, and the last tile's rows get a launch of their own with
+// their keys split this many ways (merged after). 0 when the plan does not
+// apply.
+int attn_tail_splits(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal);
 // fp32 elements of partial output the split needs: nsplit*(B*Sq*H*D + B*H*Sq).
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D);
 

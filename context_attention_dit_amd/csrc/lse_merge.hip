@@ -40,7 +40,7 @@ template <bool OUT_BF16, int NC>
 __global__ __launch_bounds__(1024) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int P,
     void* __restrict__ o, float* __restrict__ lse, uint32_t Sq, FastDiv heads, FastDiv tiles,
-    FastDiv cols, int64_t part_stride_o, int64_t part_stride_l) {
+    FastDiv cols, int64_t part_stride_o, int64_t part_stride_l, uint32_t lse_stride) {
   const uint32_t bt = heads.div(blockIdx.x);
   const uint32_t h = blockIdx.x - bt * heads.d;
   const uint32_t b = tiles.div(bt);
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(1024) void lse_merge_kernel(
   const uint32_t seg = cols.d;                    // distance between a thread's columns
   const uint32_t i = t * (blockDim.x / cols.d) + r;
   if (i >= Sq) return;
-  const uint32_t lrow = (b * heads.d + h) * Sq + i;    // LSE index: (b*H + h)*Sq + i
+  const uint32_t lrow = (b * heads.d + h) * Sq + i;    // partial LSE index: (b*H + h)*Sq + i
   const uint32_t row = (b * Sq + i) * heads.d + h;     // O row: (b*Sq + i)*H + h
 
   const f32x4* src = reinterpret_cast<const f32x4*>(o_parts) + static_cast<int64_t>(row) * NC * seg + col;
@@ -120,12 +120,13 @@ __global__ __launch_bounds__(1024) void lse_merge_kernel(
       reinterpret_cast<f32x4*>(o)[off + n * seg] = acc[n];
     }
   }
-  if (col == 0) lse[lrow] = out_lse;
+  if (col == 0) lse[(b * heads.d + h) * lse_stride + i] = out_lse;
 }
 
 template <bool OUT_BF16, int NC>
 void launch_nc(const float* o_parts, const float* lse_parts, int P, void* o, float* lse,
-               int64_t B, int64_t H, int64_t Sq, int64_t D, hipStream_t stream) {
+               int64_t B, int64_t H, int64_t Sq, int64_t D, int64_t lse_stride,
+               hipStream_t stream) {
   const int64_t ncols = D / (4 * NC);         // <= 1024 (D <= 4096)
   const int64_t R = ncols < kThreads ? kThreads / ncols : 1;  // rows per block
   const int64_t T = (Sq + R - 1) / R;
@@ -137,21 +138,23 @@ void launch_nc(const float* o_parts, const float* lse_parts, int P, void* o, flo
   hipLaunchKernelGGL((lse_merge_kernel<OUT_BF16, NC>), dim3(blocks),
                      dim3(static_cast<uint32_t>(ncols * R)), 0, stream, o_parts, lse_parts, P, o,
                      lse, static_cast<uint32_t>(Sq), heads, tiles, cols, B * Sq * H * D,
-                     B * H * Sq);
+                     B * H * Sq, static_cast<uint32_t>(lse_stride));
 }
 
 }  // namespace
 
-// Caller guarantees: P >= 1, D % 4 == 0, D <= 4096, B*Sq*H*(D/4) < 2^31.
+// Caller guarantees: P >= 1, D % 4 == 0, D <= 4096, B*Sq*H*(D/4) < 2^31,
+// Sq <= lse_stride and B*H*lse_stride < 2^32 when lse_stride > 0.
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, void* o,
                             float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, bool out_bf16,
-                            hipStream_t stream) {
+                            hipStream_t stream, int64_t lse_stride) {
+  const int64_t ls = lse_stride > 0 ? lse_stride : Sq;
   if (D % 8 == 0) {
-    if (out_bf16) launch_nc<true, 2>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, stream);
-    else launch_nc<false, 2>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, stream);
+    if (out_bf16) launch_nc<true, 2>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, ls, stream);
+    else launch_nc<false, 2>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, ls, stream);
   } else {
-    if (out_bf16) launch_nc<true, 1>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, stream);
-    else launch_nc<false, 1>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, stream);
+    if (out_bf16) launch_nc<true, 1>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, ls, stream);
+    else launch_nc<false, 1>(o_parts, lse_parts, P, o, lse, B, H, Sq, D, ls, stream);
   }
   return hipGetLastError();
 }

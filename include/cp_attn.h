@@ -125,7 +125,10 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
  * block and no workspace is needed. Between one and two tiles per compute
  * unit, cp_ring_attention splits each tile's keys over two blocks; the
  * splits' fp32 (O, LSE) partials live in the workspace and are merged exactly
- * as cp_lse_merge does. Host function; queries the current device's
+ * as cp_lse_merge does. (A non-causal single-batch call whose last query tile
+ * holds at most 32 rows, when the other tiles fit one per compute unit,
+ * splits only that tile's keys, up to 8 ways, and uses less of the same
+ * workspace.) Host function; queries the current device's
  * compute-unit count; returns 0 for invalid sizes (which cp_ring_attention
  * then rejects).
  */

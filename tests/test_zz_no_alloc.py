@@ -59,7 +59,8 @@ def _compare(q, k, v, chunks, causal=False, q_pos0=0):
 
 def test_noalloc_matches_ring_twice_then_smaller():
     # ring-anything rank 0 (S 4099, H 32, chunks 1025/1025/1025/1024): 288 query
-    # tiles, two key splits
+    # tiles, the last one a single row: the 256 full tiles as two-group blocks,
+    # the last row's keys split 8 ways with their partials in the scratch
     say("noalloc: call 1, Sq 1025 H 32, chunks 1025/1025/1025/1024")
     q, k, v, ch = _case(32, 1025, [1025, 1025, 1025, 1024], 4100)
     need1 = _compare(q, k, v, ch)
@@ -73,6 +74,10 @@ def test_noalloc_matches_ring_twice_then_smaller():
 
 
 def test_noalloc_causal_and_fp32():
+    say("noalloc: causal ring-anything rank 2 shape, Sq 1025 H 32")
+    q, k, v, ch = _case(32, 1025, [1025, 1025, 1025, 1024], 4250)
+    _compare(q, k, v, ch, causal=True, q_pos0=2050)
+    del q, k, v, ch
     say("noalloc: causal ragged ring (no split), Sq 700 H 8")
     q, k, v, ch = _case(8, 700, [300, 500, 211], 4300)
     _compare(q, k, v, ch, causal=True, q_pos0=250)
