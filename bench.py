@@ -373,7 +373,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
-                    help="run only this detail workload (flux, qwen, wan, overlap, ra, merge, "
+                    help="run only this detail workload (flux, qwen, wan, overlap, ra, merge, llmring, "
                          "anything, kvgather, unified, bwd) after the headline; for profiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -419,6 +419,8 @@ def main() -> int:
             q0 = vis = None
         detail.update(other_workloads(torch, cp, synthetic, dev, q0, vis, synthetic.FLUX_RING,
                                       args.only))
+        if args.only in (None, "llmring"):
+            detail["llm-128k-causal-ring8-rank7"] = llm_ring_workload(torch, cp, dev, w, qkv_cpu)
 
     rec = counter_record()
     traffic = None if rec is None else rec.get("bytes_per_launch")
@@ -467,6 +469,36 @@ def main() -> int:
         detail["cpu_oracle_relayout"] = cpu_oracle_relayout()
     print(json.dumps(line), flush=True)
     return 0
+
+
+def llm_ring_workload(torch, cp, dev, w, qkv_cpu):
+    """The headline's 128K causal sequence split as a ring of 8 instead:
+    rank 7 holds query rows [7*16384, 8*16384) over all 32 heads and visits
+    the 8 key chunks in ring order 7, 6, .., 0 (the rank that sees every
+    key; its own chunk is the diagonal), one cp_ring_attention call."""
+    P = w.P
+    S_l = w.S // P
+    q, k, v = qkv_cpu
+    r = P - 1
+    q7 = q[:, r * S_l:(r + 1) * S_l].contiguous().to(dev)
+    kd, vd = k.to(dev), v.to(dev)
+    chunks = [(kd[:, c * S_l:(c + 1) * S_l], vd[:, c * S_l:(c + 1) * S_l], c * S_l)
+              for c in range(r, -1, -1)]
+    chunks = [(a.contiguous(), b.contiguous(), p0) for a, b, p0 in chunks]
+    del kd, vd
+    o = torch.empty_like(q7)
+    lse = torch.empty((1, w.H, S_l), dtype=torch.float32, device=dev)
+    # visible pairs per head: every key of chunks 0..6, the diagonal of chunk 7
+    flops = 4.0 * w.D * w.H * (S_l * S_l * r + causal_pairs_square(S_l))
+    ms = time_back_to_back(torch, lambda: cp.ring_attention(
+        q7, chunks, o, lse, causal=True, q_pos0=r * S_l), 1, 5)
+    res = {"kernel_ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+           "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "gflop": flops / 1e9,
+           "kernel": "attn_pp_kernel chunk-list form (8-wave blocks of 256 query rows)"}
+    log(f"llm-128k-causal-ring8-rank7: {ms:.2f} ms, {res['tflops']:.0f} TFLOP/s")
+    del q7, chunks, o, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 def other_workloads(torch, cp, synthetic, dev, q0, vis, wf, only=None):

@@ -556,7 +556,7 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
 // its softmax while the other keeps the matrix cores busy. A block barrier
 // separates the half-steps. The arithmetic per row is that of
 // attn_bf16_kernel (same products, same order), so results are identical.
-template <int D, bool CAUSAL, bool OUT_BF16>
+template <int D, bool CAUSAL, bool OUT_BF16, bool MULTI>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   constexpr int NW = 8;
   constexpr int KB = 64;
@@ -573,6 +573,12 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char s_v1[TB];
 
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto uni_ptr = [](const char* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w8 = uni(tid >> 6);
@@ -631,7 +637,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
     v_src[n] = 2u * static_cast<uint32_t>(row * rs + v_unit * 8);
   }
 
-  // the chunk: its keys this block can see, and its K/V rows of this (b, h)
+  // One chunk: its keys this block can see, and its K/V rows of this (b, h);
+  // tile j starts j tile strides into them.
   const int len = a.chunks[0].len;
   const int delta = a.chunks[0].delta;
   const int nk = CAUSAL ? max(0, min(len, blk_last + delta + 1)) : len;
@@ -640,9 +647,54 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
                        2 * (static_cast<int64_t>(b) * len * rs + h * D);
   const char* vbase0 = reinterpret_cast<const char*>(a.chunks[0].v) +
                        2 * (static_cast<int64_t>(b) * len * rs + h * D);
-  auto issue = [&](char* dst, int t_abs, bool is_v) {
-    const int n_valid = max(0, min(nk - t_abs * KB, KB));
-    const char* base = (is_v ? vbase0 : kbase0) + t_abs * tile_bytes;
+  auto rows_at = [&](int t_abs) { return max(0, min(nk - t_abs * KB, KB)); };
+  // A chunk list (MULTI): the block's key tiles are every chunk's keys that a
+  // row of the block can see, in chunk order. Each wave walks them with two
+  // cursors, one for the copies (K two tiles ahead; a tile's V source is kept
+  // from its K copy for the V copy one step later) and one for the masking
+  // of its S phases; their fields are wave-uniform, in scalar registers.
+  auto keys_of = [&](int c) {
+    c = uni(c);
+    int nkc = a.chunks[c].len;
+    if (CAUSAL) nkc = max(0, min(nkc, blk_last + a.chunks[c].delta + 1));
+    return nkc;
+  };
+  struct Cur {
+    int c, kt;
+    int nk, len, delta;
+    const char* tk;
+    const char* tv;
+  };
+  auto enter = [&](Cur& x, bool ptrs) {
+    const int c = uni(x.c);
+    if (c < a.nchunks) {
+      x.len = uni(a.chunks[c].len);
+      x.delta = uni(a.chunks[c].delta);
+      x.nk = uni(CAUSAL ? max(0, min(x.len, blk_last + x.delta + 1)) : x.len);
+      if (ptrs) {
+        const int64_t off =
+            2 * ((static_cast<int64_t>(b) * x.len + uni(x.kt) * KB) * rs + h * D);
+        x.tk = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].k) + off);
+        x.tv = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].v) + off);
+      }
+    }
+  };
+  auto next_of = [&](Cur x, bool ptrs) {
+    x.kt = uni(x.kt) + 1;
+    if (x.kt * KB >= x.nk) {
+      x.kt = 0;
+      x.c = uni(x.c) + 1;
+      while (x.c < a.nchunks && keys_of(x.c) == 0) ++x.c;
+      enter(x, ptrs);
+    } else if (ptrs) {
+      x.tk = uni_ptr(x.tk + tile_bytes);
+      x.tv = uni_ptr(x.tv + tile_bytes);
+    }
+    return x;
+  };
+  auto rows_of = [&](const Cur& x) { return uni(max(0, min(x.nk - uni(x.kt) * KB, KB))); };
+  // copy one tile (n_valid rows of it from base, zeros for the rest) into dst
+  auto issue = [&](char* dst, const char* base, int n_valid, bool is_v) {
     char* l = dst + w8 * NL * 1024;
     const __amdgpu_buffer_rsrc_t rsrc =
         tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
@@ -678,7 +730,19 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int n = uni((nk + KB - 1) / KB);  // key tiles of this block
+  int n = 0;  // key tiles of this block
+  Cur ck{0, 0, 0, 0, 0, nullptr, nullptr};  // MULTI: the next K copy
+  if constexpr (MULTI) {
+    for (int cc = 0; cc < a.nchunks; ++cc) n += (keys_of(cc) + KB - 1) / KB;
+    while (ck.c < a.nchunks && keys_of(ck.c) == 0) ++ck.c;
+    enter(ck, true);
+  } else {
+    n = (nk + KB - 1) / KB;
+  }
+  n = uni(n);
+  Cur mc = ck;                 // MULTI: the tile of this wave's next S phase
+  const char* vb_p = nullptr;  // MULTI: V source and rows of the next V copy
+  int vb_n = 0;
 
   // Two phases per tile and wave. S(j): masking and softmax of tile j (VALU
   // only). M(j): O += P(j) V(j) and S(j+1) = K(j+1) Q^T (matrix cores and LDS
@@ -687,12 +751,21 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   f32x16 sacc[NMB];
   bf16x8 pf[NT];
   auto phase_s = [&](int j) {
-    const int key0 = j * KB;
-    const bool masked = (key0 + KB > len) || (CAUSAL && key0 + KB - 1 > q_first + delta);
+    // bounds relative to the tile's first key: rl = len - key0, rd = delta - key0
+    int rl, rd;
+    if constexpr (MULTI) {
+      const int key0 = uni(mc.kt) * KB;
+      rl = uni(mc.len - key0);
+      rd = uni(mc.delta - key0);
+    } else {
+      rl = len - j * KB;
+      rd = delta - j * KB;
+    }
+    const bool masked = (rl < KB) || (CAUSAL && rd < KB - 1 - q_first);
     if (masked) {
       asm volatile("" ::: "memory");
-      int lim = len - key0;
-      if (CAUSAL) lim = min(lim, irow + delta - key0 + 1);
+      int lim = rl;
+      if (CAUSAL) lim = min(lim, irow + rd + 1);
       lim -= 8 * half;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -727,6 +800,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
         pf[t][e] = static_cast<__bf16>(p);
       }
     l_run += psum;
+    if constexpr (MULTI) mc = next_of(mc, false);
   };
   auto phase_m = [&](const char* kl, const char* vl) {
 #pragma unroll
@@ -774,9 +848,22 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 
   // prologue: K(0), K(1), V(0); S(0) for both groups, group 0's softmax of tile 0
   if (n > 0) {
-    issue(s_k0, 0, false);
-    issue(s_v0, 0, true);
-    if (n > 1) issue(s_k1, 1, false);
+    if constexpr (MULTI) {
+      const int nv0 = rows_of(ck);
+      issue(s_k0, ck.tk, nv0, false);
+      issue(s_v0, ck.tv, nv0, true);
+      if (n > 1) {
+        ck = next_of(ck, true);
+        vb_n = rows_of(ck);
+        vb_p = ck.tv;
+        issue(s_k1, ck.tk, vb_n, false);
+        if (n > 2) ck = next_of(ck, true);
+      }
+    } else {
+      issue(s_k0, kbase0, rows_at(0), false);
+      issue(s_v0, vbase0, rows_at(0), true);
+      if (n > 1) issue(s_k1, kbase0 + tile_bytes, rows_at(1), false);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -793,8 +880,27 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
     const int j = hs >> 1;
     bool any = false;
     if (Q % 2 == 0) {
-      if (j + 2 < n) { issue(Q == 0 ? s_k0 : s_k1, j + 2, false); any = true; }
-      if (j + 1 < n) { issue(Q == 0 ? s_v1 : s_v0, j + 1, true); any = true; }
+      if constexpr (MULTI) {
+        const char* vp = vb_p;
+        const int vn = vb_n;
+        if (j + 2 < n) {
+          vb_n = rows_of(ck);
+          vb_p = ck.tv;
+          issue(Q == 0 ? s_k0 : s_k1, ck.tk, vb_n, false);
+          if (j + 3 < n) ck = next_of(ck, true);
+          any = true;
+        }
+        if (j + 1 < n) { issue(Q == 0 ? s_v1 : s_v0, vp, vn, true); any = true; }
+      } else {
+        if (j + 2 < n) {
+          issue(Q == 0 ? s_k0 : s_k1, kbase0 + (j + 2) * tile_bytes, rows_at(j + 2), false);
+          any = true;
+        }
+        if (j + 1 < n) {
+          issue(Q == 0 ? s_v1 : s_v0, vbase0 + (j + 1) * tile_bytes, rows_at(j + 1), true);
+          any = true;
+        }
+      }
     }
     return any;
   };
@@ -1324,14 +1430,23 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  if (a.nchunks == 1 && a.nsplit <= 1) {
-    // one chunk, no key splits: the ping-pong kernel, 256 query rows a block
-    const int64_t nqt = (a.Sq + 255) / 256;
-    const int64_t nitems = nqt * a.B * a.H;
-    const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
-    hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(512), 0, stream, a);
+  // No key splits: the ping-pong kernel, 256 query rows a block, for one
+  // chunk, and for a causal chunk list (D = 128) when its blocks fill the CUs
+  // (measured: a non-causal chunk list, D = 64 or fewer blocks than CUs run
+  // faster on the 4-wave kernel)
+  const int64_t nitems = (a.Sq + 255) / 256 * a.B * a.H;
+  const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
+  if (a.nsplit <= 1 && a.nchunks == 1) {
+    hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false>),
+                       dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, a);
     return hipGetLastError();
+  }
+  if constexpr (CAUSAL && D == 128) {
+    if (a.nsplit <= 1 && a.nchunks > 1 && nitems >= device_cus()) {
+      hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, true>),
+                         dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
   }
   return launch_g<D, CAUSAL, OUT_BF16, 1>(a, stream);
 }

@@ -4,7 +4,10 @@ attn_pp_kernel: one K/V chunk on grids of more query tiles than CUs (8-wave
 blocks over 256 query rows, two groups half a step apart). Shapes put the
 last 256-row block's second group partly or wholly past Sq, make keys
 ragged, empty or shorter than a tile, and cover causal offsets, D = 64, fp32
-outputs, a negative scale and the ring entry point with one chunk.
+outputs, a negative scale and the ring entry point with one chunk. Its
+chunk-list form (causal rings whose 256-row blocks fill the CUs) is checked
+on ragged, empty and reordered chunks, two batches, and blocks that see no
+key.
 
 attn_g2pp_kernel: small grids (no more query tiles than CUs, at least four
 key tiles, D = 128): 8-wave blocks over one 128-row query tile whose two
@@ -157,6 +160,36 @@ def test_two_group_ring(H, Sq, lens, pos, order, causal, q0):
     rows = _rows(Sq)
     ref = [(to_f64(ks[c]), to_f64(vs[c]), pos[c] + np.arange(lens[c])) for c in range(len(lens))]
     wo, wl = oracle.ring_attention(to_f64(q)[:, rows], ref, order, 1 / math.sqrt(D), causal,
+                                   q0 + rows)
+    check_o(o[:, rows], wo, "bf16", "O")
+    check_lse(lse[:, :, rows], wl, "LSE")
+
+
+@pytest.mark.parametrize("B,H,Sq,lens,pos,order,q0", [
+    # 8 blocks of 256 rows x 32 heads: ragged and empty chunks, reversed order,
+    # the diagonal inside the last chunk visited
+    (1, 32, 2048, (700, 0, 1000, 900, 500), (0, 700, 700, 1700, 2600), (4, 3, 2, 1, 0), 1100),
+    # two batches, last 256-row block partly past Sq
+    (2, 16, 1900, (1200, 1300), (0, 1200), (1, 0), 600),
+    # keys placed after the first queries: the first blocks see no key at all
+    (1, 32, 2048, (800, 800), (1000, 1800), (0, 1), 0),
+])
+def test_pingpong_causal_chunk_list(B, H, Sq, lens, pos, order, q0):
+    """The large-grid ping-pong kernel walks a causal chunk list (D = 128,
+    at least as many 256-row blocks as CUs, no key splits)."""
+    D = 128
+    say(f"ping-pong causal chunk list B={B} H={H} Sq={Sq} lens={lens} order={order} q0={q0}")
+    assert B * H * ((Sq + 255) // 256) >= torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * H * ((Sq + 127) // 128) > 256   # no two-group blocks (causal: never split)
+    q = synthetic.make_tensor((B, Sq, H, D), torch.bfloat16, 91 + Sq)
+    ks = [synthetic.make_tensor((B, n, H, D), torch.bfloat16, 92 + 2 * c) for c, n in enumerate(lens)]
+    vs = [synthetic.make_tensor((B, n, H, D), torch.bfloat16, 93 + 2 * c) for c, n in enumerate(lens)]
+    dev = [(ks[c].to(DEV), vs[c].to(DEV), pos[c]) for c in range(len(lens))]
+    o, lse = cp.ring_attention(q.to(DEV), [dev[c] for c in order], causal=True, q_pos0=q0)
+    torch.cuda.synchronize()
+    rows = _rows(Sq)
+    ref = [(to_f64(ks[c]), to_f64(vs[c]), pos[c] + np.arange(lens[c])) for c in range(len(lens))]
+    wo, wl = oracle.ring_attention(to_f64(q)[:, rows], ref, order, 1 / math.sqrt(D), True,
                                    q0 + rows)
     check_o(o[:, rows], wo, "bf16", "O")
     check_lse(lse[:, :, rows], wl, "LSE")
