@@ -596,11 +596,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
     qt = nqt - 1 - L / BH;
     bh = L % BH;
   } else {
-    const int per_xcd = (nitems + 7) / 8;  // one head's tiles stay on one XCD
+    const int nu = a.units > 0 ? a.units : nitems;  // this launch's units
+    const int per_xcd = (nu + 7) / 8;               // one head's tiles stay on one XCD
     const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (L >= nitems) return;
-    bh = L / nqt;
-    qt = L % nqt;
+    if (L >= nu) return;
+    const int u = a.unit0 + L;
+    bh = u / nqt;
+    qt = u % nqt;
   }
   const int b = uni(bh / a.H);
   const int h = uni(bh - b * a.H);
@@ -1024,11 +1026,13 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
     qt = nqt - 1 - L / BH;
     bh = L % BH;
   } else {
-    const int per_xcd = (nitems + 7) / 8;
+    const int nu = a.units > 0 ? a.units : nitems;  // this launch's units
+    const int per_xcd = (nu + 7) / 8;
     const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (L >= nitems) return;
-    bh = L / nqt;
-    qt = L % nqt;
+    if (L >= nu) return;
+    const int u = a.unit0 + L;
+    bh = u / nqt;
+    qt = u % nqt;
   }
   const int b = uni(bh / a.H);
   const int h = uni(bh - b * a.H);
@@ -1437,6 +1441,33 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   const int64_t nitems = (a.Sq + 255) / 256 * a.B * a.H;
   const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
   if (a.nsplit <= 1 && a.nchunks == 1) {
+    if constexpr (!CAUSAL && D == 128) {
+      // Equal blocks over more rounds than one: when the last round would be
+      // at most half full, its rows run instead as 128-row two-group blocks
+      // (half a 256-row block's work each), one round of half the length.
+      const int64_t cus = device_cus();
+      const int64_t rest = nitems % cus;
+      if (nitems > cus && rest > 0 && 2 * rest <= cus) {
+        AttnArgs m = a;
+        m.unit0 = 0;
+        m.units = static_cast<int32_t>(nitems - rest);
+        hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false>),
+                           dim3(static_cast<uint32_t>((m.units + 7) / 8 * 8)), dim3(512), 0,
+                           stream, m);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t nqt256 = (a.Sq + 255) / 256, nqt128 = (a.Sq + kBM - 1) / kBM;
+        const int64_t bh_s = m.units / nqt256, qt_s = m.units % nqt256;
+        AttnArgs t = a;
+        t.groups = 2;
+        t.unit0 = static_cast<int32_t>(bh_s * nqt128 + 2 * qt_s);
+        t.units = static_cast<int32_t>(a.B * a.H * nqt128 - t.unit0);
+        hipLaunchKernelGGL((attn_g2pp_kernel<D, CAUSAL, OUT_BF16>),
+                           dim3(static_cast<uint32_t>((t.units + 7) / 8 * 8)), dim3(512), 0,
+                           stream, t);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false>),
                        dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, a);
     return hipGetLastError();

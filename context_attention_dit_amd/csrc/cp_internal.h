@@ -95,6 +95,10 @@ struct AttnArgs {
   // the window's first row, lse to its first column) writes its LSE into the
   // shard's [H][S] array with this stride.
   int32_t lse_stride;
+  // Non-causal ping-pong kernels: the flat range [unit0, unit0 + units) of
+  // the (batch*head, query tile) units this launch covers, in the kernel's
+  // own query tiling (units = 0: all of them)
+  int32_t unit0, units;
   ChunkDesc chunks[CP_MAX_RING_CHUNKS];
 };
 

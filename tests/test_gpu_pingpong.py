@@ -7,7 +7,9 @@ ragged, empty or shorter than a tile, and cover causal offsets, D = 64, fp32
 outputs, a negative scale and the ring entry point with one chunk. Its
 chunk-list form (causal rings whose 256-row blocks fill the CUs) is checked
 on ragged, empty and reordered chunks, two batches, and blocks that see no
-key.
+key; non-causal grids whose last round of 256-row blocks is at most half
+full (its rows then run as two-group blocks) on split points inside a head,
+a short last block, two batches and fp32 outputs.
 
 attn_g2pp_kernel: small grids (no more query tiles than CUs, at least four
 key tiles, D = 128): 8-wave blocks over one 128-row query tile whose two
@@ -193,3 +195,32 @@ def test_pingpong_causal_chunk_list(B, H, Sq, lens, pos, order, q0):
                                    q0 + rows)
     check_o(o[:, rows], wo, "bf16", "O")
     check_lse(lse[:, :, rows], wl, "LSE")
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,out_dtype", [
+    (1, 80, 1000, 777, torch.bfloat16),    # 320 blocks: the last 64 as two-group blocks
+    (1, 96, 900, 500, torch.bfloat16),     # 384: the last 128 (a half round exactly)
+    (1, 72, 850, 1300, torch.bfloat16),    # 288; last 256-row block of a head has 82 rows
+    (2, 36, 900, 700, torch.float32),      # two batches, fp32 out
+])
+def test_pingpong_last_round_as_two_group_blocks(B, H, Sq, Skv, out_dtype):
+    """Non-causal, one chunk, more 256-row blocks than CUs with a last round at
+    most half full: that round's rows run as 128-row two-group blocks in a
+    second launch (the split point falls inside a head, so one head's rows
+    come from both kernels)."""
+    D = 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = B * H * ((Sq + 255) // 256)
+    assert units > cus and 0 < 2 * (units % cus) <= cus
+    say(f"ping-pong last round as two-group blocks: B={B} H={H} Sq={Sq} Skv={Skv} {out_dtype}")
+    q = synthetic.make_tensor((B, Sq, H, D), torch.bfloat16, 131 + H)
+    k = synthetic.make_tensor((B, Skv, H, D), torch.bfloat16, 132 + H)
+    v = synthetic.make_tensor((B, Skv, H, D), torch.bfloat16, 133 + H)
+    o, lse = cp.attn_chunk_partial(q.to(DEV), k.to(DEV), v.to(DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    # every head at the split point and the last head, sampled rows
+    _check(o, lse, q, k, v, 1 / math.sqrt(D), False, 0, 0, out_dtype)
+    if out_dtype == torch.bfloat16:   # the ring with this one chunk (its own plan)
+        ro, rl = cp.ring_attention(q.to(DEV), [(k.to(DEV), v.to(DEV), 0)])
+        torch.cuda.synchronize()
+        _check(ro, rl, q, k, v, 1 / math.sqrt(D), False, 0, 0, out_dtype)
