@@ -440,7 +440,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": h["achieved"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": h["achieved"] / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "attn_pp_kernel<128, causal=true, out_bf16=true> (8-wave blocks of 256 query rows)",
+                     "kernel": "attn_pp_kernel<128, causal=true, out_bf16=true, chunk list=false> (8-wave blocks of 256 query rows)",
                      "flop_per_launch": h["flops"], "kernel_ms": h["attn_ms"],
                      # clock and MFMA busy of this kernel from the rocprofv3
                      # counter pass on the current source (profiles/), or null
