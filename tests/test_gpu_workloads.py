@@ -1,10 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
 
 Outputs the oracle can afford are compared in full (FLUX ring rank, the
-ring-anything split of 4099 tokens); for the long Ulysses sequences the oracle
-computes a sample of query rows one by one (first rows, last rows and seeded
-random rows of every local head) against the full K/V, with explicit
-positions. Relayouts are compared bit for bit with the oracle's permutation.
+ring-anything split of 4099 tokens); for the long Ulysses sequences, and the
+128K sequence as a ring of 8, the oracle computes a sample of query rows one
+by one (first rows, last rows and seeded random rows of every head) against
+the full K/V, with explicit positions. Relayouts are compared bit for bit with the oracle's permutation.
 """
 import math
 
@@ -123,6 +123,36 @@ def test_ulysses_rank0(wname, n_edge, n_rand):
     got_l = lse[:, :, torch.from_numpy(rows).to(DEV)]
     check_o(got_o, wo, "bf16", "rank 0 O (sampled rows)")
     check_lse(got_l, wl, "rank 0 LSE (sampled rows)")
+
+
+def test_llm_128k_causal_ring8_rank7():
+    """The 128K causal sequence split as a ring of 8 instead: rank 7 (query
+    rows 114688-131071, all 32 heads) over the 8 key chunks in ring order
+    7, 6, ..., 0, one ring call (the chunk-list ping-pong kernel); sampled rows
+    against the oracle over every key up to the row's position."""
+    w = synthetic.LLM_ULYSSES
+    P, D = w.P, w.D
+    S_l = w.S // P
+    say(f"{w.name} as a ring of {P}, rank {P - 1}: generating inputs")
+    q, k, v = synthetic.make_qkv(w)
+    r = P - 1
+    kd, vd = k.to(DEV), v.to(DEV)
+    chunks = [(kd[:, c * S_l:(c + 1) * S_l].contiguous(), vd[:, c * S_l:(c + 1) * S_l].contiguous(),
+               c * S_l) for c in range(r, -1, -1)]
+    del kd, vd
+    say(f"ring rank {r}: attention")
+    o, lse = cp.ring_attention(q[:, r * S_l:(r + 1) * S_l].contiguous().to(DEV), chunks, causal=True,
+                               q_pos0=r * S_l)
+    torch.cuda.synchronize()
+    del chunks
+    rows = _rows(S_l, 8, 24, seed=w.seed + 7)
+    say(f"ring rank {r}: oracle on {len(rows)} rows x {w.H} heads")
+    pos = r * S_l + rows
+    wo, wl = oracle.attention(to_f64(q[:, pos]), to_f64(k), to_f64(v), 1 / math.sqrt(D), True,
+                              q_pos=pos, k_pos=np.arange(w.S))
+    idx = torch.from_numpy(rows).to(DEV)
+    check_o(o[:, idx], wo, "bf16", f"ring rank {r} O (sampled rows)")
+    check_lse(lse[:, :, idx], wl, f"ring rank {r} LSE (sampled rows)")
 
 
 def test_ulysses_anything_flux1008_rank0():
