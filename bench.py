@@ -637,9 +637,15 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
     lse = torch.empty((1, w.H_local, w.S), dtype=torch.float32, device=dev)
     flops = 4.0 * D * w.H_local * (causal_pairs_square(w.S) if w.causal else w.S * w.S)
     reps = 3 if w.causal else 10
-    d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
+    d_cp = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
         rq, rk, rv, o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)]
-    del o, lse
+    # the same attention through the ring call with one chunk and the workspace
+    # it reports (which lets a half-full last round of query tiles split keys)
+    ws = torch.empty(max(1, cp.ring_attention_workspace_bytes(1, 1, w.H_local, w.S, D)),
+                     dtype=torch.uint8, device=dev)
+    d_att = [time_back_to_back(torch, lambda: cp.ring_attention(
+        rq, [(rk, rv, 0)], o, lse, causal=w.causal, workspace=ws), 1, reps)]
+    del o, lse, ws
     # the rank's Q, K and V regrouped together in one launch (stacked tensors)
     qkv3 = torch.stack(qkv)
     heads3 = torch.empty((3,) + tuple(heads[0].shape), dtype=w.dtype, device=dev)
@@ -651,9 +657,12 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
     copy1 = copy_same_bytes(torch, cp, dev, nbytes)
     copy3 = copy_same_bytes(torch, cp, dev, 3 * nbytes)
     res = {
+        "attn_call": "cp_ring_attention, one chunk, with its workspace",
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attn_us_chunk_partial": median(d_cp) * 1e3,
+        "attn_tflops_chunk_partial": flops / (median(d_cp) * 1e-3) / 1e12,
         "seq2head_us": d_s2h * 1e3,
         "seq2head_gbs": nbytes / (d_s2h * 1e-3) / 1e9,
         "head2seq_us": d_h2s * 1e3,
@@ -666,7 +675,8 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
         "copy_same_bytes_gbs": copy1[0], "copy_same_bytes_qkv_gbs": copy3[0],
         "causal": w.causal, "gflop": flops / 1e9,
     }
-    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s (chunk_partial "
+        f"{res['attn_tflops_chunk_partial']:.0f}), seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
         f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}; same-size copies "
         f"{res['copy_same_bytes_gbs']:.0f} / {res['copy_same_bytes_qkv_gbs']:.0f}")
@@ -709,9 +719,12 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
         rq, rk, rv, o, lse, out_dtype=torch.bfloat16), 5, 50)]
     res = {
         "seq_split": s_lens, "head_split": h_counts,
+        "attn_call": "cp_ring_attention, one chunk, with its workspace",
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attn_us_chunk_partial": median(d_cp) * 1e3,
+        "attn_tflops_chunk_partial": flops / (median(d_cp) * 1e-3) / 1e12,
         "seq2head_us": d_s2h * 1e3,
         "seq2head_gbs": nbytes / (d_s2h * 1e-3) / 1e9,
         "head2seq_us": d_h2s * 1e3,
@@ -724,7 +737,8 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
         "copy_same_bytes_gbs": copy1[0], "copy_same_bytes_qkv_gbs": copy3[0],
         "gflop": flops / 1e9,
     }
-    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s (chunk_partial "
+        f"{res['attn_tflops_chunk_partial']:.0f}), seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
         f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}; same-size copies "
         f"{res['copy_same_bytes_gbs']:.0f} / {res['copy_same_bytes_qkv_gbs']:.0f}")

@@ -5,6 +5,7 @@
 // modes fail on sizes they cannot split instead of padding silently:
 // Context parallelism guide (diffusers), variant table and the 1008x1008
 // benchmark rows). No entry point allocates device memory.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -190,26 +191,44 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
                     fn);
 }
 
-size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D) {
+}  // extern "C"
+
+namespace {
+
+bool ring_sizes_ok(int64_t B, int64_t H, int64_t Sq, int64_t D) {
+  return B > 0 && H > 0 && Sq > 0 && (D == 64 || D == 128) && Sq < kMaxSeq &&
+         sat_mul({(Sq + 63) / 64, B, H}) <= kMaxGrid / 8;
+}
+
+// Workspace a cp_ring_attention call cannot do without: the bf16 kernel's
+// key-split partials (the most key splits any chunk list can get for these
+// sizes, i.e. long chunks); the fp32 path never splits, so it needs none.
+size_t ring_workspace_need(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D,
+                           cp_dtype in_dtype) {
   (void)P;
-  if (B <= 0 || H <= 0 || Sq <= 0 || (D != 64 && D != 128) || Sq >= kMaxSeq ||
-      sat_mul({(Sq + 63) / 64, B, H}) > kMaxGrid / 8)
-    return 0;
-  // the most key splits any chunk list can get for these sizes (long chunks)
+  if (in_dtype != CP_BF16 || !ring_sizes_ok(B, H, Sq, D)) return 0;
   const int s = cpattn::attn_split_count(B, H, Sq, int64_t(1) << 40, false);
   return static_cast<size_t>(cpattn::attn_split_floats(s, B, H, Sq, D)) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D) {
+  if (!ring_sizes_ok(B, H, Sq, D)) return 0;
+  const size_t need = ring_workspace_need(P, B, H, Sq, D, CP_BF16);
+  // one chunk: the optional key split of a last round (long chunk, non-causal)
+  const size_t last =
+      P == 1 ? static_cast<size_t>(cpattn::attn_last_split_floats(B, H, Sq, D, int64_t(1) << 40,
+                                                                  false)) * sizeof(float)
+             : 0;
+  return std::max(need, last);
 }
 
 }  // extern "C"
 
 namespace {
-
-// Workspace cp_ring_attention needs for a call: the bf16 kernel's key-split
-// partials; the fp32 path never splits, so it needs none.
-size_t ring_workspace_need(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D,
-                           cp_dtype in_dtype) {
-  return in_dtype == CP_BF16 ? cp_ring_attention_workspace_bytes(P, B, H, Sq, D) : 0;
-}
 
 // Body of cp_ring_attention and cp_ring_attention_noalloc. `scratch_source`
 // (non-null for the no-alloc entry point) yields the device scratch used as
@@ -252,7 +271,24 @@ cp_status ring_attention_impl(const char* fn, const void* q, const cp_kv_chunk* 
   if (!q || !o || !lse) return fail(CP_E_INVALID, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse 4 B)", fn);
-  const int64_t ws_bytes = static_cast<int64_t>(need);
+  // One chunk: when the workspace (the scratch, for the no-alloc entry point)
+  // has room, a non-causal grid whose last round of 256-row blocks would be at
+  // most half full runs that round with its keys split, merged after.
+  int last_split = 0;
+  size_t last_bytes = 0;
+  if (in_dtype == CP_BF16 && P == 1) {
+    const int64_t t1 = (chunks[0].len + 63) / 64;
+    last_split = cpattn::attn_last_splits(B, H, Sq, D, t1, causal != 0);
+    last_bytes = static_cast<size_t>(
+                     cpattn::attn_last_split_floats(B, H, Sq, D, t1, causal != 0)) * sizeof(float);
+    const size_t avail = scratch_source ? static_cast<size_t>(CP_NOALLOC_SCRATCH_BYTES)
+                                        : (workspace ? workspace_bytes : 0);
+    if (last_split < 2 || last_bytes > avail) {
+      last_split = 0;
+      last_bytes = 0;
+    }
+  }
+  const int64_t ws_bytes = static_cast<int64_t>(std::max(need, last_bytes));
   if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
       overlap(lse, l_bytes, q, q_bytes) || overlap(workspace, ws_bytes, q, q_bytes) ||
       overlap(workspace, ws_bytes, o, o_bytes) || overlap(workspace, ws_bytes, lse, l_bytes))
@@ -288,7 +324,7 @@ cp_status ring_attention_impl(const char* fn, const void* q, const cp_kv_chunk* 
     a.chunks[c].delta = clamp_delta(q_pos0, chunks[c].pos0, Sq, chunks[c].len);
     tiles += (chunks[c].len + 63) / 64;
   }
-  if (scratch_source && need > 0) {
+  if (scratch_source && (need > 0 || last_split > 0)) {
     // every argument is valid: only now fetch (and on first use look up) the scratch
     s = scratch_source(fn, &workspace, &workspace_bytes);
     if (s != CP_OK) return s;
@@ -329,10 +365,20 @@ cp_status ring_attention_impl(const char* fn, const void* q, const cp_kv_chunk* 
       return launch_attention(fn, t, in_dtype, true, causal, st);
     }
     a.groups = cpattn::attn_groups(B, H, Sq, tiles);
-    a.nsplit = a.groups == 2 ? 1 : cpattn::attn_split_count(B, H, Sq, tiles, causal != 0);
+    // (one chunk runs on the ping-pong kernel, as cp_attn_chunk_partial does:
+    // measured faster than 4-wave blocks split across blocks, Qwen-Image
+    // rank 239 against 310 us)
+    a.nsplit = (a.groups == 2 || P == 1)
+                   ? 1
+                   : cpattn::attn_split_count(B, H, Sq, tiles, causal != 0);
     if (a.nsplit > 1) {
       a.part_o = static_cast<float*>(workspace);
       a.part_lse = a.part_o + a.nsplit * B * Sq * H * D;
+    } else if (last_split > 1 && a.groups == 1) {
+      const int64_t rest = (Sq + 255) / 256 * B * H % cpattn::device_cus();
+      a.last_split = last_split;
+      a.part_o = static_cast<float*>(workspace);
+      a.part_lse = a.part_o + last_split * rest * 256 * D;
     }
   }
   return launch_attention(fn, a, in_dtype, in_dtype == CP_BF16, causal,

@@ -63,6 +63,7 @@ constexpr float kTau = 8.0f;      // log2 headroom before the exponent offset is
 constexpr int kMaxSplit = 2;      // key splits per query tile on small grids
 constexpr int kTailRows = 32;     // last query tiles at most this short get a launch of their own
 constexpr int kTailSplit = 8;     // key splits of that launch
+constexpr int kLastSplit = 8;     // key splits of a last round's units
 
 __device__ __forceinline__ int swap_bits23(int k) {
   return k ^ ((((k >> 2) ^ (k >> 3)) & 1) * 12);
@@ -556,8 +557,9 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
 // its softmax while the other keeps the matrix cores busy. A block barrier
 // separates the half-steps. The arithmetic per row is that of
 // attn_bf16_kernel (same products, same order), so results are identical.
-template <int D, bool CAUSAL, bool OUT_BF16, bool MULTI>
+template <int D, bool CAUSAL, bool OUT_BF16, bool MULTI, bool SPLIT = false>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
+  static_assert(!SPLIT || (!CAUSAL && !MULTI), "key splits: one chunk, non-causal");
   constexpr int NW = 8;
   constexpr int KB = 64;
   constexpr int NMB = KB / 32;
@@ -591,16 +593,22 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   const int BH = a.B * a.H;
   const int nitems = nqt * BH;
   int bh, qt;
+  // key splits of each unit (one chunk, non-causal): block L takes split
+  // sp = L mod ns of the launch's unit L / ns
+  const int ns = SPLIT ? max(1, a.pp_split) : 1;
+  int nu = nitems, lu = 0, sp = 0;
   if (CAUSAL) {
     const int L = blockIdx.x;  // heaviest (last) query tiles first
     qt = nqt - 1 - L / BH;
     bh = L % BH;
   } else {
-    const int nu = a.units > 0 ? a.units : nitems;  // this launch's units
-    const int per_xcd = (nu + 7) / 8;               // one head's tiles stay on one XCD
+    nu = a.units > 0 ? a.units : nitems;  // this launch's units
+    const int per_xcd = (nu * ns + 7) / 8;  // one head's tiles stay on one XCD
     const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (L >= nu) return;
-    const int u = a.unit0 + L;
+    if (L >= nu * ns) return;
+    lu = L / ns;
+    sp = L - lu * ns;
+    const int u = a.unit0 + lu;
     bh = u / nqt;
     qt = u % nqt;
   }
@@ -641,14 +649,21 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 
   // One chunk: its keys this block can see, and its K/V rows of this (b, h);
   // tile j starts j tile strides into them.
-  const int len = a.chunks[0].len;
+  // (a key split sees the tiles [t0, t1) of the chunk: len counts its keys)
+  const int len_c = a.chunks[0].len;
+  int t0 = 0, len = len_c;
+  if (ns > 1) {
+    const int nt = (len_c + KB - 1) / KB;
+    t0 = nt * sp / ns;
+    len = min(len_c, nt * (sp + 1) / ns * KB) - t0 * KB;
+  }
   const int delta = a.chunks[0].delta;
   const int nk = CAUSAL ? max(0, min(len, blk_last + delta + 1)) : len;
   const int64_t tile_bytes = 2 * static_cast<int64_t>(KB) * rs;
   const char* kbase0 = reinterpret_cast<const char*>(a.chunks[0].k) +
-                       2 * (static_cast<int64_t>(b) * len * rs + h * D);
+                       2 * (static_cast<int64_t>(b) * len_c * rs + h * D) + t0 * tile_bytes;
   const char* vbase0 = reinterpret_cast<const char*>(a.chunks[0].v) +
-                       2 * (static_cast<int64_t>(b) * len * rs + h * D);
+                       2 * (static_cast<int64_t>(b) * len_c * rs + h * D) + t0 * tile_bytes;
   auto rows_at = [&](int t_abs) { return max(0, min(nk - t_abs * KB, KB)); };
   // A chunk list (MULTI): the block's key tiles are every chunk's keys that a
   // row of the block can see, in chunk order. Each wave walks them with two
@@ -951,6 +966,21 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = ((static_cast<int64_t>(b) * a.Sq + i) * a.H + h) * D;
   const float lse_val = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if constexpr (SPLIT) {
+    if (ns > 1) {  // normalised fp32 partial: [split][unit in launch][row in unit]
+      const int64_t prow = (static_cast<int64_t>(sp) * nu + lu) * kTM + (i - blk_first);
+      float* dst = a.part_o + prow * D;
+#pragma unroll
+      for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(dst + 32 * md + 8 * g + 4 * half) =
+              make_float4(oacc[md][4 * g] * inv, oacc[md][4 * g + 1] * inv,
+                          oacc[md][4 * g + 2] * inv, oacc[md][4 * g + 3] * inv);
+      if (half == 0) a.part_lse[prow] = lse_val;
+      return;
+    }
+  }
 #pragma unroll
   for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
@@ -1451,11 +1481,27 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
         AttnArgs m = a;
         m.unit0 = 0;
         m.units = static_cast<int32_t>(nitems - rest);
+        m.pp_split = 1;
         hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false>),
                            dim3(static_cast<uint32_t>((m.units + 7) / 8 * 8)), dim3(512), 0,
                            stream, m);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.last_split > 1 && a.part_o) {
+          // with a workspace: the last round's units as 256-row blocks again,
+          // each unit's keys split last_split ways, and a merge of their rows
+          AttnArgs t = a;
+          t.unit0 = m.units;
+          t.units = static_cast<int32_t>(rest);
+          t.pp_split = a.last_split;
+          hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false, true>),
+                             dim3(static_cast<uint32_t>((rest * a.last_split + 7) / 8 * 8)),
+                             dim3(512), 0, stream, t);
+          e = hipGetLastError();
+          if (e != hipSuccess) return e;
+          return launch_unit_merge(a.part_o, a.part_lse, a.last_split, a.o, a.lse, a.H, a.Sq, D,
+                                   256, t.unit0, rest, OUT_BF16, stream, a.lse_stride);
+        }
         const int64_t nqt256 = (a.Sq + 255) / 256, nqt128 = (a.Sq + kBM - 1) / kBM;
         const int64_t bh_s = m.units / nqt256, qt_s = m.units % nqt256;
         AttnArgs t = a;
@@ -1544,6 +1590,27 @@ int attn_tail_splits(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causa
 
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D) {
   return nsplit <= 1 ? 0 : nsplit * (B * Sq * H * D + B * H * Sq);
+}
+
+// The last round of equal 256-row blocks, at most half full: its units' keys
+// split so that their blocks fill the CUs once (at most kLastSplit ways, at
+// least 4 key tiles a split). The launcher applies it to one-chunk grids.
+int attn_last_splits(int64_t B, int64_t H, int64_t Sq, int64_t D, int64_t tiles, bool causal) {
+  if (causal || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return 0;
+  const int64_t cus = device_cus();
+  const int64_t nitems = (Sq + 255) / 256 * B * H;
+  const int64_t rest = nitems % cus;
+  if (nitems <= cus || rest == 0 || 2 * rest > cus) return 0;
+  const int64_t s = std::min<int64_t>({kLastSplit, cus / rest, tiles / 4});
+  return s >= 2 ? static_cast<int>(s) : 0;
+}
+
+int64_t attn_last_split_floats(int64_t B, int64_t H, int64_t Sq, int64_t D, int64_t tiles,
+                               bool causal) {
+  const int s = attn_last_splits(B, H, Sq, D, tiles, causal);
+  if (s < 2) return 0;
+  const int64_t rest = (Sq + 255) / 256 * B * H % device_cus();
+  return s * rest * 256 * (D + 1);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream) {

@@ -64,6 +64,14 @@ hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc&
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, void* o,
                             float* lse, int64_t B, int64_t H, int64_t Sq, int64_t D, bool out_bf16,
                             hipStream_t stream, int64_t lse_stride = 0);
+// The same merge over the rows of a range of (batch*head, `rows`-row query
+// tile) units [unit0, unit0 + units), ceil(Sq/rows) tiles per head, with the
+// compact partial layout of AttnArgs::pp_split. O is [B][Sq][H][D], LSE
+// [B][H][lse_stride] (0: Sq).
+hipError_t launch_unit_merge(const float* o_parts, const float* lse_parts, int P, void* o,
+                             float* lse, int64_t H, int64_t Sq, int64_t D, int64_t rows,
+                             int64_t unit0, int64_t units, bool out_bf16, hipStream_t stream,
+                             int64_t lse_stride);
 
 // ----- attention (attn_bf16.hip, attn_f32.hip)
 struct ChunkDesc {
@@ -99,6 +107,15 @@ struct AttnArgs {
   // the (batch*head, query tile) units this launch covers, in the kernel's
   // own query tiling (units = 0: all of them)
   int32_t unit0, units;
+  // Non-causal one-chunk ping-pong kernel at D = 128: split each unit's key
+  // tiles over this many blocks (<= 1: none). The splits write normalised fp32
+  // partials in a compact per-unit layout, part_o [split][unit - unit0][256][D]
+  // and part_lse [split][unit - unit0][256], which launch_unit_merge combines.
+  int32_t pp_split;
+  // Ring launches: when the last round of 256-row ping-pong blocks would be
+  // at most half full, split its units' keys this many ways (partials in
+  // part_o / part_lse as above, merged after); <= 1: the two-group plan
+  int32_t last_split;
   ChunkDesc chunks[CP_MAX_RING_CHUNKS];
 };
 
@@ -117,6 +134,12 @@ int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles);
 int attn_tail_splits(int64_t B, int64_t H, int64_t Sq, int64_t tiles, bool causal);
 // fp32 elements of partial output the split needs: nsplit*(B*Sq*H*D + B*H*Sq).
 int64_t attn_split_floats(int64_t nsplit, int64_t B, int64_t H, int64_t Sq, int64_t D);
+// Key splits of the last round's units (see AttnArgs::last_split) for a
+// non-causal one-chunk bf16 call with these sizes; 0 when the plan does not
+// apply. Its partials take attn_last_split_floats(...) fp32 elements.
+int attn_last_splits(int64_t B, int64_t H, int64_t Sq, int64_t D, int64_t tiles, bool causal);
+int64_t attn_last_split_floats(int64_t B, int64_t H, int64_t Sq, int64_t D, int64_t tiles,
+                               bool causal);
 
 // ----- backward (attn_bwd.hip)
 struct BwdChunk {

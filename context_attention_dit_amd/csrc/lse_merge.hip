@@ -141,7 +141,85 @@ void launch_nc(const float* o_parts, const float* lse_parts, int P, void* o, flo
                      B * H * Sq, static_cast<uint32_t>(lse_stride));
 }
 
+// Rows of a unit range (AttnArgs::pp_split partials): block x takes rows
+// R*x .. R*x + R-1 of the flat (unit, row in unit) order, R = blockDim.x /
+// (D/8) rows, D/8 lanes a row with two float4 columns half a row apart each
+// (D % 8 == 0). Same weights, order and output rounding as lse_merge_kernel.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void unit_merge_kernel(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int P,
+    void* __restrict__ o, float* __restrict__ lse, uint32_t H, uint32_t Sq, uint32_t D,
+    uint32_t rows, uint32_t nqt, uint32_t unit0, uint32_t units, uint32_t lse_stride) {
+  const uint32_t cols = D / 8;
+  const uint32_t r_blk = blockDim.x / cols;
+  const uint32_t t = threadIdx.x / cols, col = threadIdx.x - t * (D / 8);
+  const uint32_t flat = blockIdx.x * r_blk + t;  // (unit in range) * rows + row in unit
+  if (flat >= units * rows) return;
+  const uint32_t lu = flat / rows, rr = flat - lu * rows;
+  const uint32_t u = unit0 + lu;
+  const uint32_t bh = u / nqt, qt = u - bh * nqt;
+  const uint32_t i = qt * rows + rr;
+  if (i >= Sq) return;
+  const uint32_t b = bh / H, h = bh - b * H;
+  const uint32_t seg = cols;  // a lane's two columns: col and col + D/8 (float4 units)
+  const int64_t part_rows = static_cast<int64_t>(units) * rows;
+  const f32x4* src = reinterpret_cast<const f32x4*>(o_parts) + static_cast<int64_t>(flat) * (D / 4) + col;
+  const int64_t so = part_rows * (D / 4);
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float out_lse = -INFINITY;
+  float m = -INFINITY;
+  for (int c = 0; c < P; ++c) m = fmaxf(m, lse_parts[c * part_rows + flat]);
+  if (m != -INFINITY) {
+    float z = 0.f;
+    for (int c = 0; c < P; ++c) z += __builtin_amdgcn_exp2f((lse_parts[c * part_rows + flat] - m) * kLog2e);
+    out_lse = m + __builtin_amdgcn_logf(z) * kLn2;
+    for (int c = 0; c < P; ++c) {
+      const float w = __builtin_amdgcn_exp2f((lse_parts[c * part_rows + flat] - out_lse) * kLog2e);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[n] += w * __builtin_nontemporal_load(src + c * so + n * seg);
+    }
+  }
+  const int64_t off = (((static_cast<int64_t>(b) * Sq + i) * H + h) * D) / 4 + col;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    if (OUT_BF16) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = static_cast<__bf16>(acc[n][e]);
+      reinterpret_cast<bf16x4*>(o)[off + n * seg] = r;
+    } else {
+      reinterpret_cast<f32x4*>(o)[off + n * seg] = acc[n];
+    }
+  }
+  if (col == 0) lse[(static_cast<int64_t>(b) * H + h) * lse_stride + i] = out_lse;
+}
+
 }  // namespace
+
+// Caller guarantees: P >= 1, D % 8 == 0, units * rows < 2^32, the unit range
+// lies inside the B*H*ceil(Sq/rows) units, Sq <= lse_stride when lse_stride > 0.
+hipError_t launch_unit_merge(const float* o_parts, const float* lse_parts, int P, void* o,
+                             float* lse, int64_t H, int64_t Sq, int64_t D, int64_t rows,
+                             int64_t unit0, int64_t units, bool out_bf16, hipStream_t stream,
+                             int64_t lse_stride) {
+  const int64_t r_blk = kThreads / (D / 8);
+  const uint32_t blocks = static_cast<uint32_t>((units * rows + r_blk - 1) / r_blk);
+  const uint32_t nqt = static_cast<uint32_t>((Sq + rows - 1) / rows);
+  const uint32_t ls = static_cast<uint32_t>(lse_stride > 0 ? lse_stride : Sq);
+  const uint32_t threads = static_cast<uint32_t>(r_blk * (D / 8));
+  if (out_bf16)
+    hipLaunchKernelGGL((unit_merge_kernel<true>), dim3(blocks), dim3(threads), 0, stream, o_parts,
+                       lse_parts, P, o, lse, static_cast<uint32_t>(H), static_cast<uint32_t>(Sq),
+                       static_cast<uint32_t>(D), static_cast<uint32_t>(rows), nqt,
+                       static_cast<uint32_t>(unit0), static_cast<uint32_t>(units), ls);
+  else
+    hipLaunchKernelGGL((unit_merge_kernel<false>), dim3(blocks), dim3(threads), 0, stream, o_parts,
+                       lse_parts, P, o, lse, static_cast<uint32_t>(H), static_cast<uint32_t>(Sq),
+                       static_cast<uint32_t>(D), static_cast<uint32_t>(rows), nqt,
+                       static_cast<uint32_t>(unit0), static_cast<uint32_t>(units), ls);
+  return hipGetLastError();
+}
 
 // Caller guarantees: P >= 1, D % 4 == 0, D <= 4096, B*Sq*H*(D/4) < 2^31,
 // Sq <= lse_stride and B*H*lse_stride < 2^32 when lse_stride > 0.

@@ -119,18 +119,24 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
                        void* stream);
 
 /*
- * cp_ring_attention_workspace_bytes — device workspace cp_ring_attention needs
- * for these sizes (may be 0). With at most one query tile (128 rows of one
- * batch and head) per compute unit, each tile's keys are split inside its
+ * cp_ring_attention_workspace_bytes — device workspace for a cp_ring_attention
+ * call with these sizes (may be 0). With at most one query tile (128 rows of
+ * one batch and head) per compute unit, each tile's keys are split inside its
  * block and no workspace is needed. Between one and two tiles per compute
  * unit, cp_ring_attention splits each tile's keys over two blocks; the
  * splits' fp32 (O, LSE) partials live in the workspace and are merged exactly
  * as cp_lse_merge does. (A non-causal single-batch call whose last query tile
  * holds at most 32 rows, when the other tiles fit one per compute unit,
  * splits only that tile's keys, up to 8 ways, and uses less of the same
- * workspace.) Host function; queries the current device's
- * compute-unit count; returns 0 for invalid sizes (which cp_ring_attention
- * then rejects).
+ * workspace.) With P == 1 the value also covers an optional plan: when a
+ * non-causal call's 256-row query tiles take more than one round of the
+ * compute units and the last round would be at most half full, that round's
+ * tiles have their keys split (up to 8 ways, at least 4 key tiles a split)
+ * and are merged the same way. A call given less workspace than this value
+ * but at least what the first plans need runs that last round unsplit
+ * instead (same results to rounding). Host function; queries the current
+ * device's compute-unit count; returns 0 for invalid sizes (which
+ * cp_ring_attention then rejects).
  */
 size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D);
 
@@ -152,10 +158,11 @@ size_t cp_ring_attention_workspace_bytes(int64_t P, int64_t B, int64_t H, int64_
  *   o [B][Sq][H][D] in in_dtype; lse [B][H][Sq] fp32.
  *   causal != 0: key j of chunk c is visible to query i iff
  *   chunks[c].pos0 + j <= q_pos0 + i.
- *   workspace: 16-byte aligned device buffer of at least
- *   cp_ring_attention_workspace_bytes(P, B, H, Sq, D) bytes (NULL if 0), owned
- *   by the caller, contents need no initialisation and are scratch afterwards;
- *   concurrent calls must not share one workspace. Too small: CP_E_WORKSPACE.
+ *   workspace: 16-byte aligned device buffer of cp_ring_attention_workspace_bytes(
+ *   P, B, H, Sq, D) bytes (NULL if 0), owned by the caller, contents need no
+ *   initialisation and are scratch afterwards; concurrent calls must not
+ *   share one workspace. Less than the key-split partials need:
+ *   CP_E_WORKSPACE (the optional last-round split above is skipped instead).
  *   CP_F32 inputs never split keys and need no workspace (NULL, 0 accepted).
  *
  * 0 <= P <= CP_MAX_RING_CHUNKS; chunk lengths may differ and may be 0. Same D

@@ -144,6 +144,23 @@ def test_ring_zero_size_is_noop_and_workspace_query():
     assert _ring(H=300, ws_bytes=n - 16) == WORKSPACE
 
 
+def test_workspace_query_one_chunk_last_round():
+    # one chunk: the query also covers the optional key split of a last round
+    # of 256-row tiles that is at most half full. Wan rank (5 heads x 128
+    # tiles = 640 on 256 CUs, 128 in the last round): 2 splits x 128 tiles x
+    # 256 rows x (128 + 1) fp32; with two chunks (or none of that) nothing
+    assert cp.ring_attention_workspace_bytes(1, 1, 5, 32760, 128) == 2 * 128 * 256 * 129 * 4
+    assert cp.ring_attention_workspace_bytes(2, 1, 5, 32760, 128) == 0
+    # 280 tiles (24 in the last round): up to 8 splits
+    assert cp.ring_attention_workspace_bytes(1, 1, 40, 1792, 128) == 8 * 24 * 256 * 129 * 4
+    # exactly 5 rounds (K/V-gather rank), or a last round more than half full
+    # (400 tiles, 144 in the last round): no split
+    assert cp.ring_attention_workspace_bytes(1, 1, 10, 32760, 128) == 0
+    assert cp.ring_attention_workspace_bytes(1, 1, 100, 1024, 128) == 0
+    # D = 64 keeps the two-group last round
+    assert cp.ring_attention_workspace_bytes(1, 1, 5, 32760, 64) == 0
+
+
 def test_ring_fp32_needs_no_workspace():
     # the fp32 path never splits keys: at a size where bf16 needs a workspace, an
     # fp32 call without one passes the workspace check (and here fails on the

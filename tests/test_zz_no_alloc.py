@@ -73,6 +73,16 @@ def test_noalloc_matches_ring_twice_then_smaller():
     assert 0 < need2 < need1
 
 
+def test_noalloc_one_chunk_last_round_split():
+    # one chunk, 280 query tiles of 256 rows: the last round's 24 tiles split
+    # their keys 8 ways, partials in the scratch (ring call: in its workspace)
+    say("noalloc: one chunk, Sq 1792 H 40, 2100 keys (last round split)")
+    q, k, v, ch = _case(40, 1792, [2100], 4300)
+    need = _compare(q, k, v, ch)
+    assert 0 < need <= cp.NOALLOC_SCRATCH_BYTES
+    del q, k, v, ch
+
+
 def test_noalloc_causal_and_fp32():
     say("noalloc: causal ring-anything rank 2 shape, Sq 1025 H 32")
     q, k, v, ch = _case(32, 1025, [1025, 1025, 1025, 1024], 4250)
