@@ -719,12 +719,9 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
         rq, rk, rv, o, lse, out_dtype=torch.bfloat16), 5, 50)]
     res = {
         "seq_split": s_lens, "head_split": h_counts,
-        "attn_call": "cp_ring_attention, one chunk, with its workspace",
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "attn_us_chunk_partial": median(d_cp) * 1e3,
-        "attn_tflops_chunk_partial": flops / (median(d_cp) * 1e-3) / 1e12,
         "seq2head_us": d_s2h * 1e3,
         "seq2head_gbs": nbytes / (d_s2h * 1e-3) / 1e9,
         "head2seq_us": d_h2s * 1e3,
@@ -737,8 +734,7 @@ def ulysses_anything_workload(torch, cp, synthetic, dev):
         "copy_same_bytes_gbs": copy1[0], "copy_same_bytes_qkv_gbs": copy3[0],
         "gflop": flops / 1e9,
     }
-    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s (chunk_partial "
-        f"{res['attn_tflops_chunk_partial']:.0f}), seq2head "
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, seq2head "
         f"{res['seq2head_gbs']:.0f} GB/s, head2seq {res['head2seq_gbs']:.0f}, "
         f"Q+K+V in one launch {res['seq2head_qkv_gbs']:.0f}; same-size copies "
         f"{res['copy_same_bytes_gbs']:.0f} / {res['copy_same_bytes_qkv_gbs']:.0f}")
