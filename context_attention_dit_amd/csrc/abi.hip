@@ -203,10 +203,18 @@ bool ring_sizes_ok(int64_t B, int64_t H, int64_t Sq, int64_t D) {
 // Workspace a cp_ring_attention call cannot do without: the bf16 kernel's
 // key-split partials (the most key splits any chunk list can get for these
 // sizes, i.e. long chunks); the fp32 path never splits, so it needs none.
+// One chunk never splits across blocks (it runs the plan of
+// cp_attn_chunk_partial) except for a short last query tile.
 size_t ring_workspace_need(int64_t P, int64_t B, int64_t H, int64_t Sq, int64_t D,
                            cp_dtype in_dtype) {
-  (void)P;
   if (in_dtype != CP_BF16 || !ring_sizes_ok(B, H, Sq, D)) return 0;
+  if (P == 1) {
+    const int ts = cpattn::attn_tail_splits(B, H, Sq, int64_t(1) << 40, false);
+    const int64_t row0 = (Sq - 1) / 128 * 128;
+    return ts > 0 ? static_cast<size_t>(cpattn::attn_split_floats(ts, B, H, Sq - row0, D)) *
+                        sizeof(float)
+                  : 0;
+  }
   const int s = cpattn::attn_split_count(B, H, Sq, int64_t(1) << 40, false);
   return static_cast<size_t>(cpattn::attn_split_floats(s, B, H, Sq, D)) * sizeof(float);
 }

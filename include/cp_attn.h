@@ -123,9 +123,10 @@ cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, 
  * call with these sizes (may be 0). With at most one query tile (128 rows of
  * one batch and head) per compute unit, each tile's keys are split inside its
  * block and no workspace is needed. Between one and two tiles per compute
- * unit, cp_ring_attention splits each tile's keys over two blocks; the
- * splits' fp32 (O, LSE) partials live in the workspace and are merged exactly
- * as cp_lse_merge does. (A non-causal single-batch call whose last query tile
+ * unit, cp_ring_attention splits each tile's keys over two blocks when P > 1
+ * (one chunk runs as cp_attn_chunk_partial does); the splits' fp32 (O, LSE)
+ * partials live in the workspace and are merged exactly as cp_lse_merge
+ * does. (A non-causal single-batch call whose last query tile
  * holds at most 32 rows, when the other tiles fit one per compute unit,
  * splits only that tile's keys, up to 8 ways, and uses less of the same
  * workspace.) With P == 1 the value also covers an optional plan: when a

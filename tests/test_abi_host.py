@@ -159,6 +159,12 @@ def test_workspace_query_one_chunk_last_round():
     assert cp.ring_attention_workspace_bytes(1, 1, 100, 1024, 128) == 0
     # D = 64 keeps the two-group last round
     assert cp.ring_attention_workspace_bytes(1, 1, 5, 32760, 64) == 0
+    # between one and two 128-row tiles per CU (Qwen-Image rank, 444 tiles): a
+    # chunk list splits keys across blocks, one chunk does not
+    assert cp.ring_attention_workspace_bytes(2, 1, 6, 9472, 128) > 0
+    assert cp.ring_attention_workspace_bytes(1, 1, 6, 9472, 128) == 0
+    # one chunk with a one-row last tile (4099-token ring rank): that row's split
+    assert 0 < cp.ring_attention_workspace_bytes(1, 1, 32, 1025, 128) < 8 * 32 * 129 * 4 + 1
 
 
 def test_ring_fp32_needs_no_workspace():

@@ -97,14 +97,15 @@ def test_noalloc_causal_and_fp32():
 
 
 def test_noalloc_rejects_sizes_beyond_scratch():
-    # one head, 511 query tiles: two splits of 65408 x 128 fp32 partials exceed 64 MiB
+    # one head, 511 query tiles, a list of two chunks: two key splits of
+    # 65408 x 128 fp32 partials exceed 64 MiB (one chunk would not split)
     B, H, D = 1, 1, 128
     Sq = 511 * 128
-    need = cp.ring_attention_workspace_bytes(1, B, H, Sq, D)
+    need = cp.ring_attention_workspace_bytes(2, B, H, Sq, D)
     assert need > cp.NOALLOC_SCRATCH_BYTES
     q = torch.zeros((B, Sq, H, D), dtype=torch.bfloat16, device="cuda")
     kv = torch.zeros((B, 4096, H, D), dtype=torch.bfloat16, device="cuda")
     o, lse = torch.empty_like(q), torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
     with pytest.raises(cp.CpAttnError) as e:
-        cp.ring_attention_noalloc(q, [(kv, kv, 0)], o, lse)
+        cp.ring_attention_noalloc(q, [(kv, kv, 0), (kv, kv, 4096)], o, lse)
     assert e.value.status == 4
