@@ -373,6 +373,23 @@ cp_status ring_attention_impl(const char* fn, const void* q, const cp_kv_chunk* 
       return launch_attention(fn, t, in_dtype, true, causal, st);
     }
     a.groups = cpattn::attn_groups(B, H, Sq, tiles);
+    if (causal && a.groups == 1 && D == 128 && tiles >= 4 &&
+        (Sq + 127) / 128 * B * H <= 2 * static_cast<int64_t>(cpattn::device_cus())) {
+      // A causal grid of one to two query tiles per CU launches its heaviest
+      // tiles first, so the ones past the first round are the lightest. When
+      // the first query tile sees at most 4 key tiles, that second round is
+      // short and two-group blocks (one round of whole-CU tiles, then the
+      // rest) beat two 4-wave blocks per CU (rank 0 of a causal 4099-token
+      // ring, 1025 rows that see only their own chunk: 24.5 against 26.6 us).
+      int64_t first = 0;
+      const int64_t last_row = std::min<int64_t>(Sq, 128) - 1;
+      for (int64_t c = 0; c < P; ++c) {
+        const int64_t vis = std::max<int64_t>(
+            0, std::min<int64_t>(chunks[c].len, last_row + a.chunks[c].delta + 1));
+        first += (vis + 63) / 64;
+      }
+      if (first <= 4) a.groups = 2;
+    }
     // (one chunk runs on the ping-pong kernel, as cp_attn_chunk_partial does:
     // measured faster than 4-wave blocks split across blocks, Qwen-Image
     // rank 239 against 310 us)
