@@ -1556,9 +1556,9 @@ int device_cus() {
 // Blocks of 128 query rows, two resident per CU. A grid of at most one query
 // tile per CU runs two-group blocks: eight waves per tile, its keys split
 // between the groups and merged in LDS. A grid between one and two tiles per
-// CU (ring calls, which have a workspace) is split along the keys across
-// blocks until it covers the GPU, keeping at least 8 tiles per split (the
-// merge pass costs one fp32 read/write per split).
+// CU (ring calls over a chunk list, which have a workspace) is split along
+// the keys across blocks until it covers the GPU, keeping at least 8 tiles
+// per split (the merge pass costs one fp32 read/write per split).
 int attn_groups(int64_t B, int64_t H, int64_t Sq, int64_t tiles) {
   const int64_t units = (Sq + kBM - 1) / kBM * B * H;
   return units <= device_cus() && tiles >= 4 ? 2 : 1;
