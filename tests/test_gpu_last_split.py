@@ -9,6 +9,8 @@ below that size (the last round then runs unsplit), too few key tiles to
 split, a causal call. Every case is checked against the fp64 oracle on
 sampled rows that include rows of the split tiles and of the full rounds,
 and the split and unsplit runs of one shape are compared with each other.
+The Qwen-Image rank (one round of tiles, no split) runs through the same call
+as the benchmark times it, at full size.
 """
 import math
 
@@ -100,19 +102,25 @@ def test_last_round_controls():
     _run(1, 40, 1792, 2100, True, 22, expect_split=False)
 
 
-def test_wan_rank0_ring_one_chunk():
-    """The Wan 21x30x52 Ulysses rank 0 (32760 rows, 5 heads, 640 tiles of
-    which 128 in the last round, 2 key splits) through the ring call with one
-    chunk, sampled rows against the oracle."""
-    w = synthetic.WAN_ULYSSES
+@pytest.mark.parametrize("wname,splits", [
+    ("wan-21x30x52-ulysses8-rank0", 2),       # 640 tiles, 128 in the last round
+    ("qwen-image-1536-ulysses4-rank0", 0),    # 222 tiles: one round, no split
+])
+def test_ulysses_rank0_ring_one_chunk(wname, splits):
+    """A Ulysses rank 0's attention through the ring call with one chunk (the
+    call the benchmark times): Wan 21x30x52 (32760 rows, 5 heads, its last
+    round split 2 ways) and Qwen-Image 1536 (9472 rows, 6 heads, the
+    ping-pong plan of cp_attn_chunk_partial), sampled rows against the
+    oracle."""
+    w = synthetic.WORKLOADS[wname]
     H, D = w.H_local, w.D
     say(f"{w.name}: inputs")
     q, k, v = (x[:, :, :H].contiguous() for x in synthetic.make_qkv(w))  # rank 0's heads
     if _cus() == 256:
-        assert _splits(1, H, w.S, w.S, False) == 2
+        assert _splits(1, H, w.S, w.S, False) == splits
     say(f"{w.name}: ring call with one chunk")
     o, lse = cp.ring_attention(q.to(DEV), [(k.to(DEV), v.to(DEV), 0)])
     torch.cuda.synchronize()
     rows = _rows(w.S, w.seed, n_rand=64, tile_stride=8)
     say(f"{w.name}: oracle on {len(rows)} rows x {H} heads")
-    _check(q, k, v, o, lse, False, rows, "Wan rank 0")
+    _check(q, k, v, o, lse, False, rows, f"{w.name} rank 0")
