@@ -20,7 +20,7 @@
 namespace cpattn {
 namespace {
 
-constexpr int kThreads = 512;           // uneven regrouping
+constexpr int kThreads = 256;           // uneven regrouping: 2 words a work-item
 constexpr int kRelayoutThreads = 512;   // standard regrouping (1% faster than 256 measured)
 
 template <int UNIT>
@@ -112,7 +112,9 @@ hipError_t launch_unit(const void* in, void* out, const RelayoutDesc& d, hipStre
 // launch can move several tensors stored back to back, such as a rank's Q, K
 // and V). The destination group runs fastest in the block order, so the
 // blocks dispatched together copy every group's run of the same source rows
-// (whole rows of the sequence shard). One word per work-item.
+// (whole rows of the sequence shard). A work-item moves two words, half a
+// block apart (256 threads a block: measured 5% faster than one word on each
+// of 512 threads on FLUX 1008 and the Wan K/V gather).
 struct AnyGeometry {
   int32_t P, nq;                  // nq: shards with tokens
   FastDiv np;                     // groups with heads
@@ -146,15 +148,18 @@ __global__ __launch_bounds__(kThreads) void any_relayout_kernel(const void* __re
   const uint64_t group_base =
       (static_cast<uint64_t>(g.B) * g.S * g.h_off[p] +
        (static_cast<uint64_t>(b) * g.S + g.s_off[q]) * hp) * g.wd;
-  const uint32_t u = chunk * kThreads + threadIdx.x;
-  if (u >= n) return;
-  const uint32_t r = g.row[p].div(u), w = u - r * row_words;
-  const uint64_t sh = shard_base + static_cast<uint64_t>(r) * g.H * g.wd + w;
-  const uint64_t gr = group_base + u;
-  if (SEQ2HEAD)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(in + sh), out + gr);
-  else
-    __builtin_nontemporal_store(__builtin_nontemporal_load(in + gr), out + sh);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // words u and u + kThreads of the block's 2*kThreads
+    const uint32_t u = chunk * (2 * kThreads) + k * kThreads + threadIdx.x;
+    if (u >= n) return;
+    const uint32_t r = g.row[p].div(u), w = u - r * row_words;
+    const uint64_t sh = shard_base + static_cast<uint64_t>(r) * g.H * g.wd + w;
+    const uint64_t gr = group_base + u;
+    if (SEQ2HEAD)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(in + sh), out + gr);
+    else
+      __builtin_nontemporal_store(__builtin_nontemporal_load(in + gr), out + sh);
+  }
 }
 
 template <int UNIT>
@@ -186,7 +191,7 @@ hipError_t launch_any_unit(const void* in, void* out, const AnyRelayoutDesc& d,
     max_h = std::max<uint64_t>(max_h, hp);
   }
   const uint64_t max_words = max_s * max_h * g.wd;
-  const uint32_t per_block = kThreads;
+  const uint32_t per_block = 2 * kThreads;
   // (the caller guarantees S > 0 and H > 0, so np, nq >= 1)
   const dim3 grid(static_cast<uint32_t>((max_words + per_block - 1) / per_block * np),
                   static_cast<uint32_t>(nq), static_cast<uint32_t>(g.B * d.count));
