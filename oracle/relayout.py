@@ -12,6 +12,9 @@ ranks' shards:
     seq2head:  out[p][b][q*S_l + s][h][d] = in[q][b][s][p*H_l + h][d]
     head2seq:  out[q][b][s][p*H_l + h][d] = in[p][b][q*S_l + s][h][d]
 
+and, for the value tensor only, a key-contiguous form of seq2head (seq2head_vt:
+each head's values as [D][P*S_l] rows), the operand order of the P.V product.
+
 with P ranks, S_l = S/P tokens per sequence shard (source rank q holds tokens
 [q*S_l, (q+1)*S_l)), and H_l = H/P heads per head group (destination rank p
 gets heads [p*H_l, (p+1)*H_l)). Both are pure copies: values are moved, never
@@ -54,6 +57,32 @@ def seq2head_loop(x: np.ndarray, P: int) -> np.ndarray:
                     for h in range(H_l):
                         for d in range(D):
                             out[p, b, q * S_l + s, h, d] = x[q, b, s, p * H_l + h, d]
+    return out
+
+
+def seq2head_vt(x: np.ndarray, P: int) -> np.ndarray:
+    """``[P][B][S_l][H][D]`` -> ``[P][B][H/P][D][P*S_l]``: the seq2head regrouping of
+    the value tensor, delivered with each (group, batch, head, feature) a row over
+    all P*S_l tokens of the head shard (keys contiguous). Still a pure permutation:
+
+        out[p][b][h][d][q*S_l + s] = in[q][b][s][p*H_l + h][d]
+    """
+    y = seq2head(x, P)                                  # [p][b][t][h][d]
+    return np.ascontiguousarray(np.transpose(y, (0, 1, 3, 4, 2)))
+
+
+def seq2head_vt_loop(x: np.ndarray, P: int) -> np.ndarray:
+    """The key-contiguous regrouping as explicit loops over every index (tiny shapes only)."""
+    _, B, S_l, H, D = x.shape
+    H_l = H // P
+    out = np.empty((P, B, H_l, D, P * S_l), dtype=x.dtype)
+    for p in range(P):
+        for b in range(B):
+            for h in range(H_l):
+                for d in range(D):
+                    for q in range(P):
+                        for s in range(S_l):
+                            out[p, b, h, d, q * S_l + s] = x[q, b, s, p * H_l + h, d]
     return out
 
 

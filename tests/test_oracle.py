@@ -312,6 +312,22 @@ def test_relayout_loops_and_roundtrip(P, S_l, H, D):
         assert np.array_equal(y, x)
 
 
+@pytest.mark.parametrize("P,S_l,H,D", [(1, 3, 2, 4), (2, 3, 4, 2), (4, 2, 8, 3), (3, 5, 6, 1)])
+def test_relayout_vt_loop_and_index_formula(P, S_l, H, D):
+    """Key-contiguous seq2head against its loop form and, element by element, the
+    index formula out[p][b][h][d][q*S_l + s] = in[q][b][s][p*H_l + h][d]."""
+    x = np.arange(P * 2 * S_l * H * D).reshape(P, 2, S_l, H, D)
+    y = oracle.seq2head_vt(x, P)
+    assert y.shape == (P, 2, H // P, D, P * S_l)
+    assert np.array_equal(y, oracle.seq2head_vt_loop(x, P))
+    H_l = H // P
+    for (p, b, h, d, t), val in np.ndenumerate(y):
+        q, s = divmod(t, S_l)
+        assert val == x[q, b, s, p * H_l + h, d]
+    # every value moved exactly once
+    assert sorted(y.ravel().tolist()) == sorted(x.ravel().tolist())
+
+
 def test_relayout_moves_bits_unchanged():
     bits = synthetic.random_bits((4, 1, 6, 8, 16), 2, seed=60).numpy()
     y = oracle.seq2head(bits, 4)
