@@ -13,7 +13,8 @@ ranks' shards:
     head2seq:  out[q][b][s][p*H_l + h][d] = in[p][b][q*S_l + s][h][d]
 
 and, for the value tensor only, a key-contiguous form of seq2head (seq2head_vt:
-each head's values as [D][P*S_l] rows), the operand order of the P.V product.
+each head's values in tiles of 64 tokens, each tile [D][64]), the operand order
+of the P.V product.
 
 with P ranks, S_l = S/P tokens per sequence shard (source rank q holds tokens
 [q*S_l, (q+1)*S_l)), and H_l = H/P heads per head group (destination rank p
@@ -60,29 +61,42 @@ def seq2head_loop(x: np.ndarray, P: int) -> np.ndarray:
     return out
 
 
-def seq2head_vt(x: np.ndarray, P: int) -> np.ndarray:
-    """``[P][B][S_l][H][D]`` -> ``[P][B][H/P][D][P*S_l]``: the seq2head regrouping of
-    the value tensor, delivered with each (group, batch, head, feature) a row over
-    all P*S_l tokens of the head shard (keys contiguous). Still a pure permutation:
+VT_TILE = 64   # keys per tile of the key-contiguous value layout
 
-        out[p][b][h][d][q*S_l + s] = in[q][b][s][p*H_l + h][d]
+
+def seq2head_vt(x: np.ndarray, P: int) -> np.ndarray:
+    """``[P][B][S_l][H][D]`` -> ``[P][B][H/P][ceil(T/64)][D][64]``, T = P*S_l: the
+    seq2head regrouping of the value tensor, delivered in tiles of 64 tokens with
+    each (group, batch, head, tile, feature) a row of the tile's 64 tokens (keys
+    contiguous). Token t = q*S_l + s sits in tile t // 64 at column t % 64;
+    columns past T in the last tile are zero. A permutation plus zero padding:
+
+        out[p][b][h][t // 64][d][t % 64] = in[q][b][s][p*H_l + h][d]
     """
     y = seq2head(x, P)                                  # [p][b][t][h][d]
-    return np.ascontiguousarray(np.transpose(y, (0, 1, 3, 4, 2)))
+    Pp, B, T, H_l, D = y.shape
+    nt = -(-T // VT_TILE)
+    pad = np.zeros((Pp, B, nt * VT_TILE, H_l, D), dtype=y.dtype)
+    pad[:, :, :T] = y
+    t = pad.reshape(Pp, B, nt, VT_TILE, H_l, D)         # [p][b][tile][j][h][d]
+    return np.ascontiguousarray(np.transpose(t, (0, 1, 4, 2, 5, 3)))
 
 
 def seq2head_vt_loop(x: np.ndarray, P: int) -> np.ndarray:
-    """The key-contiguous regrouping as explicit loops over every index (tiny shapes only)."""
+    """The tiled key-contiguous regrouping as explicit loops (tiny shapes only)."""
     _, B, S_l, H, D = x.shape
     H_l = H // P
-    out = np.empty((P, B, H_l, D, P * S_l), dtype=x.dtype)
+    T = P * S_l
+    nt = -(-T // VT_TILE)
+    out = np.zeros((P, B, H_l, nt, D, VT_TILE), dtype=x.dtype)
     for p in range(P):
         for b in range(B):
             for h in range(H_l):
                 for d in range(D):
                     for q in range(P):
                         for s in range(S_l):
-                            out[p, b, h, d, q * S_l + s] = x[q, b, s, p * H_l + h, d]
+                            t = q * S_l + s
+                            out[p, b, h, t // VT_TILE, d, t % VT_TILE] = x[q, b, s, p * H_l + h, d]
     return out
 
 

@@ -312,20 +312,29 @@ def test_relayout_loops_and_roundtrip(P, S_l, H, D):
         assert np.array_equal(y, x)
 
 
-@pytest.mark.parametrize("P,S_l,H,D", [(1, 3, 2, 4), (2, 3, 4, 2), (4, 2, 8, 3), (3, 5, 6, 1)])
+@pytest.mark.parametrize("P,S_l,H,D", [(1, 3, 2, 4), (2, 3, 4, 2), (4, 2, 8, 3), (3, 5, 6, 1),
+                                       (2, 40, 2, 2), (1, 128, 1, 1)])
 def test_relayout_vt_loop_and_index_formula(P, S_l, H, D):
-    """Key-contiguous seq2head against its loop form and, element by element, the
-    index formula out[p][b][h][d][q*S_l + s] = in[q][b][s][p*H_l + h][d]."""
-    x = np.arange(P * 2 * S_l * H * D).reshape(P, 2, S_l, H, D)
+    """Tiled key-contiguous seq2head against its loop form and, element by
+    element, out[p][b][h][t // 64][d][t % 64] = in[q][b][s][p*H_l + h][d] with
+    t = q*S_l + s; the padding columns past T = P*S_l are zero."""
+    x = np.arange(1, P * 2 * S_l * H * D + 1).reshape(P, 2, S_l, H, D)
     y = oracle.seq2head_vt(x, P)
-    assert y.shape == (P, 2, H // P, D, P * S_l)
+    T = P * S_l
+    nt = -(-T // 64)
+    assert y.shape == (P, 2, H // P, nt, D, 64)
     assert np.array_equal(y, oracle.seq2head_vt_loop(x, P))
     H_l = H // P
-    for (p, b, h, d, t), val in np.ndenumerate(y):
-        q, s = divmod(t, S_l)
-        assert val == x[q, b, s, p * H_l + h, d]
-    # every value moved exactly once
-    assert sorted(y.ravel().tolist()) == sorted(x.ravel().tolist())
+    for (p, b, h, tile, d, j), val in np.ndenumerate(y):
+        t = 64 * tile + j
+        if t >= T:
+            assert val == 0
+        else:
+            q, s = divmod(t, S_l)
+            assert val == x[q, b, s, p * H_l + h, d]
+    # every value moved exactly once, the rest is padding
+    nz = y[y != 0]
+    assert sorted(nz.tolist()) == sorted(x.ravel().tolist())
 
 
 def test_relayout_moves_bits_unchanged():
