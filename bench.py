@@ -262,10 +262,14 @@ def copy_same_bytes(torch, cp, dev, nbytes: int):
     return cbytes / (dc * 1e-3) / 1e9, dc * 1e3
 
 
-def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
+def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu, vt: bool = True,
+             warm_ms: float = HEADLINE_WARM_MS):
     """The 128K causal Ulysses rank's step: stacked seq2head of Q, K, V (all 8
     ranks' regrouping), rank 0's causal attention on its 4 heads, head2seq of O
-    (rank 0's output in its slot; the other slots hold stand-in outputs)."""
+    (rank 0's output in its slot; the other slots hold stand-in outputs).
+    vt: Q and K regrouped in one launch and V by cp_ulysses_seq2head_vt (each
+    head's values key-contiguous), attention by cp_attn_chunk_partial_vt;
+    otherwise Q, K, V in one launch and cp_attn_chunk_partial."""
     w = synthetic.LLM_ULYSSES
     P, S_l, H, D, Hl, S = w.P, w.S_local, w.H, w.D, w.H_local, w.S
     log(f"{w.name}: inputs to the GPU")
@@ -274,18 +278,29 @@ def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
     o_all = torch.empty((P, 1, S, Hl, D), dtype=w.dtype, device=dev)
     back = torch.empty((P, 1, S_l, H, D), dtype=w.dtype, device=dev)
     lse = torch.empty((1, Hl, S), dtype=torch.float32, device=dev)
+    vt_all = torch.empty((P, 1, Hl, S // 64, D, 64), dtype=w.dtype, device=dev) if vt else None
     cp.ulysses_seq2head(qkv, P, heads)
     o_all.copy_(heads[2])   # the other ranks' slots: their V head shards as stand-ins
     rq, rk, rv, ro = heads[0, 0], heads[1, 0], heads[2, 0], o_all[0]
+
+    def regroup():
+        if vt:
+            cp.ulysses_seq2head(qkv[:2], P, heads[:2])
+            cp.ulysses_seq2head_vt(qkv[2], P, vt_all)
+        else:
+            cp.ulysses_seq2head(qkv, P, heads)
     flops = 4.0 * D * Hl * causal_pairs_square(S)
     relayout_bytes = 3 * 2 * qkv[0].numel() * qkv.element_size() + \
         2 * o_all.numel() * o_all.element_size()
 
     def attend():
-        cp.attn_chunk_partial(rq, rk, rv, ro, lse, causal=True, out_dtype=w.dtype)
+        if vt:
+            cp.attn_chunk_partial_vt(rq, rk, vt_all[0], ro, lse, causal=True, out_dtype=w.dtype)
+        else:
+            cp.attn_chunk_partial(rq, rk, rv, ro, lse, causal=True, out_dtype=w.dtype)
 
     def step(ev=None):
-        cp.ulysses_seq2head(qkv, P, heads)
+        regroup()
         if ev is not None:
             ev[0].record()
         attend()
@@ -293,10 +308,10 @@ def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
             ev[1].record()
         cp.ulysses_head2seq(o_all, P, back)
 
-    log(f"{w.name}: warmup {warmup} steps, then >= {HEADLINE_WARM_MS:.0f} ms of steps")
+    log(f"{w.name}: warmup {warmup} steps, then >= {warm_ms:.0f} ms of steps")
     for _ in range(warmup):
         step()
-    warm_ms_per_step = warm_up(torch, step, HEADLINE_WARM_MS)
+    warm_ms_per_step = warm_up(torch, step, warm_ms)
     # K steps back to back; an event pair around each attention launch (on the
     # launch stream: torch's current stream, which the binding passes) gives
     # the attention kernel's own duration inside the step
@@ -321,7 +336,7 @@ def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
     log(f"{w.name}: {ms_step:.2f} ms/step ({value:.0f} TFLOP/s), attention kernel "
         f"{attn_ms:.2f} ms ({achieved:.0f} TFLOP/s), regroupings {relayout_ms * 1e3:.0f} us")
     # the regroupings alone, back to back over cold buffer sets, for their GB/s
-    s2h_qkv = time_rotating(torch, [lambda: cp.ulysses_seq2head(qkv, P, heads)], 1, 5)
+    s2h_qkv = time_rotating(torch, [regroup], 1, 5)
     h2s = time_rotating(torch, [lambda: cp.ulysses_head2seq(o_all, P, back)], 1, 5)
     s2h_bytes = 3 * 2 * qkv[0].numel() * qkv.element_size()
     h2s_bytes = 2 * o_all.numel() * o_all.element_size()
@@ -334,7 +349,8 @@ def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu):
         "seq2head_qkv_gbs": s2h_bytes / (s2h_qkv * 1e-3) / 1e9,
         "head2seq_us": h2s * 1e3, "head2seq_gbs": h2s_bytes / (h2s * 1e-3) / 1e9,
     }
-    del qkv, heads, o_all, back, lse, rq, rk, rv, ro
+    res["v_layout"] = "key-contiguous per head" if vt else "token-major"
+    del qkv, heads, o_all, back, lse, rq, rk, rv, ro, vt_all
     torch.cuda.empty_cache()
     return res
 
@@ -423,6 +439,18 @@ def main() -> int:
                                       args.only))
         if args.only in (None, "llmring"):
             detail["llm-128k-causal-ring8-rank7"] = llm_ring_workload(torch, cp, dev, w, qkv_cpu)
+        if args.only in (None, "layout"):
+            # the same step with V token-major (Q, K, V regrouped in one launch,
+            # cp_attn_chunk_partial): what the key-contiguous layout gains
+            hb = headline(torch, cp, synthetic, dev, args.steps, 0, qkv_cpu, vt=False,
+                          warm_ms=WARM_MS * 10)
+            detail["llm-128k-causal-ulysses8-rank0-v-token-major"] = {
+                "step_tflops": hb["value"], "ms_per_step": hb["ms_per_step"],
+                "attn_ms": hb["attn_ms"], "attn_tflops": hb["achieved"],
+                "attn_mfma_frac": hb["achieved"] / PEAK_BF16_TFLOPS,
+                "seq2head_qkv_us": hb["seq2head_qkv_us"], "head2seq_us": hb["head2seq_us"],
+                "kernel": "attn_pp_kernel<128, causal=true, out_bf16=true> with V token-major "
+                          "(transposing LDS reads for P*V)"}
 
     rec = counter_record()
     traffic = None if rec is None else rec.get("bytes_per_launch")
@@ -435,14 +463,18 @@ def main() -> int:
         "data": "synthetic N(0,1) inputs, seed 1005, rounded to bf16",
         "config": {"workload": "128K-token causal LLM, Ulysses SP8 rank 0: S=131072 H=32 "
                                "(4 heads per rank) D=128 bf16, causal from positions; step = "
-                               "seq2head of Q, K, V [8][1][16384][32][128] -> "
-                               "[8][1][131072][4][128] (one launch), rank-0 attention, "
-                               "head2seq of O",
+                               "seq2head of Q and K [8][1][16384][32][128] -> "
+                               "[8][1][131072][4][128] (one launch) and of V into each head's "
+                               "key-contiguous 64-key tiles [8][1][4][2048][128][64] "
+                               "(cp_ulysses_seq2head_vt), "
+                               "rank-0 attention (cp_attn_chunk_partial_vt), head2seq of O",
                    "global_batch": 1, "seq_len": w.S, "parallelism": "one Ulysses rank (P=8)"},
         "roofline": {"bound": "mfma", "achieved": h["achieved"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": h["achieved"] / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "attn_pp_kernel<128, causal=true, out_bf16=true, chunk list=false> (8-wave blocks of 256 query rows)",
+                     "kernel": "attn_pp_kernel<128, causal=true, out_bf16=true, chunk list=false, "
+                               "split=false, key-contiguous V=true> (8-wave blocks of 256 query "
+                               "rows)",
                      "flop_per_launch": h["flops"], "kernel_ms": h["attn_ms"],
                      # clock and MFMA busy of this kernel from the rocprofv3
                      # counter pass on the current source (profiles/), or null
@@ -454,7 +486,8 @@ def main() -> int:
                      "mfma_busy": None if rec is None else rec.get("mfma_busy"),
                      "peak_at_measured_sclk": (PEAK_BF16_TFLOPS * sclk / 2400.0
                                                if sclk else None)},
-        "relayout": {"seq2head_qkv_gbs": h["seq2head_qkv_gbs"],
+        "relayout": {"seq2head_qkv": "Q and K in one launch, V key-contiguous in a second",
+                     "seq2head_qkv_gbs": h["seq2head_qkv_gbs"],
                      "seq2head_qkv_hbm_frac": h["seq2head_qkv_gbs"] / PEAK_HBM_GBS,
                      "head2seq_gbs": h["head2seq_gbs"],
                      "head2seq_hbm_frac": h["head2seq_gbs"] / PEAK_HBM_GBS,

@@ -70,6 +70,9 @@ def _sig(name, args, res=ctypes.c_int):
 
 _chunk_partial = _sig("cp_attn_chunk_partial", [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                                 _i64, _int, _int, _f32, _int, _i64, _i64, _vp])
+_chunk_partial_vt = _sig("cp_attn_chunk_partial_vt",
+                         [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _f32,
+                          _int, _i64, _i64, _vp])
 _lse_merge = _sig("cp_lse_merge", [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp])
 _ring_ws = _sig("cp_ring_attention_workspace_bytes", [_i64] * 5, ctypes.c_size_t)
 _ring = _sig("cp_ring_attention", [_vp, ctypes.POINTER(KVChunk), _i64, _vp, _vp, _i64, _i64, _i64,
@@ -79,6 +82,7 @@ _ring_noalloc = _sig("cp_ring_attention_noalloc",
                       _f32, _int, _i64, _vp])
 _seq2head = _sig("cp_ulysses_seq2head", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _head2seq = _sig("cp_ulysses_head2seq", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
+_seq2head_vt = _sig("cp_ulysses_seq2head_vt", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _seq2head_n = _sig("cp_ulysses_seq2head_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
 _head2seq_n = _sig("cp_ulysses_head2seq_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
 _any_seq2head = _sig("cp_ulysses_anything_seq2head",
@@ -184,6 +188,34 @@ def attn_chunk_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check("cp_attn_chunk_partial", _chunk_partial(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Skv, D, _dtype_code(q.dtype),
+        _dtype_code(o.dtype), scale, int(causal), q_pos0, kv_pos0, _stream(stream)))
+    return o, lse
+
+
+def attn_chunk_partial_vt(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor,
+                          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
+                          scale: Optional[float] = None, causal: bool = False, q_pos0: int = 0,
+                          kv_pos0: int = 0, out_dtype: torch.dtype = torch.float32,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """As attn_chunk_partial with V key-contiguous in 64-key tiles,
+    ``vt [B][H][ceil(Skv/64)][D][64]``; see cp_attn_chunk_partial_vt in include/cp_attn.h."""
+    B, Sq, H, D = _bshd(q, "q")
+    Bk, Skv, Hk, Dk = _bshd(k, "k")
+    if (Bk, Hk, Dk) != (B, H, D):
+        raise ValueError("q, k shapes disagree")
+    if k.dtype != q.dtype or vt.dtype != q.dtype:
+        raise TypeError("q, k, vt must share one dtype")
+    _want(k, "k", k.shape, q.dtype, q.device)
+    _want(vt, "vt", (B, H, (Skv + 63) // 64, D, 64), q.dtype, q.device)
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _want(o, "o", (B, Sq, H, D), o.dtype, q.device)
+    _want(lse, "lse", (B, H, Sq), torch.float32, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check("cp_attn_chunk_partial_vt", _chunk_partial_vt(
+        _ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(lse), B, H, Sq, Skv, D, _dtype_code(q.dtype),
         _dtype_code(o.dtype), scale, int(causal), q_pos0, kv_pos0, _stream(stream)))
     return o, lse
 
@@ -308,6 +340,22 @@ def ulysses_seq2head(x: torch.Tensor, P: int, out: Optional[torch.Tensor] = None
     else:
         _check("cp_ulysses_seq2head", _seq2head(_ptr(x), _ptr(out), P, B, S_l, H, D,
                                                 _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
+def ulysses_seq2head_vt(x: torch.Tensor, P: int, out: Optional[torch.Tensor] = None, *,
+                        stream=None) -> torch.Tensor:
+    """``[P][B][S_l][H][D]`` -> ``[P][B][H/P][ceil(P*S_l/64)][D][64]`` (V delivered
+    key-contiguous per head in 64-token tiles); see cp_ulysses_seq2head_vt."""
+    if x.dim() != 5 or x.shape[0] != P:
+        raise ValueError("x must be [P][B][S_local][H][D]")
+    _, B, S_l, H, D = x.shape
+    shape = (P, B, H // P, (P * S_l + 63) // 64, D, 64)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _want(out, "out", shape, x.dtype, x.device)
+    _check("cp_ulysses_seq2head_vt", _seq2head_vt(_ptr(x), _ptr(out), P, B, S_l, H, D,
+                                                  _dtype_code(x.dtype), _stream(stream)))
     return out
 
 
@@ -523,7 +571,7 @@ def ring_attention_backward(q: torch.Tensor,
     return dq, list(grads)
 
 
-__all__ = ["attn_chunk_partial", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
+__all__ = ["attn_chunk_partial", "attn_chunk_partial_vt", "ulysses_seq2head_vt", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
            "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
            "ulysses_anything_head2seq", "kv_gather", "attn_backward_delta",
            "attn_chunk_backward", "ring_attention_backward", "KVGrad", "BWD_ACCUMULATE_DQ",

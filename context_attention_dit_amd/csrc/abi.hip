@@ -113,11 +113,15 @@ int cp_abi_version(void) { return CP_ATTN_ABI_VERSION; }
 
 const char* cp_last_error(void) { return g_err.c_str(); }
 
-cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                                cp_dtype in_dtype, cp_dtype o_dtype, float scale, int causal,
-                                int64_t q_pos0, int64_t kv_pos0, void* stream) {
-  const char* fn = "cp_attn_chunk_partial";
+}  // extern "C"
+
+namespace {
+
+// One chunk's attention; vt: v is key-contiguous per head, [B][H][D][Skv]
+cp_status chunk_partial(const char* fn, const void* q, const void* k, const void* v, void* o,
+                        float* lse, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                        cp_dtype in_dtype, cp_dtype o_dtype, float scale, int causal,
+                        int64_t q_pos0, int64_t kv_pos0, void* stream, bool vt) {
   cp_status s = check_attn_common(fn, B, H, Sq, D, in_dtype, causal, scale);
   if (s != CP_OK) return s;
   if (Skv < 0) return fail(CP_E_INVALID, "%s: negative Skv", fn);
@@ -125,9 +129,13 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
   if (!valid_dtype(o_dtype)) return fail(CP_E_INVALID, "%s: unknown o_dtype %d", fn, o_dtype);
   if (in_dtype == CP_F32 && o_dtype != CP_F32)
     return fail(CP_E_UNSUPPORTED, "%s: fp32 inputs give fp32 outputs only", fn);
+  if (vt && (in_dtype != CP_BF16 || D != 128))
+    return fail(CP_E_UNSUPPORTED, "%s: key-contiguous V needs bf16 inputs and D = 128", fn);
   if (B == 0 || H == 0 || Sq == 0) return ok();
   const int64_t es = elem_size(in_dtype);
   const int64_t q_bytes = sat_mul({B, Sq, H, D, es}), kv_bytes = sat_mul({B, Skv, H, D, es});
+  // key-contiguous V: [B][H][ceil(Skv/64)][D][64]
+  const int64_t v_bytes = vt ? sat_mul({B, H, (Skv + 63) / 64, D, 64, es}) : kv_bytes;
   const int64_t o_bytes = sat_mul({B, Sq, H, D, elem_size(o_dtype)});
   const int64_t l_bytes = sat_mul({B, H, Sq, 4});
   if (!q || !o || !lse || (Skv > 0 && (!k || !v)))
@@ -136,9 +144,9 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
       !aligned(lse, 4))
     return fail(CP_E_INVALID, "%s: misaligned pointer (tensors need 16 B, lse 4 B)", fn);
   if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
-      overlap(o, o_bytes, v, kv_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
+      overlap(o, o_bytes, v, v_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
       overlap(lse, l_bytes, q, q_bytes) || overlap(lse, l_bytes, k, kv_bytes) ||
-      overlap(lse, l_bytes, v, kv_bytes))
+      overlap(lse, l_bytes, v, v_bytes))
     return fail(CP_E_INVALID, "%s: outputs overlap inputs or each other", fn);
 
   cpattn::AttnArgs a{};
@@ -157,8 +165,29 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
   a.chunks[0].v = v;
   a.chunks[0].len = static_cast<int32_t>(Skv);
   a.chunks[0].delta = clamp_delta(q_pos0, kv_pos0, Sq, Skv);
+  a.vt = vt ? 1 : 0;
   return launch_attention(fn, a, in_dtype, o_dtype == CP_BF16, causal,
                           static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                cp_dtype in_dtype, cp_dtype o_dtype, float scale, int causal,
+                                int64_t q_pos0, int64_t kv_pos0, void* stream) {
+  return chunk_partial("cp_attn_chunk_partial", q, k, v, o, lse, B, H, Sq, Skv, D, in_dtype,
+                       o_dtype, scale, causal, q_pos0, kv_pos0, stream, false);
+}
+
+cp_status cp_attn_chunk_partial_vt(const void* q, const void* k, const void* vt, void* o,
+                                   float* lse, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                   int64_t D, cp_dtype in_dtype, cp_dtype o_dtype, float scale,
+                                   int causal, int64_t q_pos0, int64_t kv_pos0, void* stream) {
+  return chunk_partial("cp_attn_chunk_partial_vt", q, k, vt, o, lse, B, H, Sq, Skv, D, in_dtype,
+                       o_dtype, scale, causal, q_pos0, kv_pos0, stream, true);
 }
 
 cp_status cp_lse_merge(const float* o_parts, const float* lse_parts, int64_t P, void* o,
@@ -508,6 +537,33 @@ cp_status cp_ulysses_seq2head(const void* in, void* out, int64_t P, int64_t B, i
 cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
                               int64_t H, int64_t D, cp_dtype dtype, void* stream) {
   return relayout("cp_ulysses_head2seq", in, out, 1, P, B, S_local, H, D, dtype, stream, false);
+}
+
+cp_status cp_ulysses_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                                 int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  const char* fn = "cp_ulysses_seq2head_vt";
+  if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
+  if (B < 0 || S_local < 0 || H < 0 || D < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
+  if (!valid_dtype(dtype)) return fail(CP_E_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "%s: bf16 only", fn);
+  if (D != 128 && D != 0)
+    return fail(CP_E_UNSUPPORTED, "%s: D=%lld (key-contiguous V needs D = 128)", fn, (long long)D);
+  if (H % P != 0)
+    return fail(CP_E_DIVISIBILITY, "%s: H=%lld heads do not divide by P=%lld", fn, (long long)H,
+                (long long)P);
+  if (B == 0 || S_local == 0 || H == 0 || D == 0) return ok();
+  if (!in || !out) return fail(CP_E_INVALID, "%s: null pointer", fn);
+  if (!aligned(in, 16) || !aligned(out, 16))
+    return fail(CP_E_INVALID, "%s: misaligned pointer (16 B needed)", fn);
+  const int64_t bytes = sat_mul({P, B, S_local, H, D, 2});
+  const int64_t out_bytes = sat_mul({P, B, H / P, (P * S_local + 63) / 64, D, 64, 2});
+  if (overlap(in, bytes, out, out_bytes)) return fail(CP_E_INVALID, "%s: out overlaps in", fn);
+  const int64_t T = sat_mul({P, S_local});
+  if (T >= (int64_t(1) << 31) || sat_mul({B, H, (T + 127) / 128}) >= (int64_t(1) << 31))
+    return fail(CP_E_UNSUPPORTED, "%s: tensor too large for one launch", fn);
+  return hip_status(cpattn::launch_seq2head_vt(in, out, P, B, S_local, H, D,
+                                               static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 cp_status cp_ulysses_seq2head_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,

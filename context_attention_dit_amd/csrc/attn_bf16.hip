@@ -557,8 +557,11 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void attn_bf16_kernel(Attn
 // its softmax while the other keeps the matrix cores busy. A block barrier
 // separates the half-steps. The arithmetic per row is that of
 // attn_bf16_kernel (same products, same order), so results are identical.
-template <int D, bool CAUSAL, bool OUT_BF16, bool MULTI, bool SPLIT = false>
+template <int D, bool CAUSAL, bool OUT_BF16, bool MULTI, bool SPLIT = false, bool VT = false>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
+  // VT: V arrives key-contiguous in 64-key tiles, [B][H][tiles][D][64] (one
+  // chunk, no key splits): each V tile is one contiguous 16 KB block
+  static_assert(!VT || (D == 128 && !MULTI && !SPLIT), "key-contiguous V: one chunk at D = 128");
   static_assert(!SPLIT || (!CAUSAL && !MULTI), "key splits: one chunk, non-causal");
   constexpr int NW = 8;
   constexpr int KB = 64;
@@ -645,6 +648,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
     const int v_unit = pu ^ ((row & 3) << 1);
     k_src[n] = 2u * static_cast<uint32_t>(k_key * rs + k_unit * 8);
     v_src[n] = 2u * static_cast<uint32_t>(row * rs + v_unit * 8);
+    if constexpr (VT) {
+      // V^T tile: D rows of 64 keys (128 bytes, 8 units), unit u of row d at
+      // u ^ ((d >> 1) & 7): the 16 rows of one 16-lane read phase (two rows
+      // per 256-byte bank line) then hit distinct banks
+      const int d = s >> 3, vu = (s & 7) ^ ((d >> 1) & 7);
+      v_src[n] = 128u * d + 16u * vu;
+    }
   }
 
   // One chunk: its keys this block can see, and its K/V rows of this (b, h);
@@ -664,6 +674,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
                        2 * (static_cast<int64_t>(b) * len_c * rs + h * D) + t0 * tile_bytes;
   const char* vbase0 = reinterpret_cast<const char*>(a.chunks[0].v) +
                        2 * (static_cast<int64_t>(b) * len_c * rs + h * D) + t0 * tile_bytes;
+  // VT: this (b, h)'s V tiles, [tiles][D][64]; tile j is the j-th 16 KB block
+  const char* vt_base = reinterpret_cast<const char*>(a.chunks[0].v) +
+                        2 * ((static_cast<int64_t>(b) * a.H + h) * ((len_c + KB - 1) / KB)) * D * KB;
   auto rows_at = [&](int t_abs) { return max(0, min(nk - t_abs * KB, KB)); };
   // A chunk list (MULTI): the block's key tiles are every chunk's keys that a
   // row of the block can see, in chunk order. Each wave walks them with two
@@ -713,8 +726,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   // copy one tile (n_valid rows of it from base, zeros for the rest) into dst
   auto issue = [&](char* dst, const char* base, int n_valid, bool is_v) {
     char* l = dst + w8 * NL * 1024;
+    // (a V^T tile is a whole 16 KB block: its padding keys past the chunk are
+    // finite and get weight 0)
     const __amdgpu_buffer_rsrc_t rsrc =
-        tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
+        VT && is_v ? tile_rsrc(base, 2u * D * KB)
+                   : tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
 #pragma unroll
     for (int n = 0; n < NL; ++n) lds_load16(rsrc, is_v ? v_src[n] : k_src[n], l + n * 1024);
   };
@@ -729,6 +745,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 #pragma unroll
   for (int md = 0; md < D / 32; ++md)
     v_rd[md] = v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+  // VT: the A fragment of k-step t is row d = 32 md + col, keys 16 t + 8 half .. +7
+  uint32_t vt_rd[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) vt_rd[t] = 128u * col + 16u * ((2 * t + half) ^ ((col >> 1) & 7));
 
   auto qk = [&](const char* kl, f32x16* sacc) {
 #pragma unroll
@@ -824,24 +844,38 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
     for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const char* vr = vl + v_rd[md] + 16 * t * RB;
-        const bf16x4 lo = read_tr(vr);
-        const bf16x4 hi = read_tr(vr + 4 * RB);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 vf;
+        if constexpr (VT) {
+          vf = *reinterpret_cast<const bf16x8*>(vl + vt_rd[t] + md * 32 * 128);
+        } else {
+          const char* vr = vl + v_rd[md] + 16 * t * RB;
+          const bf16x4 lo = read_tr(vr);
+          const bf16x4 hi = read_tr(vr + 4 * RB);
+          vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
       }
     }
     qk(kl, sacc);
     // one MFMA per group with its fragment reads two groups ahead
     constexpr int NVF = NT * (D / 32), NKF = NMB * (D / 16);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if constexpr (VT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int k = 0; k < NVF; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (k < NVF - 2)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else
+      for (int k = 0; k < NVF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < NVF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k < NVF - 2)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
 #pragma unroll
     for (int k = 0; k < NKF; ++k) {
@@ -878,7 +912,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
       }
     } else {
       issue(s_k0, kbase0, rows_at(0), false);
-      issue(s_v0, vbase0, rows_at(0), true);
+      issue(s_v0, VT ? vt_base : vbase0, rows_at(0), true);
       if (n > 1) issue(s_k1, kbase0 + tile_bytes, rows_at(1), false);
     }
   }
@@ -914,7 +948,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
           any = true;
         }
         if (j + 1 < n) {
-          issue(Q == 0 ? s_v1 : s_v0, vbase0 + (j + 1) * tile_bytes, rows_at(j + 1), true);
+          issue(Q == 0 ? s_v1 : s_v0,
+                VT ? vt_base + 2 * D * KB * (j + 1) : vbase0 + (j + 1) * tile_bytes, rows_at(j + 1),
+                true);
           any = true;
         }
       }
@@ -1017,8 +1053,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 // opposite phases. Same products in the same order as the two-group case of
 // attn_bf16_kernel, so the results are identical. (At head dim 64 the
 // softmax outweighs the matrix work and that kernel is faster.)
-template <int D, bool CAUSAL, bool OUT_BF16>
+template <int D, bool CAUSAL, bool OUT_BF16, bool VT = false>
 __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
+  // VT: V arrives key-contiguous in 64-key tiles, [B][H][tiles][D][64] (one
+  // chunk): each V tile is one contiguous 16 KB block
+  static_assert(!VT || D == 128, "key-contiguous V: D = 128");
   constexpr int WPG = 4;
   constexpr int TPG = WPG * 64;
   constexpr int KB = 64;
@@ -1096,6 +1135,10 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
     const int v_unit = pu ^ ((row & 3) << 1);
     k_src[n] = 2u * static_cast<uint32_t>(k_key * rs + k_unit * 8);
     v_src[n] = 2u * static_cast<uint32_t>(row * rs + v_unit * 8);
+    if constexpr (VT) {  // V^T tile: D rows of 8 16-byte units, unit u of row d at u ^ ((d >> 1) & 7)
+      const int d = s >> 3, vu = (s & 7) ^ ((d >> 1) & 7);
+      v_src[n] = 128u * d + 16u * vu;
+    }
   }
 
   auto keys_of = [&](int c) {
@@ -1121,6 +1164,10 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
           2 * ((static_cast<int64_t>(b) * x.len + uni(x.kt) * KB) * rs + h * D);
       x.tk = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].k) + off);
       x.tv = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].v) + off);
+      if constexpr (VT)
+        x.tv = uni_ptr(reinterpret_cast<const char*>(a.chunks[c].v) +
+                       2 * ((static_cast<int64_t>(b) * a.H + h) * ((x.len + KB - 1) / KB) +
+                            uni(x.kt)) * D * KB);
     }
   };
   auto next_of = [&](Cur x) {
@@ -1132,15 +1179,18 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
       enter(x);
     } else {
       x.tk = uni_ptr(x.tk + tile_bytes);
-      x.tv = uni_ptr(x.tv + tile_bytes);
+      x.tv = uni_ptr(x.tv + (VT ? 2 * D * KB : tile_bytes));
     }
     return x;
   };
   // copy one tile (n_valid rows of it from base, zeros for the rest) into dst
+  // (a V^T tile is a whole 16 KB block: its padding keys past the chunk are
+  // finite and get weight 0)
   auto issue = [&](char* dst, const char* base, int n_valid, bool is_v) {
     char* l = dst + gbase + wave * NL * 1024;
     const __amdgpu_buffer_rsrc_t rsrc =
-        tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
+        VT && is_v ? tile_rsrc(base, 2u * D * KB)
+                   : tile_rsrc(base, static_cast<uint32_t>(n_valid) * static_cast<uint32_t>(2 * rs));
 #pragma unroll
     for (int n = 0; n < NL; ++n) lds_load16(rsrc, is_v ? v_src[n] : k_src[n], l + n * 1024);
   };
@@ -1155,6 +1205,10 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
 #pragma unroll
   for (int md = 0; md < D / 32; ++md)
     v_rd[md] = gbase + v_unit_off<D>(v_row, (32 * md + v_el) >> 3) + ((v_el & 4) ? 8 : 0);
+  // VT: the A fragment of k-step t is row d = 32 md + col, keys 16 t + 8 half .. +7
+  uint32_t vt_rd[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) vt_rd[t] = gbase + 128u * col + 16u * ((2 * t + half) ^ ((col >> 1) & 7));
 
   auto qk = [&](const char* kl, f32x16* sacc) {
 #pragma unroll
@@ -1275,23 +1329,37 @@ __global__ __launch_bounds__(512, 1) void attn_g2pp_kernel(AttnArgs a) {
     for (int md = 0; md < D / 32; ++md) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const char* vr = vl + v_rd[md] + 16 * t * RB;
-        const bf16x4 lo = read_tr(vr);
-        const bf16x4 hi = read_tr(vr + 4 * RB);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 vf;
+        if constexpr (VT) {
+          vf = *reinterpret_cast<const bf16x8*>(vl + vt_rd[t] + md * 32 * 128);
+        } else {
+          const char* vr = vl + v_rd[md] + 16 * t * RB;
+          const bf16x4 lo = read_tr(vr);
+          const bf16x4 hi = read_tr(vr + 4 * RB);
+          vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[md], 0, 0, 0);
       }
     }
     qk(kl, sacc);
     constexpr int NVF = NT * (D / 32), NKF = NMB * (D / 16);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if constexpr (VT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int k = 0; k < NVF; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (k < NVF - 2)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else
+      for (int k = 0; k < NVF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < NVF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k < NVF - 2)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
 #pragma unroll
     for (int k = 0; k < NKF; ++k) {
@@ -1450,16 +1518,16 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
                           a.Sq, D, OUT_BF16, stream, a.lse_stride);
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
+template <int D, bool CAUSAL, bool OUT_BF16, bool VT = false>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   if (a.groups == 2) {
-    if constexpr (D == 64) {
+    if constexpr (D == 64 && !VT) {
       return launch_g<D, CAUSAL, OUT_BF16, 2>(a, stream);
     } else {
       // one 128-row query tile a block, its keys split between two groups
       const int64_t nitems = (a.Sq + kBM - 1) / kBM * a.B * a.H;
       const int64_t blocks = CAUSAL ? nitems : (nitems + 7) / 8 * 8;
-      hipLaunchKernelGGL((attn_g2pp_kernel<D, CAUSAL, OUT_BF16>),
+      hipLaunchKernelGGL((attn_g2pp_kernel<D, CAUSAL, OUT_BF16, VT>),
                          dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, a);
       return hipGetLastError();
     }
@@ -1482,12 +1550,12 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
         m.unit0 = 0;
         m.units = static_cast<int32_t>(nitems - rest);
         m.pp_split = 1;
-        hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false>),
+        hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false, false, VT>),
                            dim3(static_cast<uint32_t>((m.units + 7) / 8 * 8)), dim3(512), 0,
                            stream, m);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (a.last_split > 1 && a.part_o) {
+        if (!VT && a.last_split > 1 && a.part_o) {
           // with a workspace: the last round's units as 256-row blocks again,
           // each unit's keys split last_split ways, and a merge of their rows
           AttnArgs t = a;
@@ -1508,16 +1576,19 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
         t.groups = 2;
         t.unit0 = static_cast<int32_t>(bh_s * nqt128 + 2 * qt_s);
         t.units = static_cast<int32_t>(a.B * a.H * nqt128 - t.unit0);
-        hipLaunchKernelGGL((attn_g2pp_kernel<D, CAUSAL, OUT_BF16>),
+        hipLaunchKernelGGL((attn_g2pp_kernel<D, CAUSAL, OUT_BF16, VT>),
                            dim3(static_cast<uint32_t>((t.units + 7) / 8 * 8)), dim3(512), 0,
                            stream, t);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false>),
+    hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, false, false, VT>),
                        dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
+  if constexpr (VT) {
+    return hipErrorInvalidValue;  // key-contiguous V: one chunk, no key splits (checked by the caller)
+  } else {
   if constexpr (CAUSAL && D == 128) {
     if (a.nsplit <= 1 && a.nchunks > 1 && nitems >= device_cus()) {
       hipLaunchKernelGGL((attn_pp_kernel<D, CAUSAL, OUT_BF16, true>),
@@ -1526,6 +1597,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     }
   }
   return launch_g<D, CAUSAL, OUT_BF16, 1>(a, stream);
+  }
 }
 
 
@@ -1614,6 +1686,13 @@ int64_t attn_last_split_floats(int64_t B, int64_t H, int64_t Sq, int64_t D, int6
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool causal, bool out_bf16, hipStream_t stream) {
+  if (a.vt) {  // key-contiguous V (D = 128, one chunk, no key splits: checked by the caller)
+    if (causal)
+      return out_bf16 ? launch_t<128, true, true, true>(a, stream)
+                      : launch_t<128, true, false, true>(a, stream);
+    return out_bf16 ? launch_t<128, false, true, true>(a, stream)
+                    : launch_t<128, false, false, true>(a, stream);
+  }
   return a.D == 64 ? launch_d<64>(a, causal, out_bf16, stream)
                    : launch_d<128>(a, causal, out_bf16, stream);
 }

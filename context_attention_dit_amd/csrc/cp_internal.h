@@ -41,6 +41,10 @@ struct RelayoutDesc {
 };
 int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d);
 hipError_t launch_relayout(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream);
+// seq2head of a bf16 value tensor into [P][B][H/P][ceil(P*S_local/64)][D][64]
+// (keys contiguous in 64-key tiles, zero padding past P*S_local)
+hipError_t launch_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                              int64_t H, int64_t D, hipStream_t stream);
 
 // Ulysses Anything: uneven per-rank token counts and head counts. The P
 // sequence shards (shard q = [B][S_q][H][D]) and the P head groups (group p
@@ -116,6 +120,10 @@ struct AttnArgs {
   // at most half full, split its units' keys this many ways (partials in
   // part_o / part_lse as above, merged after); <= 1: the two-group plan
   int32_t last_split;
+  // bf16 kernel: 1 = chunk 0's v is key-contiguous in 64-key tiles,
+  // [B][H][ceil(len/64)][D][64] (one chunk, D = 128, no key splits);
+  // 0 = [B][len][H][D] like k
+  int32_t vt;
   ChunkDesc chunks[CP_MAX_RING_CHUNKS];
 };
 

@@ -227,6 +227,106 @@ hipError_t launch_any_relayout(const void* in, void* out, const AnyRelayoutDesc&
   }
 }
 
+// ---------------------------------------------------------------- key-contiguous V
+// seq2head of the value tensor into out[p][b][h][t / 64][d][t % 64], t = q*S_l
+// + s over the head shard's T = P*S_l tokens: per (group, batch, head) a
+// transpose of (token, feature) in tiles of 64 tokens, each tile one
+// contiguous 16 KB block, so that attention copies a tile of V in the order the
+// P*V product reads it. Columns past T in the last tile are written as zeros.
+// A block of 256 threads takes 128 tokens (two tiles) x 128 features of one
+// (p, b, h) through LDS: 16 lanes read one token's 256-byte row (8 16-byte
+// units a thread), and each thread forms two features' 8-token units from 8
+// 4-byte LDS reads and byte permutes; a block writes its two tiles whole. LDS rows hold 64 words; word w of token r sits at
+// w ^ (4 (r / 8 mod 16)), so the 16 rows r, r + 8, ... that one read phase
+// touches fall in distinct banks, and a row's 16-byte units stay whole.
+// Blocks walk the tokens fastest: neighbouring blocks read neighbouring rows
+// and extend the same output rows.
+struct VtGeometry {
+  uint32_t T;         // tokens per head shard (P * S_l)
+  FastDiv seq;        // S_l
+  uint32_t B, H, H_l;
+  uint32_t tiles;     // ceil(T / 64): 64-token tiles per (p, b, h)
+  uint32_t tblocks;   // ceil(T / 128)
+  uint32_t blocks;    // P * B * H_l * tblocks
+};
+
+__global__ __launch_bounds__(256) void seq2head_vt_kernel(const uint16_t* __restrict__ in,
+                                                          uint16_t* __restrict__ out,
+                                                          VtGeometry g) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];
+  const uint32_t blk = blockIdx.x;
+  uint32_t r = blk;
+  const uint32_t tb = r % g.tblocks;
+  r /= g.tblocks;
+  const uint32_t h = r % g.H_l;
+  r /= g.H_l;
+  const uint32_t b = r % g.B;
+  const uint32_t p = r / g.B;
+  const uint32_t t_base = tb * 128;
+  const uint64_t head_col = static_cast<uint64_t>(p) * g.H_l + h;
+  const int tid = threadIdx.x;
+  // load: unit k = tid + 256 i is token k / 16, feature unit k % 16
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = tid + 256 * i;
+    const int tok = k >> 4, fu = k & 15;
+    const uint32_t t = t_base + tok;
+    u32x4 x = u32x4{0, 0, 0, 0};
+    if (t < g.T) {
+      const uint32_t q = g.seq.div(t);
+      const uint32_t s = t - q * g.seq.d;
+      const uint64_t row = (static_cast<uint64_t>(q) * g.B + b) * g.seq.d + s;
+      x = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(in + (row * g.H + head_col) * D + 8 * fu));
+    }
+    *reinterpret_cast<u32x4*>(&tile[tok * 64 + ((4 * fu) ^ (4 * ((tok >> 3) & 15)))]) = x;
+  }
+  __syncthreads();
+  // store: work-item k = tid + 256 i is feature pair k / 16, token unit k % 16
+  uint16_t* obase = out + ((static_cast<uint64_t>(p) * g.B + b) * g.H_l + h) * g.tiles * D * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = tid + 256 * i;
+    const int fp = k >> 4, tu = k & 15;
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = tile[(8 * tu + j) * 64 + (fp ^ (4 * tu))];
+    const uint32_t t0 = t_base + 8 * tu;
+    const uint32_t tile = t0 >> 6;
+    if (tile >= g.tiles) continue;   // the block's second tile lies past T
+    uint16_t* tbase = obase + static_cast<uint64_t>(tile) * D * 64 + (t0 & 63);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {   // feature 2 fp + e: the low (e = 0) or high halves
+      const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+      u32x4 y;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) y[m] = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], sel);
+      __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(tbase + (2 * fp + e) * 64));
+    }
+  }
+}
+
+// The caller has checked: 2-byte elements, D = 128, 16-byte aligned pointers,
+// fewer than 2^31 tokens and blocks.
+hipError_t launch_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                              int64_t H, int64_t D, hipStream_t stream) {
+  (void)D;
+  VtGeometry g;
+  g.T = static_cast<uint32_t>(P * S_local);
+  g.seq.init(static_cast<uint32_t>(S_local));
+  g.B = static_cast<uint32_t>(B);
+  g.H = static_cast<uint32_t>(H);
+  g.H_l = static_cast<uint32_t>(H / P);
+  g.tiles = (g.T + 63) / 64;
+  g.tblocks = (g.T + 127) / 128;
+  g.blocks = static_cast<uint32_t>(P * B * (H / P) * g.tblocks);
+  hipLaunchKernelGGL(seq2head_vt_kernel, dim3(g.blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), g);
+  return hipGetLastError();
+}
+
 // Widest word that divides the run length and both base addresses.
 int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d) {
   const int64_t run_bytes = (d.H / d.P) * d.D * d.elem_bytes;

@@ -100,6 +100,33 @@ cp_status cp_attn_chunk_partial(const void* q, const void* k, const void* v, voi
                                 int64_t q_pos0, int64_t kv_pos0, void* stream);
 
 /*
+ * cp_attn_chunk_partial_vt — cp_attn_chunk_partial with V given key-contiguous
+ * per head, in tiles of 64 keys: vt [B][H][ceil(Skv/64)][D][64],
+ * vt[b][h][j / 64][d][j % 64] = v[b][j][h][d]. Each tile is one contiguous
+ * 16 KB block; its columns past Skv (the last tile's padding) must hold
+ * finite values (they get weight 0; cp_ulysses_seq2head_vt writes zeros).
+ *
+ * Defined by: as cp_attn_chunk_partial (the local attention of a Ulysses rank,
+ * Ulysses Sequence Parallelism article, detailed notes 4; Context parallelism
+ * guide (diffusers), section Ulysses Attention). Only the storage order of V
+ * differs: it is the order in which the P*V product consumes V, and
+ * cp_ulysses_seq2head_vt produces it for each destination rank, so the rank's
+ * attention reads V with full-width LDS reads instead of transposing ones.
+ * q, k, o, lse, the causal rule, the arithmetic and the order of every sum
+ * are those of cp_attn_chunk_partial: O and LSE equal its results on the same
+ * values bit for bit.
+ *
+ * Supported: in_dtype CP_BF16, D = 128, o_dtype CP_F32 or CP_BF16 (anything
+ * else is CP_E_UNSUPPORTED); other limits as cp_attn_chunk_partial. vt
+ * 16-byte aligned (else CP_E_INVALID). Skv == 0 is allowed (O = 0,
+ * LSE = -inf; vt may be NULL).
+ */
+cp_status cp_attn_chunk_partial_vt(const void* q, const void* k, const void* vt, void* o,
+                                   float* lse, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                   int64_t D, cp_dtype in_dtype, cp_dtype o_dtype, float scale,
+                                   int causal, int64_t q_pos0, int64_t kv_pos0, void* stream);
+
+/*
  * cp_lse_merge — merge P partial (O_c, LSE_c) pairs into attention over all their keys.
  *
  * Defined by: the diffusers parallel API, ContextParallelConfig
@@ -236,6 +263,27 @@ cp_status cp_ulysses_seq2head(const void* in, void* out, int64_t P, int64_t B, i
  */
 cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
                               int64_t H, int64_t D, cp_dtype dtype, void* stream);
+
+/*
+ * cp_ulysses_seq2head_vt — cp_ulysses_seq2head for the value tensor, with each
+ * destination rank's head shard stored key-contiguous: the V layout
+ * cp_attn_chunk_partial_vt reads.
+ *
+ * Defined by: as cp_ulysses_seq2head (Context parallelism guide (diffusers),
+ * section Ulysses Attention): the same regrouping, the head shard written in
+ * tiles of 64 tokens, each tile feature-major; a bit permutation plus zero
+ * padding. With t = q*S_local + s and T = P*S_local:
+ *   out[p][b][h][t / 64][d][t % 64] = in[q][b][s][p*(H/P) + h][d]
+ *   and out[p][b][h][T / 64][d][c] = 0 for the last tile's columns c >= T % 64.
+ *
+ *   in  [P][B][S_local][H][D] (as cp_ulysses_seq2head)
+ *   out [P][B][H/P][ceil(T/64)][D][64] (rank p's V is out[p])
+ * dtype CP_BF16 only and D = 128 (else CP_E_UNSUPPORTED); in and
+ * out 16-byte aligned (else CP_E_INVALID); H % P != 0 is CP_E_DIVISIBILITY.
+ * P*S_local < 2^31.
+ */
+cp_status cp_ulysses_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                                 int64_t H, int64_t D, cp_dtype dtype, void* stream);
 
 /*
  * cp_ulysses_seq2head_n / cp_ulysses_head2seq_n — the same regroupings for

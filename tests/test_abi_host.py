@@ -468,3 +468,47 @@ def test_batched_relayout_rejects(name, count, kw, status):
     assert fn(args["inp"], args["out"], count, args["P"], args["B"], args["S"], args["H"],
               args["D"], args["dt"], None) == status
     assert cp.last_error().startswith("cp_ulysses")
+
+
+def _partial_vt(**kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, B=1, H=2, Sq=8, Skv=8, D=128, dt=BF16,
+             odt=F32, scale=0.1, causal=0, qp=0, kp=0)
+    a.update(kw)
+    return cp._chunk_partial_vt(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"],
+                                a["Skv"], a["D"], a["dt"], a["odt"], a["scale"], a["causal"],
+                                a["qp"], a["kp"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), UNSUPPORTED),                 # key-contiguous V: D = 128 only
+    (dict(dt=F32, odt=F32), UNSUPPORTED),      # bf16 inputs only
+    (dict(Skv=1 << 30), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(v=None), INVALID),
+    (dict(v=FAKE3 + 8), INVALID),
+    (dict(o=FAKE3 + 64), INVALID),             # output overlaps vt
+    (dict(causal=2), INVALID),
+])
+def test_chunk_partial_vt_rejects(kw, status):
+    assert _partial_vt(**kw) == status
+    assert cp.last_error().startswith("cp_attn_chunk_partial_vt")
+
+
+def test_chunk_partial_vt_zero_size_is_noop():
+    assert _partial_vt(Sq=0) == OK
+    assert _partial_vt(B=0, q=None, o=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=6), DIVISIBILITY), (dict(P=0), INVALID), (dict(B=-1), INVALID),
+    (dict(inp=None), INVALID), (dict(out=FAKE + 256), INVALID), (dict(dt=F32), UNSUPPORTED),
+    (dict(dt=5), INVALID), (dict(D=96), UNSUPPORTED), (dict(inp=FAKE + 8), INVALID),
+])
+def test_seq2head_vt_rejects(kw, status):
+    assert _relayout(cp._seq2head_vt, **kw) == status
+    assert cp.last_error().startswith("cp_ulysses_seq2head_vt")
+
+
+def test_seq2head_vt_zero_size_is_noop():
+    assert _relayout(cp._seq2head_vt, S=0) == OK
+    assert _relayout(cp._seq2head_vt, B=0, inp=None, out=None) == OK

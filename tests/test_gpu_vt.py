@@ -1,0 +1,119 @@
+"""GPU parity of the key-contiguous V path: cp_ulysses_seq2head_vt (bit-exact
+against the oracle's index permutation) and cp_attn_chunk_partial_vt (O and
+LSE bit-identical to cp_attn_chunk_partial on the same values, and within the
+bf16 bars of the fp64 oracle), on every launch plan of the attention call:
+two-group blocks (small grids), ping-pong blocks (large grids, causal and
+not) and the non-causal last-round plan; ragged query and key tails, two
+batches, causal offsets, fp32 and bf16 outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests._parity import check_lse, check_o_scaled, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import context_attention_dit_amd as cp
+DEV = "cuda:0"
+
+
+def _vt_of(v: torch.Tensor) -> torch.Tensor:
+    """[B][S][H][D] -> [B][H][ceil(S/64)][D][64], zero padding (test-side
+    marshalling of the same values)."""
+    B, S, H, D = v.shape
+    nt = (S + 63) // 64
+    pad = torch.zeros((B, nt * 64, H, D), dtype=v.dtype, device=v.device)
+    pad[:, :S] = v
+    return pad.view(B, nt, 64, H, D).permute(0, 3, 1, 4, 2).contiguous()
+
+
+@pytest.mark.parametrize("P,B,S_l,H,D", [(2, 1, 5, 4, 128), (3, 2, 5, 6, 128), (4, 2, 67, 8, 128),
+                                         (8, 1, 4095, 40, 128), (1, 1, 130, 2, 128),
+                                         (2, 1, 128, 2, 128), (8, 1, 2048, 32, 128)])
+def test_seq2head_vt_bit_exact(P, B, S_l, H, D):
+    say(f"seq2head_vt P={P} B={B} S_l={S_l} H={H} D={D}")
+    bits = synthetic.random_bits((P, B, S_l, H, D), 2, seed=700 + S_l)
+    x = bits.view(torch.bfloat16).to(DEV)
+    y = cp.ulysses_seq2head_vt(x, P)
+    torch.cuda.synchronize()
+    want = oracle.seq2head_vt(bits.numpy(), P)
+    assert np.array_equal(y.cpu().view(torch.int16).numpy(), want)
+
+
+def test_seq2head_vt_leaves_out_untouched_beyond_its_extent():
+    """Ragged token count (T = 15): the one tile is written whole (zeros past T),
+    nothing after it."""
+    P, B, S_l, H, D = 3, 1, 5, 3, 128
+    bits = synthetic.random_bits((P, B, S_l, H, D), 2, seed=711)
+    n = P * B * (H // P) * 1 * D * 64
+    buf = torch.full((n + 64,), -1, dtype=torch.int16, device=DEV)
+    out = buf[:n].view(torch.bfloat16).view(P, B, H // P, 1, D, 64)
+    cp.ulysses_seq2head_vt(bits.view(torch.bfloat16).to(DEV), P, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().view(torch.int16).numpy(), oracle.seq2head_vt(bits.numpy(), P))
+    assert torch.all(buf[n:] == -1)
+
+
+# (B, H, Sq, Skv, causal, q_pos0, kv_pos0): two-group grids, ping-pong grids,
+# the non-causal last-round plan (320 blocks of 256 rows: 64 in the last round)
+PLANS = [
+    (1, 2, 300, 1001, False, 0, 0),        # two-group blocks, ragged query and key tails
+    (2, 3, 129, 520, True, 0, 0),          # two-group, two batches, causal
+    (1, 2, 200, 1016, True, 900, 0),       # causal offsets: every row sees >= 901 keys
+    (1, 2, 200, 1016, True, 0, 100),       # causal offsets: rows 0..99 see no key
+    (1, 16, 1100, 1107, False, 0, 0),      # ping-pong blocks, ragged
+    (1, 4, 2056, 2056, True, 0, 0),        # ping-pong, causal
+    (1, 10, 8192, 264, False, 0, 0),       # last-round plan: 320 units
+    (1, 3, 64, 0, False, 0, 0),            # empty chunk
+]
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,causal,q0,k0", PLANS)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_chunk_partial_vt_matches_bshd_call_bitwise(B, H, Sq, Skv, causal, q0, k0, out_dtype):
+    D = 128
+    say(f"chunk_partial_vt B={B} H={H} Sq={Sq} Skv={Skv} causal={causal} q0={q0} k0={k0} "
+        f"out={out_dtype}")
+    q = synthetic.make_tensor((B, Sq, H, D), torch.bfloat16, 820).to(DEV)
+    k = synthetic.make_tensor((B, Skv, H, D), torch.bfloat16, 821).to(DEV)
+    v = synthetic.make_tensor((B, Skv, H, D), torch.bfloat16, 822).to(DEV)
+    vt = _vt_of(v)
+    kw = dict(causal=causal, q_pos0=q0, kv_pos0=k0, out_dtype=out_dtype)
+    o1, l1 = cp.attn_chunk_partial(q, k, v, **kw)
+    o2, l2 = cp.attn_chunk_partial_vt(q, k, vt, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), "O bits differ"
+    assert torch.equal(l1.view(torch.uint8), l2.view(torch.uint8)), "LSE bits differ"
+    if Sq * Skv * H * B <= 2_000_000:   # small enough for the oracle on every row
+        want_o, want_l = oracle.chunk_partial(to_f64(q), to_f64(k), to_f64(v), 1 / np.sqrt(D),
+                                              causal, np.arange(q0, q0 + Sq),
+                                              np.arange(k0, k0 + Skv))
+        check_o_scaled(o2, want_o)
+        check_lse(l2, want_l)
+
+
+def test_ulysses_rank_through_vt_path_against_oracle():
+    """A whole Ulysses rank step on the key-contiguous path: Q and K regrouped by
+    cp_ulysses_seq2head_n, V by cp_ulysses_seq2head_vt, rank p's attention by
+    cp_attn_chunk_partial_vt, O back by cp_ulysses_head2seq; every rank, every
+    row against the oracle's full attention."""
+    P, B, S_l, H, D = 4, 1, 96, 8, 128
+    say(f"ulysses vt step P={P} S_l={S_l} H={H}")
+    qkv = [synthetic.make_tensor((P, B, S_l, H, D), torch.bfloat16, 840 + t) for t in range(3)]
+    g = [x.to(DEV) for x in qkv]
+    qk = cp.ulysses_seq2head(torch.stack(g[:2]), P)       # [2][P][B][S][H_l][D]
+    vt = cp.ulysses_seq2head_vt(g[2], P)                  # [P][B][H_l][tiles][D][64]
+    o = torch.empty((P, B, P * S_l, H // P, D), dtype=torch.bfloat16, device=DEV)
+    for p in range(P):
+        cp.attn_chunk_partial_vt(qk[0, p], qk[1, p], vt[p], o[p], out_dtype=torch.bfloat16)
+    back = cp.ulysses_head2seq(o, P)                      # [P][B][S_l][H][D]
+    torch.cuda.synchronize()
+    full = [to_f64(x).transpose(1, 0, 2, 3, 4).reshape(B, P * S_l, H, D) for x in qkv]
+    want, _ = oracle.chunk_partial(full[0], full[1], full[2], 1 / np.sqrt(D))
+    got = to_f64(back).transpose(1, 0, 2, 3, 4).reshape(B, P * S_l, H, D)
+    err = np.abs(got - want)
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
