@@ -680,7 +680,14 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
                      dtype=torch.uint8, device=dev)
     d_att = [time_back_to_back(torch, lambda: cp.ring_attention(
         rq, [(rk, rv, 0)], o, lse, causal=w.causal, workspace=ws), 1, reps)]
-    del o, lse, ws
+    # V regrouped key-contiguous (cp_ulysses_seq2head_vt) and the attention that reads it
+    vt = cp.ulysses_seq2head_vt(qkv[2], P)
+    d_vt = [time_back_to_back(torch, lambda: cp.attn_chunk_partial_vt(
+        rq, rk, vt[0], o, lse, causal=w.causal, out_dtype=torch.bfloat16), 1, reps)]
+    vt_pairs = rotating_pairs(qkv[2], vt, nbytes)
+    d_s2h_vt = time_rotating(torch, [lambda x=x, y=y: cp.ulysses_seq2head_vt(x, P, y)
+                                     for x, y in vt_pairs], 1, 5)
+    del o, lse, ws, vt, vt_pairs
     # the rank's Q, K and V regrouped together in one launch (stacked tensors)
     qkv3 = torch.stack(qkv)
     heads3 = torch.empty((3,) + tuple(heads[0].shape), dtype=w.dtype, device=dev)
@@ -696,6 +703,10 @@ def ulysses_workload(torch, cp, synthetic, dev, w):
         "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attn_us_chunk_partial_vt": median(d_vt) * 1e3,
+        "attn_tflops_chunk_partial_vt": flops / (median(d_vt) * 1e-3) / 1e12,
+        "seq2head_vt_us": d_s2h_vt * 1e3,
+        "seq2head_vt_gbs": nbytes / (d_s2h_vt * 1e-3) / 1e9,
         "attn_us_chunk_partial": median(d_cp) * 1e3,
         "attn_tflops_chunk_partial": flops / (median(d_cp) * 1e-3) / 1e12,
         "seq2head_us": d_s2h * 1e3,
