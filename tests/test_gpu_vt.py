@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synthetic
-from tests._parity import check_lse, check_o_scaled, say, to_f64
+from tests._parity import check_lse, check_o, check_o_scaled, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +117,49 @@ def test_ulysses_rank_through_vt_path_against_oracle():
     got = to_f64(back).transpose(1, 0, 2, 3, 4).reshape(B, P * S_l, H, D)
     err = np.abs(got - want)
     assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("wname,n_edge,n_rand", [
+    ("qwen-image-1536-ulysses4-rank0", 64, 128),
+    ("wan-21x30x52-ulysses8-rank0", 48, 96),
+    ("llm-128k-causal-ulysses8-rank0", 48, 80),
+])
+def test_ulysses_rank0_full_size_vt(wname, n_edge, n_rand):
+    """The benchmark's path at full size: V of all ranks regrouped key-contiguous
+    (bit-exact against the oracle on rank 0's group), rank 0's attention through
+    cp_attn_chunk_partial_vt, equal bit for bit to the token-major call, and
+    sampled rows against the oracle."""
+    from tests.test_gpu_workloads import _rows
+    import math
+    w = synthetic.WORKLOADS[wname]
+    P, S_l, H, D = w.P, w.S_local, w.H, w.D
+    say(f"{w.name}: generating inputs")
+    q, k, v = synthetic.make_qkv(w)
+    shards = [x.view(P, 1, S_l, H, D).to(DEV) for x in (q, k, v)]
+    say(f"{w.name}: seq2head (Q, K), seq2head_vt (V)")
+    qk = cp.ulysses_seq2head(torch.stack(shards[:2]), P)
+    vt = cp.ulysses_seq2head_vt(shards[2], P)
+    vh = cp.ulysses_seq2head(shards[2], P)
+    torch.cuda.synchronize()
+    say(f"{w.name}: seq2head_vt vs oracle (rank 0's group)")
+    want = oracle.seq2head_vt(v.view(torch.int16).numpy().reshape(P, 1, S_l, H, D), P)
+    assert np.array_equal(vt[0].cpu().view(torch.int16).numpy(), want[0])
+    del want, shards
+    say(f"{w.name}: rank 0 attention, both V layouts (causal={w.causal})")
+    o, lse = cp.attn_chunk_partial_vt(qk[0, 0], qk[1, 0], vt[0], causal=w.causal,
+                                      out_dtype=torch.bfloat16)
+    o2, lse2 = cp.attn_chunk_partial(qk[0, 0], qk[1, 0], vh[0], causal=w.causal,
+                                     out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "O bits differ"
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32)), "LSE bits differ"
+    del o2, lse2, vh, vt, qk
+    rows = _rows(w.S, n_edge, n_rand, seed=w.seed)
+    say(f"{w.name}: oracle on {len(rows)} rows x {w.H_local} heads")
+    heads = slice(0, w.H_local)
+    wo, wl = oracle.attention(to_f64(q[:, rows][:, :, heads]), to_f64(k[:, :, heads]),
+                              to_f64(v[:, :, heads]), 1 / math.sqrt(D), w.causal, q_pos=rows,
+                              k_pos=np.arange(w.S))
+    idx = torch.from_numpy(rows).to(DEV)
+    check_o(o[:, idx], wo, "bf16", "rank 0 O (sampled rows)")
+    check_lse(lse[:, :, idx], wl, "rank 0 LSE (sampled rows)")
