@@ -27,7 +27,7 @@ Functions and the passages they follow:
   relayout.anything_seq2head / anything_head2seq (and *_loop forms)
                             the same with uneven per-rank token and head counts
                             (diffusers guide, Ulysses Anything Attention)
-  relayout.kv_gather (and kv_gather_loop)
+  relayout.kv_gather (and kv_gather_loop; kv_gather_vt: V key-contiguous)
                             the K/V all-gather's unpack (SGLang Diffusion
                             Sequence Parallelism, Choosing The Attention
                             Exchange: kv_gather)
@@ -49,12 +49,12 @@ from .attention import (attention, bf16_bits_to_f64, chunk_partial,
 from .backward import attention_grad, backward_delta, chunk_grad
 from .relayout import (anything_head2seq, anything_head2seq_loop, anything_seq2head,
                        anything_seq2head_loop, even_split, head2seq, head2seq_loop, kv_gather,
-                       kv_gather_loop, seq2head, seq2head_loop, seq2head_vt,
+                       kv_gather_loop, kv_gather_vt, seq2head, seq2head_loop, seq2head_vt,
                        seq2head_vt_loop)
 
 __all__ = ["attention", "chunk_partial", "lse_merge", "ring_attention", "softmax_matrix",
            "bf16_bits_to_f64", "seq2head", "head2seq", "seq2head_loop",
            "head2seq_loop", "seq2head_vt", "seq2head_vt_loop", "anything_seq2head",
            "anything_head2seq", "anything_seq2head_loop",
-           "anything_head2seq_loop", "even_split", "kv_gather", "kv_gather_loop",
+           "anything_head2seq_loop", "even_split", "kv_gather", "kv_gather_loop", "kv_gather_vt",
            "attention_grad", "backward_delta", "chunk_grad"]

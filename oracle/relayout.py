@@ -217,3 +217,19 @@ def kv_gather_loop(shards):
                     for d in range(D):
                         out[b, off[q] + s, h, d] = x[b, s, h, d]
     return out
+
+
+def kv_gather_vt(shards):
+    """list of ``[B][S_q][H][D]`` -> ``[B][H][ceil(S/64)][D][64]``: the all-gather's
+    unpack of the value tensor delivered key-contiguous in tiles of 64 tokens
+    (the layout of seq2head_vt), zero padding past the last token:
+
+        out[b][h][t // 64][d][t % 64] = shard_q[b][s][h][d],  t = off_q + s
+    """
+    full = kv_gather(shards)                            # [b][t][h][d]
+    B, S, H, D = full.shape
+    nt = -(-S // VT_TILE)
+    pad = np.zeros((B, nt * VT_TILE, H, D), dtype=full.dtype)
+    pad[:, :S] = full
+    return np.ascontiguousarray(
+        np.transpose(pad.reshape(B, nt, VT_TILE, H, D), (0, 3, 1, 4, 2)))

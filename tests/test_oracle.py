@@ -337,6 +337,30 @@ def test_relayout_vt_loop_and_index_formula(P, S_l, H, D):
     assert sorted(nz.tolist()) == sorted(x.ravel().tolist())
 
 
+@pytest.mark.parametrize("lens", [(3, 4), (64, 64, 1), (5,), (30, 30, 30, 30)])
+def test_kv_gather_vt_index_formula(lens):
+    """Key-contiguous gather: element by element out[b][h][t // 64][d][t % 64] =
+    shard_q[b][s][h][d] with t = off_q + s, zero padding; and for equal shards the
+    same array as the key-contiguous Ulysses regrouping with one head group of all
+    the gathered tokens."""
+    B, H, D = 2, 3, 2
+    shards = [np.arange(1, B * n * H * D + 1).reshape(B, n, H, D) + 1000 * q
+              for q, n in enumerate(lens)]
+    y = oracle.kv_gather_vt(shards)
+    S = sum(lens)
+    assert y.shape == (B, H, -(-S // 64), D, 64)
+    off = np.cumsum((0,) + tuple(lens))
+    for (b, h, tile, d, j), val in np.ndenumerate(y):
+        t = 64 * tile + j
+        if t >= S:
+            assert val == 0
+            continue
+        q = int(np.searchsorted(off, t, side="right") - 1)
+        assert val == shards[q][b, t - off[q], h, d]
+    full = np.concatenate(shards, axis=1)[None]      # one shard of all S tokens
+    assert np.array_equal(y, oracle.seq2head_vt(full, 1)[0])
+
+
 def test_relayout_moves_bits_unchanged():
     bits = synthetic.random_bits((4, 1, 6, 8, 16), 2, seed=60).numpy()
     y = oracle.seq2head(bits, 4)
