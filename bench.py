@@ -814,8 +814,23 @@ def kv_gather_workload(torch, cp, synthetic, dev):
     flops = 4.0 * D * H * n0 * S
     d_att = [time_back_to_back(torch, lambda: cp.attn_chunk_partial(
         q0, kg, vg, o, lse, out_dtype=torch.bfloat16), 1, 5)]
+    # V gathered key-contiguous (cp_kv_gather_vt, equal shards) and the attention on it
+    P = len(lens)
+    assert lens == [lens[0]] * P
+    vsh = v.view(P, 1, lens[0], H, D)
+    vt = cp.kv_gather_vt(vsh)
+    d_att_vt = [time_back_to_back(torch, lambda: cp.attn_chunk_partial_vt(
+        q0, kg, vt, o, lse, out_dtype=torch.bfloat16), 1, 5)]
+    pairs = rotating_pairs(vsh, vt, nbytes)
+    d_gvt = time_rotating(torch, [lambda x=x, y=y: cp.kv_gather_vt(x, y) for x, y in pairs], 1, 5)
+    del pairs, vt, vsh
     res = {
-        "rank_rows": n0, "attn_us": median(d_att) * 1e3,
+        "rank_rows": n0,
+        "attn_us_vt": median(d_att_vt) * 1e3,
+        "attn_tflops_vt": flops / (median(d_att_vt) * 1e-3) / 1e12,
+        "attn_mfma_frac_vt": flops / (median(d_att_vt) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gather_vt_gbs": nbytes / (d_gvt * 1e-3) / 1e9,
+        "attn_us": median(d_att) * 1e3,
         "attn_tflops": flops / (median(d_att) * 1e-3) / 1e12,
         "attn_mfma_frac": flops / (median(d_att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "gather_us": d_g * 1e3,
@@ -826,7 +841,8 @@ def kv_gather_workload(torch, cp, synthetic, dev):
         "gather_kv_hbm_frac": 2 * nbytes / (d_g2 * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "gather_bytes_per_tensor": nbytes, "gflop": flops / 1e9,
     }
-    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s, gather {res['gather_gbs']:.0f} GB/s, "
+    log(f"{w.name}: attn {res['attn_tflops']:.0f} TFLOP/s (key-contiguous V "
+        f"{res['attn_tflops_vt']:.0f}), gather {res['gather_gbs']:.0f} GB/s, "
         f"K+V in one launch {res['gather_kv_gbs']:.0f}")
     del q, k, v, kg, vg, q0, o, lse
     torch.cuda.empty_cache()

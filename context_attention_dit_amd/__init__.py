@@ -82,6 +82,7 @@ _ring_noalloc = _sig("cp_ring_attention_noalloc",
                       _f32, _int, _i64, _vp])
 _seq2head = _sig("cp_ulysses_seq2head", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _head2seq = _sig("cp_ulysses_head2seq", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
+_kv_gather_vt = _sig("cp_kv_gather_vt", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _seq2head_vt = _sig("cp_ulysses_seq2head_vt", [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp])
 _seq2head_n = _sig("cp_ulysses_seq2head_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
 _head2seq_n = _sig("cp_ulysses_head2seq_n", [_vp, _vp] + [_i64] * 6 + [_int, _vp])
@@ -359,6 +360,22 @@ def ulysses_seq2head_vt(x: torch.Tensor, P: int, out: Optional[torch.Tensor] = N
     return out
 
 
+def kv_gather_vt(x: torch.Tensor, out: Optional[torch.Tensor] = None, *,
+                 stream=None) -> torch.Tensor:
+    """``[P][B][S_l][H][D]`` (P equal shards) -> ``[B][H][ceil(P*S_l/64)][D][64]`` (the
+    gathered V, key-contiguous in 64-token tiles); see cp_kv_gather_vt."""
+    if x.dim() != 5:
+        raise ValueError("x must be [P][B][S_local][H][D]")
+    P, B, S_l, H, D = x.shape
+    shape = (B, H, (P * S_l + 63) // 64, D, 64)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _want(out, "out", shape, x.dtype, x.device)
+    _check("cp_kv_gather_vt", _kv_gather_vt(_ptr(x), _ptr(out), P, B, S_l, H, D,
+                                            _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
 def ulysses_head2seq(y: torch.Tensor, P: int, out: Optional[torch.Tensor] = None, *,
                      stream=None) -> torch.Tensor:
     """``[P][B][P*S_l][H_l][D]`` -> ``[P][B][S_l][P*H_l][D]``; see cp_ulysses_head2seq.
@@ -571,7 +588,7 @@ def ring_attention_backward(q: torch.Tensor,
     return dq, list(grads)
 
 
-__all__ = ["attn_chunk_partial", "attn_chunk_partial_vt", "ulysses_seq2head_vt", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
+__all__ = ["attn_chunk_partial", "attn_chunk_partial_vt", "ulysses_seq2head_vt", "kv_gather_vt", "lse_merge", "ring_attention", "ring_attention_workspace_bytes",
            "ulysses_seq2head", "ulysses_head2seq", "ulysses_anything_seq2head",
            "ulysses_anything_head2seq", "kv_gather", "attn_backward_delta",
            "attn_chunk_backward", "ring_attention_backward", "KVGrad", "BWD_ACCUMULATE_DQ",

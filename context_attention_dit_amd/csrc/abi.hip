@@ -539,16 +539,23 @@ cp_status cp_ulysses_head2seq(const void* in, void* out, int64_t P, int64_t B, i
   return relayout("cp_ulysses_head2seq", in, out, 1, P, B, S_local, H, D, dtype, stream, false);
 }
 
-cp_status cp_ulysses_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
-                                 int64_t H, int64_t D, cp_dtype dtype, void* stream) {
-  const char* fn = "cp_ulysses_seq2head_vt";
+}  // extern "C"
+
+namespace {
+
+// key-contiguous V: the Ulysses regrouping (groups = P) or the all-gather's
+// unpack of P equal shards (groups = 1)
+cp_status seq2head_vt(const char* fn, const void* in, void* out, int64_t P, int64_t B,
+                      int64_t S_local, int64_t H, int64_t D, cp_dtype dtype, void* stream,
+                      bool gather) {
   if (P < 1) return fail(CP_E_INVALID, "%s: P must be >= 1", fn);
   if (B < 0 || S_local < 0 || H < 0 || D < 0) return fail(CP_E_INVALID, "%s: negative size", fn);
   if (!valid_dtype(dtype)) return fail(CP_E_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (dtype != CP_BF16) return fail(CP_E_UNSUPPORTED, "%s: bf16 only", fn);
   if (D != 128 && D != 0)
     return fail(CP_E_UNSUPPORTED, "%s: D=%lld (key-contiguous V needs D = 128)", fn, (long long)D);
-  if (H % P != 0)
+  const int64_t groups = gather ? 1 : P;
+  if (H % groups != 0)
     return fail(CP_E_DIVISIBILITY, "%s: H=%lld heads do not divide by P=%lld", fn, (long long)H,
                 (long long)P);
   if (B == 0 || S_local == 0 || H == 0 || D == 0) return ok();
@@ -556,14 +563,28 @@ cp_status cp_ulysses_seq2head_vt(const void* in, void* out, int64_t P, int64_t B
   if (!aligned(in, 16) || !aligned(out, 16))
     return fail(CP_E_INVALID, "%s: misaligned pointer (16 B needed)", fn);
   const int64_t bytes = sat_mul({P, B, S_local, H, D, 2});
-  const int64_t out_bytes = sat_mul({P, B, H / P, (P * S_local + 63) / 64, D, 64, 2});
+  const int64_t out_bytes = sat_mul({B, H, (P * S_local + 63) / 64, D, 64, 2});
   if (overlap(in, bytes, out, out_bytes)) return fail(CP_E_INVALID, "%s: out overlaps in", fn);
   const int64_t T = sat_mul({P, S_local});
   if (T >= (int64_t(1) << 31) || sat_mul({B, H, (T + 127) / 128}) >= (int64_t(1) << 31))
     return fail(CP_E_UNSUPPORTED, "%s: tensor too large for one launch", fn);
-  return hip_status(cpattn::launch_seq2head_vt(in, out, P, B, S_local, H, D,
+  return hip_status(cpattn::launch_seq2head_vt(in, out, P, B, S_local, H, D, groups,
                                                static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_ulysses_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                                 int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  return seq2head_vt("cp_ulysses_seq2head_vt", in, out, P, B, S_local, H, D, dtype, stream, false);
+}
+
+cp_status cp_kv_gather_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                          int64_t H, int64_t D, cp_dtype dtype, void* stream) {
+  return seq2head_vt("cp_kv_gather_vt", in, out, P, B, S_local, H, D, dtype, stream, true);
 }
 
 cp_status cp_ulysses_seq2head_n(const void* in, void* out, int64_t count, int64_t P, int64_t B,

@@ -43,8 +43,9 @@ int relayout_word_bytes(const void* in, void* out, const RelayoutDesc& d);
 hipError_t launch_relayout(const void* in, void* out, const RelayoutDesc& d, hipStream_t stream);
 // seq2head of a bf16 value tensor into [P][B][H/P][ceil(P*S_local/64)][D][64]
 // (keys contiguous in 64-key tiles, zero padding past P*S_local)
+// (groups = P), or the K/V all-gather's unpack of P equal shards (groups = 1)
 hipError_t launch_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
-                              int64_t H, int64_t D, hipStream_t stream);
+                              int64_t H, int64_t D, int64_t groups, hipStream_t stream);
 
 // Ulysses Anything: uneven per-rank token counts and head counts. The P
 // sequence shards (shard q = [B][S_q][H][D]) and the P head groups (group p

@@ -309,19 +309,21 @@ __global__ __launch_bounds__(256) void seq2head_vt_kernel(const uint16_t* __rest
 }
 
 // The caller has checked: 2-byte elements, D = 128, 16-byte aligned pointers,
-// fewer than 2^31 tokens and blocks.
+// fewer than 2^31 tokens and blocks. `groups` head groups (P for the Ulysses
+// regrouping; 1 for the K/V all-gather's unpack, which gives every head all
+// P*S_local tokens).
 hipError_t launch_seq2head_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
-                              int64_t H, int64_t D, hipStream_t stream) {
+                              int64_t H, int64_t D, int64_t groups, hipStream_t stream) {
   (void)D;
   VtGeometry g;
   g.T = static_cast<uint32_t>(P * S_local);
   g.seq.init(static_cast<uint32_t>(S_local));
   g.B = static_cast<uint32_t>(B);
   g.H = static_cast<uint32_t>(H);
-  g.H_l = static_cast<uint32_t>(H / P);
+  g.H_l = static_cast<uint32_t>(H / groups);
   g.tiles = (g.T + 63) / 64;
   g.tblocks = (g.T + 127) / 128;
-  g.blocks = static_cast<uint32_t>(P * B * (H / P) * g.tblocks);
+  g.blocks = static_cast<uint32_t>(B * H * g.tblocks);
   hipLaunchKernelGGL(seq2head_vt_kernel, dim3(g.blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), g);
   return hipGetLastError();

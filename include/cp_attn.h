@@ -286,6 +286,27 @@ cp_status cp_ulysses_seq2head_vt(const void* in, void* out, int64_t P, int64_t B
                                  int64_t H, int64_t D, cp_dtype dtype, void* stream);
 
 /*
+ * cp_kv_gather_vt — the K/V all-gather's unpack for the value tensor, delivered
+ * key-contiguous: the V layout cp_attn_chunk_partial_vt reads, for a rank that
+ * attends its Q shard to the whole sequence's K and V.
+ *
+ * Defined by: the SGLang Diffusion Sequence Parallelism page, the table of
+ * attention modes and section K/V-Gather sequence parallelism (each rank
+ * gathers every rank's K and V shard). P shards of S_local tokens each, joined
+ * in rank order and written in tiles of 64 tokens, each tile feature-major;
+ * with t = q*S_local + s and T = P*S_local:
+ *   out[b][h][t / 64][d][t % 64] = in[q][b][s][h][d]
+ *   and the last tile's columns c >= T % 64 are 0.
+ *
+ *   in  [P][B][S_local][H][D] (shard q is in[q]), out [B][H][ceil(T/64)][D][64]
+ * Equal shards only (uneven shards: cp_kv_gather). dtype CP_BF16 and D = 128
+ * (else CP_E_UNSUPPORTED); in and out 16-byte aligned (else CP_E_INVALID).
+ * P*S_local < 2^31.
+ */
+cp_status cp_kv_gather_vt(const void* in, void* out, int64_t P, int64_t B, int64_t S_local,
+                          int64_t H, int64_t D, cp_dtype dtype, void* stream);
+
+/*
  * cp_ulysses_seq2head_n / cp_ulysses_head2seq_n — the same regroupings for
  * `count` tensors stored back to back, in one launch.
  *

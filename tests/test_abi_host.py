@@ -512,3 +512,18 @@ def test_seq2head_vt_rejects(kw, status):
 def test_seq2head_vt_zero_size_is_noop():
     assert _relayout(cp._seq2head_vt, S=0) == OK
     assert _relayout(cp._seq2head_vt, B=0, inp=None, out=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), INVALID), (dict(B=-1), INVALID), (dict(inp=None), INVALID),
+    (dict(out=FAKE + 256), INVALID), (dict(dt=F32), UNSUPPORTED), (dict(D=64), UNSUPPORTED),
+    (dict(inp=FAKE + 8), INVALID),
+])
+def test_kv_gather_vt_rejects(kw, status):
+    assert _relayout(cp._kv_gather_vt, **kw) == status
+    assert cp.last_error().startswith("cp_kv_gather_vt")
+
+
+def test_kv_gather_vt_any_head_count_and_zero_size():
+    assert _relayout(cp._kv_gather_vt, S=0) == OK
+    assert _relayout(cp._kv_gather_vt, H=6, S=0) == OK     # no head divisibility rule

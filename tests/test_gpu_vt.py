@@ -163,3 +163,27 @@ def test_ulysses_rank0_full_size_vt(wname, n_edge, n_rand):
     idx = torch.from_numpy(rows).to(DEV)
     check_o(o[:, idx], wo, "bf16", "rank 0 O (sampled rows)")
     check_lse(lse[:, :, idx], wl, "rank 0 LSE (sampled rows)")
+
+
+@pytest.mark.parametrize("P,B,S_l,H", [(4, 1, 8190, 40), (3, 2, 37, 5), (1, 1, 64, 2)])
+def test_kv_gather_vt_bit_exact_and_attention(P, B, S_l, H):
+    """The gathered V, key-contiguous, bit for bit against the oracle; a Q shard's
+    attention over the gathered K and V equal bit for bit through both layouts."""
+    D = 128
+    say(f"kv_gather_vt P={P} B={B} S_l={S_l} H={H}")
+    bits = synthetic.random_bits((P, B, S_l, H, D), 2, seed=900 + S_l)
+    y = cp.kv_gather_vt(bits.view(torch.bfloat16).to(DEV))
+    torch.cuda.synchronize()
+    want = oracle.kv_gather_vt([bits[q].numpy() for q in range(P)])
+    assert np.array_equal(y.cpu().view(torch.int16).numpy(), want)
+    Sq = min(S_l, 600)
+    q = synthetic.make_tensor((B, Sq, H, D), torch.bfloat16, 910).to(DEV)
+    kv = [synthetic.make_tensor((P, B, S_l, H, D), torch.bfloat16, 911 + t).to(DEV)
+          for t in range(2)]
+    k_full, v_full = (cp.kv_gather(x.reshape(-1), [S_l] * P, B, H, D) for x in kv)
+    vt = cp.kv_gather_vt(kv[1])
+    o1, l1 = cp.attn_chunk_partial(q, k_full, v_full, out_dtype=torch.bfloat16)
+    o2, l2 = cp.attn_chunk_partial_vt(q, k_full, vt, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
