@@ -264,8 +264,8 @@ def copy_same_bytes(torch, cp, dev, nbytes: int):
 
 def headline(torch, cp, synthetic, dev, steps: int, warmup: int, qkv_cpu, vt: bool = True,
              warm_ms: float = HEADLINE_WARM_MS):
-    """The 128K causal Ulysses rank's step: stacked seq2head of Q, K, V (all 8
-    ranks' regrouping), rank 0's causal attention on its 4 heads, head2seq of O
+    """The 128K causal Ulysses rank's step: seq2head of Q, K, V (all 8 ranks'
+    regrouping), rank 0's causal attention on its 4 heads, head2seq of O
     (rank 0's output in its slot; the other slots hold stand-in outputs).
     vt: Q and K regrouped in one launch and V by cp_ulysses_seq2head_vt (each
     head's values key-contiguous), attention by cp_attn_chunk_partial_vt;
