@@ -3,10 +3,12 @@
 Default workload (the headline line): one Ulysses rank of a 128K-token causal
 LLM at sequence-parallel degree 8 — S=131072, H=32 (4 heads per rank), D=128,
 bf16, causal from positions. One step is one pass of the rank's whole hot
-path: the Ulysses regrouping of Q, K and V ([8][1][16384][32][128] ->
-[8][1][131072][4][128], one stacked launch), rank 0's causal attention over
-the full sequence on its 4 heads (bf16 O, fp32 LSE), and the inverse
-regrouping of O. ``value`` is attention TFLOP/s over the whole step (4*D FLOP
+path: the Ulysses regrouping of Q and K ([8][1][16384][32][128] ->
+[8][1][131072][4][128], one stacked launch) and of V into each head's
+key-contiguous 64-token tiles (cp_ulysses_seq2head_vt), rank 0's causal
+attention over the full sequence on its 4 heads (cp_attn_chunk_partial_vt,
+bf16 O, fp32 LSE), and the inverse regrouping of O. The same step with V
+token-major is a detail entry. ``value`` is attention TFLOP/s over the whole step (4*D FLOP
 per visible (query, key) pair, 17.59 TFLOP per step) with inputs resident in
 HBM; ``roofline`` is the attention kernel alone, timed with HIP events on its
 launch stream.
